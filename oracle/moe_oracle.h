@@ -1,0 +1,85 @@
+/*
+ * CPU oracle for the MXFP4 routed-expert MoE layer -- TEST INFRASTRUCTURE.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this.  The GPU library shares no code, header, table or helper
+ * with it; the two meet only through the seeded input generator.
+ *
+ * Every function computes the plain definition, slowly and in the order the
+ * definition states.  Page citations name the page title and its section.
+ *
+ * Layouts (all canonical, row-major, little-endian):
+ *   MXFP4 matrix with R rows and K columns:
+ *     codes  uint8 [R][K/2]   element k of a row sits in byte k/2,
+ *                              low nibble for even k, high nibble for odd k
+ *     scales uint8 [R][K/32]  one UE8M0 byte per 32 consecutive elements
+ *   w13: [E_local][2I][H] (rows 0..I-1 = gate, rows I..2I-1 = up)
+ *   w2 : [E_local][H][I]
+ *   x  : bf16 bits [T][H];  router logits: float [T][E_global]
+ *   out: float [T][H] before rounding (out32) and bf16 bits [T][H]
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int64_t T, H, I;
+  int64_t E_global, E_local, first_local;
+  int32_t top_k;
+  float clamp_limit;
+  int32_t a4; /* 1: x and the SwiGLU output are MXFP4-quantised before each contraction */
+} orc_dims;
+
+/* element and scale decoding */
+double orc_e2m1_value(int32_t code);
+double orc_ue8m0_value(int32_t s);
+void orc_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                 float* out);
+
+/* OCP MX quantiser, one 32-element block at a time along each row */
+void orc_quantize_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales);
+void orc_quantize_f32(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales);
+void orc_quantize_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales);
+
+/* fp32 -> bf16, round to nearest even */
+uint16_t orc_bf16_from_f32(float f);
+void orc_bf16_round_array(const float* in, int64_t n, uint16_t* out);
+float orc_f32_from_bf16(uint16_t b);
+
+/* router: softmax over all global experts, top-k, renormalise over the k picks */
+int orc_route(const float* logits, int64_t T, int64_t E_global, int32_t k, int32_t* ids, float* w);
+
+/* local filter + histogram + exclusive scan + stable scatter; returns N_assign */
+int64_t orc_permute(const int32_t* ids, int64_t T, int32_t k, int64_t first_local, int64_t E_local,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv);
+
+/* clamped SwiGLU of one (gate, up) pair in fp32 */
+float orc_swiglu(float g, float u, float limit);
+
+/*
+ * Full layer.  token_mask (nullable, uint8 [T]) restricts the expert work and
+ * the combine to the tokens whose mask byte is non-zero; the routing tables are
+ * always produced for every token.  Outputs that are NULL are not written.
+ *   ids/w      [T][k]             counts [E_local], offsets [E_local+1]
+ *   sorted/inv [T*k]              act bf16 bits [T*k][I] (row p = sorted position p)
+ *   xq/xs      [T][H/2], [T][H/32]          (A4 only)
+ *   actq/acts  [T*k][I/2], [T*k][I/32]      (A4 only)
+ *   out32 float [T][H], out bf16 bits [T][H]
+ * Returns N_assign (>= 0) or a negative value on bad arguments.
+ */
+int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logits,
+                        const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                        const uint8_t* w2s, const uint8_t* token_mask, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv,
+                        uint16_t* act, uint8_t* xq, uint8_t* xs, uint8_t* actq, uint8_t* acts,
+                        float* out32, uint16_t* out, int32_t nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
