@@ -1,0 +1,183 @@
+/*
+ * mxfp4_moe.h -- C ABI of the MXFP4 routed-expert MoE layer for MI355X (gfx950).
+ *
+ * The layer (one GPU's share of it):
+ *   1. route:    per token, softmax over the E_global router logits, the top_k
+ *                experts, weights renormalised over those k picks;
+ *   2. permute:  the (token, slot) assignments whose expert is local
+ *                (first_local <= id < first_local + E_local) are counted per
+ *                expert, prefix-summed and scattered into expert-contiguous order,
+ *                keeping (token, slot) order inside each expert;
+ *   3. gate_up:  per assignment, h = W13_e x_t  (W13_e = [gate | up], 2I x H);
+ *   4. SwiGLU:   a = bf16( silu(min(g, L)) * clamp(u, -L, L) );
+ *   5. down:     y = W2_e a  (W2_e: H x I);
+ *   6. combine:  out[t] = bf16( sum over the token's local slots of w * y ).
+ * Weights are MXFP4: E2M1 codes, two per byte, and one UE8M0 power-of-two scale
+ * per 32 consecutive elements along K.
+ *
+ * Sources: the element format and its fixed 16-entry codebook and the OCP
+ * Microscaling block scale -- XFP blog, section "路线二：硬件格式（NVFP4 / MXFP4）";
+ * packed storage (a packed row is half the logical width) with a separate scale
+ * tensor, and a fused per-layer buffer of all experts -- campaign page
+ * "glm53-mxfp4-mi355x", sections "A fused tensor with two dtypes in it" and "The
+ * model card and the metadata disagree"; per-token reads of only the routed
+ * experts -- same page, section "A file is a census; a decode step is a sample";
+ * [gate | up] stacked into one weight feeding the SwiGLU -- TensorFold PR #1050,
+ * commit notes; the clamp kept by the MI355X experts -- model card
+ * "GLM-5.3-Flash-MXFP4", section "Verification compute and EAGLE"; refusing
+ * empty or overflowing shapes by name with checked arithmetic -- TensorFold PR
+ * #1050, review and commit notes.
+ *
+ * Conventions for every entry point:
+ *   - Status: 0 = MXFP4_MOE_OK, negative = a named refusal (see
+ *     mxfp4_moe_status_string).  All argument checks run on the host before any
+ *     GPU work is enqueued, so a refused call has enqueued nothing.
+ *   - Memory: every tensor pointer is device memory owned by the caller, 16-byte
+ *     aligned.  The library allocates nothing.  Inputs are read-only; outputs are
+ *     fully overwritten; the workspace's contents are undefined afterwards.
+ *   - Execution: work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without waiting.  No global mutable state: calls on different
+ *     streams with different workspaces may run concurrently.
+ *   - Shapes: int64 counts, validated with checked arithmetic.  H and I must be
+ *     multiples of 128; T may be 0 (nothing is enqueued).
+ *   - Preconditions not checked (for cost): router logits are not NaN (a NaN
+ *     logit gives an unspecified routing); NaN/inf in x or weights propagate.
+ */
+#ifndef MXFP4_MOE_H
+#define MXFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP4_MOE_ABI_VERSION 1
+
+/* status codes */
+#define MXFP4_MOE_OK 0
+#define MXFP4_MOE_ERR_NULL_POINTER (-1)        /* a required pointer is NULL */
+#define MXFP4_MOE_ERR_EMPTY_SHAPE (-2)         /* H, I, E_global, E_local or top_k is 0 */
+#define MXFP4_MOE_ERR_SHAPE_OVERFLOW (-3)      /* a byte or element count overflows */
+#define MXFP4_MOE_ERR_UNSUPPORTED_SHAPE (-4)   /* H or I not a multiple of 128, negative
+                                                  sizes, or local range outside E_global */
+#define MXFP4_MOE_ERR_BAD_TOP_K (-5)           /* top_k < 1, > E_global or > 32 */
+#define MXFP4_MOE_ERR_BAD_CLAMP (-6)           /* clamp_limit NaN or <= 0 (+inf = no clamp) */
+#define MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL (-7) /* workspace_bytes below the required size */
+#define MXFP4_MOE_ERR_MISALIGNED (-8)          /* a device pointer is not 16-byte aligned */
+#define MXFP4_MOE_ERR_UNSUPPORTED_DEVICE (-9)  /* current device is not gfx950 / no device */
+#define MXFP4_MOE_ERR_HIP (-10)                /* a HIP call failed (see last_hip_error) */
+#define MXFP4_MOE_ERR_BAD_FLAGS (-11)          /* unknown flag bits */
+#define MXFP4_MOE_ERR_BAD_ARGUMENT (-12)       /* any other invalid scalar argument */
+
+/* flags */
+#define MXFP4_MOE_A4 0x1u            /* quantise x (along H) and the SwiGLU output (along
+                                        I) to MXFP4 with the OCP rule and run both
+                                        contractions on scaled FP4 MFMA */
+#define MXFP4_MOE_DETERMINISTIC 0x2u /* combine by an ordered gather instead of fp32
+                                        atomics: bit-identical results run to run */
+
+typedef struct mxfp4_moe_dims {
+  int64_t T;           /* tokens */
+  int64_t H;           /* hidden size (K of gate_up, N of down) */
+  int64_t I;           /* per-expert intermediate size */
+  int64_t E_global;    /* experts the router chooses among (logit columns) */
+  int64_t E_local;     /* experts held by this GPU */
+  int64_t first_local; /* global id of local expert 0 */
+  uint32_t flags;      /* MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC */
+  uint32_t reserved;   /* must be 0 */
+} mxfp4_moe_dims;
+
+/* ABI version (MXFP4_MOE_ABI_VERSION of the built library). */
+int mxfp4_moe_abi_version(void);
+
+/* Static name of a status code ("MXFP4_MOE_OK", "MXFP4_MOE_ERR_..."); never NULL. */
+const char* mxfp4_moe_status_string(int status);
+
+/* hipError_t of the most recent MXFP4_MOE_ERR_HIP returned on the calling thread. */
+int mxfp4_moe_last_hip_error(void);
+
+/*
+ * Sizes of the preshuffled (gfx950) weight tensors for all E_local experts.
+ * Outputs: bytes of w13 codes, w13 scales, w2 codes, w2 scales.  Codes keep the
+ * canonical byte count; scales are padded to whole 512-element K groups.
+ */
+int mxfp4_moe_preshuffled_bytes(const mxfp4_moe_dims* d, size_t* w13_bytes,
+                                size_t* w13_scale_bytes, size_t* w2_bytes, size_t* w2_scale_bytes);
+
+/*
+ * One-time weight layout change, canonical -> gfx950 preshuffled.
+ * Canonical inputs (device):
+ *   canon_w13  uint8 [E_local][2I][H/2]   rows 0..I-1 gate, I..2I-1 up; element k of
+ *                                          a row in byte k/2, low nibble for even k
+ *   canon_w13s uint8 [E_local][2I][H/32]  UE8M0 scale of elements 32b..32b+31
+ *   canon_w2   uint8 [E_local][H][I/2],  canon_w2s uint8 [E_local][H][I/32]
+ * Outputs: buffers of the sizes mxfp4_moe_preshuffled_bytes reports.  The layout
+ * puts the 32 elements of one MX block of one row in one 16-byte lane load, with
+ * gate and up row groups interleaved.  It is an implementation detail: treat the
+ * preshuffled tensors as opaque and feed them only to mxfp4_moe_forward*.
+ */
+int mxfp4_moe_preshuffle(const mxfp4_moe_dims* d, const uint8_t* canon_w13,
+                         const uint8_t* canon_w13s, const uint8_t* canon_w2,
+                         const uint8_t* canon_w2s, uint8_t* w13, uint8_t* w13s, uint8_t* w2,
+                         uint8_t* w2s, hipStream_t stream);
+
+/* Workspace bytes mxfp4_moe_forward / mxfp4_moe_route need for these dims and top_k. */
+int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* bytes);
+
+/*
+ * The layer.  x: bf16 [T][H]; router_logits: float [T][E_global]; weights from
+ * mxfp4_moe_preshuffle; out: bf16 [T][H] (tokens with no local assignment get
+ * +0).  clamp_limit: L > 0 or +inf.  When T == 0, x, router_logits and out may
+ * be NULL and nothing is enqueued.
+ */
+int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                      const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                      const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxfp4_moe_forward that also copies the intermediates out, in canonical order
+ * (row p = sorted position p; rows at or past the assignment count are undefined):
+ *   act  bf16 [T*top_k][I]        SwiGLU output (required)
+ *   actq uint8 [T*top_k][I/2], acts uint8 [T*top_k][I/32]   A4 only (else may be NULL)
+ *   xq   uint8 [T][H/2],      xs   uint8 [T][H/32]          A4 only (else may be NULL)
+ */
+int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                            const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                            const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
+                            void* workspace, size_t workspace_bytes, void* act, uint8_t* actq,
+                            uint8_t* acts, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+
+/*
+ * Routing tables only (steps 1-2).  Outputs (device):
+ *   ids int32 [T][top_k] (rank order), weights float [T][top_k],
+ *   counts int32 [E_local], offsets int32 [E_local+1] (offsets[E_local] = N_assign),
+ *   sorted int32 [T*top_k] (first N_assign entries valid: slot t*top_k+j),
+ *   inv int32 [T*top_k] (sorted position of each slot, -1 if not local).
+ */
+int mxfp4_moe_route(const mxfp4_moe_dims* d, const float* router_logits, int32_t top_k,
+                    int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                    int32_t* sorted, int32_t* inv, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * OCP MX quantiser: rows x K values (K % 32 == 0) -> canonical MXFP4
+ * (codes uint8 [rows][K/2], scales uint8 [rows][K/32]).  Per 32-block: scale
+ * byte = clamp(floor(log2 amax) - 2 + 127, 0, 254); element = E2M1 nearest to
+ * v / 2^(scale-127), ties to the even code, saturating at +-6; a block holding
+ * NaN or inf gets scale 0xFF and zero codes.  in_dtype: 0 = bf16, 1 = float.
+ * This is the quantiser the A4 path applies to x and to the SwiGLU output, and
+ * the load-time weight quantiser.
+ */
+#define MXFP4_MOE_DTYPE_BF16 0
+#define MXFP4_MOE_DTYPE_F32 1
+int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP4_MOE_H */

@@ -1,1 +1,246 @@
-"""MXFP4 routed-expert MoE layer for MI355X (gfx950)."""
+"""MXFP4 routed-expert MoE layer for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libmxfp4_moe.so`` (C ABI in ``include/mxfp4_moe.h``).
+Every function here only marshals arguments: device pointers of torch tensors,
+shapes, and the current HIP stream.  All computation runs in the library's
+HIP kernels; there is no fallback path.  If the library is missing the calls
+raise ``MoEError``.
+
+Build the library with ``python -m mxfp4_block_scaled_router_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp4_moe.so")
+
+MXFP4_MOE_A4 = 0x1
+MXFP4_MOE_DETERMINISTIC = 0x2
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        name = status_string(status) if _lib is not None else str(status)
+        extra = ""
+        if _lib is not None and name == "MXFP4_MOE_ERR_HIP":
+            extra = " (hipError %d)" % _lib.mxfp4_moe_last_hip_error()
+        super().__init__("%s failed: %s%s" % (fn, name, extra))
+        self.status = status
+        self.name = name
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("E_global", ctypes.c_int64), ("E_local", ctypes.c_int64),
+                ("first_local", ctypes.c_int64), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+    @classmethod
+    def make(cls, T, H, I, E_global, E_local=None, first_local=0, a4=False,
+             deterministic=False) -> "Dims":
+        flags = (MXFP4_MOE_A4 if a4 else 0) | (MXFP4_MOE_DETERMINISTIC if deterministic else 0)
+        return cls(T, H, I, E_global, E_global if E_local is None else E_local, first_local,
+                   flags, 0)
+
+
+EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
+            "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
+            "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_route",
+            "mxfp4_moe_quantize")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmxfp4_moe.so and declare every exported signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoEError("load_library", -10**6)
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    PSZ = ctypes.POINTER(ctypes.c_size_t)
+    lib.mxfp4_moe_abi_version.restype = ctypes.c_int
+    lib.mxfp4_moe_abi_version.argtypes = []
+    lib.mxfp4_moe_status_string.restype = ctypes.c_char_p
+    lib.mxfp4_moe_status_string.argtypes = [ctypes.c_int]
+    lib.mxfp4_moe_last_hip_error.restype = ctypes.c_int
+    lib.mxfp4_moe_last_hip_error.argtypes = []
+    lib.mxfp4_moe_preshuffled_bytes.restype = ctypes.c_int
+    lib.mxfp4_moe_preshuffled_bytes.argtypes = [D, PSZ, PSZ, PSZ, PSZ]
+    lib.mxfp4_moe_preshuffle.restype = ctypes.c_int
+    lib.mxfp4_moe_preshuffle.argtypes = [D, P, P, P, P, P, P, P, P, P]
+    lib.mxfp4_moe_workspace_bytes.restype = ctypes.c_int
+    lib.mxfp4_moe_workspace_bytes.argtypes = [D, I32, PSZ]
+    lib.mxfp4_moe_forward.restype = ctypes.c_int
+    lib.mxfp4_moe_forward.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]
+    lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
+    lib.mxfp4_moe_forward_debug.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ,
+                                            P, P, P, P, P, P]
+    lib.mxfp4_moe_route.restype = ctypes.c_int
+    lib.mxfp4_moe_route.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.mxfp4_moe_quantize.restype = ctypes.c_int
+    lib.mxfp4_moe_quantize.argtypes = [P, I32, I64, I64, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _L():
+    return load_library()
+
+
+def status_string(status: int) -> str:
+    return _L().mxfp4_moe_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return _L().mxfp4_moe_abi_version()
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def _dev_tensor(t, dtype, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s tensor on the GPU" % (name, dtype))
+    return t
+
+
+# ---------------------------------------------------------------- sizes
+
+def mxfp4_moe_workspace_bytes(dims: Dims, top_k: int) -> int:
+    out = ctypes.c_size_t()
+    _check("mxfp4_moe_workspace_bytes",
+           _L().mxfp4_moe_workspace_bytes(ctypes.byref(dims), int(top_k), ctypes.byref(out)))
+    return out.value
+
+
+def mxfp4_moe_preshuffled_bytes(dims: Dims):
+    v = [ctypes.c_size_t() for _ in range(4)]
+    _check("mxfp4_moe_preshuffled_bytes",
+           _L().mxfp4_moe_preshuffled_bytes(ctypes.byref(dims), *[ctypes.byref(x) for x in v]))
+    return tuple(x.value for x in v)
+
+
+# ---------------------------------------------------------------- weights
+
+def mxfp4_moe_preshuffle(dims: Dims, w13, w13s, w2, w2s):
+    """Canonical MXFP4 expert weights (uint8 device tensors) -> preshuffled
+    (w13, w13s, w2, w2s) uint8 device tensors."""
+    for t, n in ((w13, "w13"), (w13s, "w13s"), (w2, "w2"), (w2s, "w2s")):
+        _dev_tensor(t, torch.uint8, n)
+    sizes = mxfp4_moe_preshuffled_bytes(dims)
+    outs = [torch.empty(n, dtype=torch.uint8, device=w13.device) for n in sizes]
+    _check("mxfp4_moe_preshuffle",
+           _L().mxfp4_moe_preshuffle(ctypes.byref(dims), _p(w13), _p(w13s), _p(w2), _p(w2s),
+                                     *[_p(o) for o in outs], _stream()))
+    return tuple(outs)
+
+
+def mxfp4_moe_quantize(values, in_dtype: int | None = None):
+    """OCP MX quantiser on the GPU: [..., K] bf16 or float32 -> (codes [..., K/2],
+    scales [..., K/32]) canonical uint8 tensors."""
+    if in_dtype is None:
+        in_dtype = DTYPE_BF16 if values.dtype == torch.bfloat16 else DTYPE_F32
+    want = torch.bfloat16 if in_dtype == DTYPE_BF16 else torch.float32
+    _dev_tensor(values, want, "values")
+    K = values.shape[-1]
+    rows = values.numel() // K if K else 0
+    codes = torch.empty(values.shape[:-1] + (K // 2,), dtype=torch.uint8, device=values.device)
+    scales = torch.empty(values.shape[:-1] + (K // 32,), dtype=torch.uint8, device=values.device)
+    _check("mxfp4_moe_quantize", _L().mxfp4_moe_quantize(_p(values), int(in_dtype), rows, K,
+                                                        _p(codes), _p(scales), _stream()))
+    return codes, scales
+
+
+# ---------------------------------------------------------------- layer
+
+def _workspace(dims, top_k, workspace, device):
+    need = mxfp4_moe_workspace_bytes(dims, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def mxfp4_moe_forward(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: int,
+                      clamp_limit: float, out=None, workspace=None):
+    """The layer: x bf16 [T, H], router_logits float32 [T, E_global], preshuffled
+    weights -> out bf16 [T, H]."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    if out is None:
+        out = torch.empty((dims.T, dims.H), dtype=torch.bfloat16, device=x.device)
+    workspace, nbytes = _workspace(dims, top_k, workspace, x.device)
+    _check("mxfp4_moe_forward",
+           _L().mxfp4_moe_forward(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13), _p(w13s),
+                                  _p(w2), _p(w2s), int(top_k), float(clamp_limit), _p(out),
+                                  _p(workspace), nbytes, _stream()))
+    return out
+
+
+def mxfp4_moe_forward_debug(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: int,
+                            clamp_limit: float, out=None, workspace=None):
+    """mxfp4_moe_forward plus the intermediates: dict with out, act (bf16 [T*k, I]) and,
+    in A4 mode, actq/acts/xq/xs."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    T, H, I, k = dims.T, dims.H, dims.I, int(top_k)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    act = torch.zeros((T * k, I), dtype=torch.bfloat16, device=dev)
+    a4 = bool(dims.flags & MXFP4_MOE_A4)
+    actq = torch.zeros((T * k, I // 2), dtype=torch.uint8, device=dev) if a4 else None
+    acts = torch.zeros((T * k, I // 32), dtype=torch.uint8, device=dev) if a4 else None
+    xq = torch.zeros((T, H // 2), dtype=torch.uint8, device=dev) if a4 else None
+    xs = torch.zeros((T, H // 32), dtype=torch.uint8, device=dev) if a4 else None
+    workspace, nbytes = _workspace(dims, top_k, workspace, dev)
+    _check("mxfp4_moe_forward_debug",
+           _L().mxfp4_moe_forward_debug(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13),
+                                        _p(w13s), _p(w2), _p(w2s), k, float(clamp_limit), _p(out),
+                                        _p(workspace), nbytes, _p(act), _p(actq), _p(acts),
+                                        _p(xq), _p(xs), _stream()))
+    return {"out": out, "act": act, "actq": actq, "acts": acts, "xq": xq, "xs": xs}
+
+
+def mxfp4_moe_route(dims: Dims, router_logits, top_k: int, workspace=None):
+    """Routing tables only: dict of ids, weights, counts, offsets, sorted, inv (device
+    tensors; the first offsets[-1] entries of sorted are valid)."""
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    T, k, El = dims.T, int(top_k), dims.E_local
+    dev = router_logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(El, dtype=torch.int32, device=dev)
+    offsets = torch.empty(El + 1, dtype=torch.int32, device=dev)
+    sorted_ = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    workspace, nbytes = _workspace(dims, top_k, workspace, dev)
+    _check("mxfp4_moe_route",
+           _L().mxfp4_moe_route(ctypes.byref(dims), _p(router_logits), k, _p(ids), _p(w),
+                                _p(counts), _p(offsets), _p(sorted_), _p(inv), _p(workspace),
+                                nbytes, _stream()))
+    return {"ids": ids, "weights": w, "counts": counts, "offsets": offsets, "sorted": sorted_,
+            "inv": inv}

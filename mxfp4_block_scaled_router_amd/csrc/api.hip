@@ -1,0 +1,487 @@
+// C ABI of the MXFP4 routed-expert MoE layer: host-side validation (checked
+// arithmetic, named refusals, all before any GPU work), workspace layout, the
+// choice of kernel variant, and the launch sequence.
+//
+// Refusing an empty or overflowing shape by name before any size is used
+// follows the loader rule of TensorFold PR #1050 (review and commit notes:
+// EmptyShape / ShapeOverflow via checked arithmetic).
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/mxfp4_moe.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace mxmoe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MXFP4_MOE_ERR_HIP;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// ---------------------------------------------------------------- shapes
+struct Shape {
+  int64_t T, H, I, Eg, El, f, k;
+  int64_t S;  // T * k
+  bool a4, ordered;
+};
+
+int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
+  if (!d) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (d->reserved != 0) return MXFP4_MOE_ERR_BAD_ARGUMENT;
+  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC)) return MXFP4_MOE_ERR_BAD_FLAGS;
+  if (d->T < 0 || d->H < 0 || d->I < 0 || d->E_global < 0 || d->E_local < 0 || d->first_local < 0)
+    return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->H == 0 || d->I == 0 || d->E_global == 0 || d->E_local == 0)
+    return MXFP4_MOE_ERR_EMPTY_SHAPE;
+  if (need_k) {
+    if (top_k == 0) return MXFP4_MOE_ERR_EMPTY_SHAPE;
+    if (top_k < 1 || top_k > d->E_global || top_k > 32) return MXFP4_MOE_ERR_BAD_TOP_K;
+  }
+  if (d->H % 128 || d->I % 128) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  int64_t last;
+  if (!add_ok(d->first_local, d->E_local, &last)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (last > d->E_global) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->E_global > 1024 || d->E_local > 1024) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  s->T = d->T;
+  s->H = d->H;
+  s->I = d->I;
+  s->Eg = d->E_global;
+  s->El = d->E_local;
+  s->f = d->first_local;
+  s->k = need_k ? top_k : 1;
+  s->a4 = (d->flags & MXFP4_MOE_A4) != 0;
+  s->ordered = (d->flags & MXFP4_MOE_DETERMINISTIC) != 0;
+  // element counts that the kernels index with int64 and int32
+  int64_t tmp;
+  if (!mul_ok(s->T, s->k, &s->S)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (s->S > INT32_MAX / 2) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;  // slot ids and positions are int32
+  if (!mul_ok(s->T, s->H, &tmp) || !mul_ok(tmp, 4, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (!mul_ok(s->T, s->Eg, &tmp) || !mul_ok(tmp, 4, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (!mul_ok(s->S, s->I, &tmp) || !mul_ok(tmp, 2, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (!mul_ok(s->S, s->H, &tmp) || !mul_ok(tmp, 4, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  int64_t per;
+  if (!mul_ok(2 * s->I, s->H, &per) || !mul_ok(per, s->El, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  return MXFP4_MOE_OK;
+}
+
+int check_clamp(float L) {
+  if (L != L || !(L > 0.0f)) return MXFP4_MOE_ERR_BAD_CLAMP;
+  return MXFP4_MOE_OK;
+}
+
+// ---------------------------------------------------------------- plans
+GemmPlan choose_plan(const Shape& s) {
+  // expected rows per local expert ~ T*k / E_global
+  GemmPlan p;
+  if (s.S <= 16 * s.Eg) {
+    p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
+  } else {
+    p.ms = 4; p.fg = 2; p.nw = 4; p.direct_a = 0;
+  }
+  return p;
+}
+
+int64_t max_tiles(const Shape& s, int mt) {
+  int64_t e = s.El < s.S ? s.El : s.S;
+  return e + s.S / mt;
+}
+
+// ---------------------------------------------------------------- workspace
+struct Layout {
+  size_t ids, w, lexp, rank, sorted, inv, chunk_cnt, counts, offsets, tile1, tile2;
+  size_t act, out32, ybuf, xq, xs, actq, acts;
+  size_t total;
+};
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout layout_of(const Shape& s) {
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  const size_t S = (size_t)s.S, El = (size_t)s.El;
+  L.ids = take(S * 4);
+  L.w = take(S * 4);
+  L.lexp = take(S * 4);
+  L.rank = take(S * 4);
+  L.sorted = take(S * 4);
+  L.inv = take(S * 4);
+  L.chunk_cnt = take(((S + 63) / 64) * El * 4);
+  L.counts = take(El * 4);
+  L.offsets = take((El + 1) * 4);
+  L.tile1 = take((El + 1) * 4);
+  L.tile2 = take((El + 1) * 4);
+  L.act = take(S * (size_t)s.I * 2);
+  L.out32 = s.ordered ? 0 : take((size_t)s.T * (size_t)s.H * 4);
+  L.ybuf = s.ordered ? take(S * (size_t)s.H * 4) : 0;
+  if (s.a4) {
+    L.xq = take((size_t)s.T * (size_t)s.H / 2);
+    L.xs = take((size_t)s.T * (size_t)s.H / 32);
+    L.actq = take(S * (size_t)s.I / 2);
+    L.acts = take(S * (size_t)s.I / 32);
+  } else {
+    L.xq = L.xs = L.actq = L.acts = 0;
+  }
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- device
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = (int)e;
+    return MXFP4_MOE_ERR_UNSUPPORTED_DEVICE;
+  }
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_ok[dev] == 1) return MXFP4_MOE_OK;
+    if (g_dev_ok[dev] == -1) return MXFP4_MOE_ERR_UNSUPPORTED_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return MXFP4_MOE_ERR_UNSUPPORTED_DEVICE;
+  }
+  bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev_ok[dev] = ok ? 1 : -1;
+  }
+  return ok ? MXFP4_MOE_OK : MXFP4_MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(base) + off);
+}
+
+RouteArgs route_args(const Shape& s, const float* logits, void* ws, const Layout& L, int mt1, int mt2) {
+  RouteArgs r;
+  r.logits = logits;
+  r.T = s.T;
+  r.E_global = (int32_t)s.Eg;
+  r.E_local = (int32_t)s.El;
+  r.first_local = (int32_t)s.f;
+  r.top_k = (int32_t)s.k;
+  r.mt1 = mt1;
+  r.mt2 = mt2;
+  r.ids = at<int32_t>(ws, L.ids);
+  r.w = at<float>(ws, L.w);
+  r.lexp = at<int32_t>(ws, L.lexp);
+  r.rank = at<int32_t>(ws, L.rank);
+  r.chunk_cnt = at<int32_t>(ws, L.chunk_cnt);
+  r.counts = at<int32_t>(ws, L.counts);
+  r.offsets = at<int32_t>(ws, L.offsets);
+  r.tile_off1 = at<int32_t>(ws, L.tile1);
+  r.tile_off2 = at<int32_t>(ws, L.tile2);
+  r.sorted = at<int32_t>(ws, L.sorted);
+  r.inv = at<int32_t>(ws, L.inv);
+  return r;
+}
+
+int check_forward_args(const mxfp4_moe_dims* d, const void* x, const float* logits, const uint8_t* w13,
+                       const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s, int32_t top_k,
+                       float clamp_limit, void* out, void* ws, size_t ws_bytes, Shape* s, Layout* L) {
+  int st = check_dims(d, top_k, true, s);
+  if (st) return st;
+  st = check_clamp(clamp_limit);
+  if (st) return st;
+  // x, logits and out may be NULL only when there are no tokens
+  if (!w13 || !w13s || !w2 || !w2s || !ws) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (s->T > 0 && (!x || !logits || !out)) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w13s, 16) || !aligned(w2, 16) ||
+      !aligned(w2s, 16) || !aligned(out, 16) || !aligned(ws, 256) || !aligned(logits, 4))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  *L = layout_of(*s);
+  if (ws_bytes < L->total) return MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MXFP4_MOE_OK;
+}
+
+int run_forward(const Shape& s, const Layout& L, const void* x, const float* logits, const uint8_t* w13,
+                const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s, float clamp_limit, void* out,
+                void* ws, hipStream_t stream) {
+  if (s.T == 0) return MXFP4_MOE_OK;
+  const GemmPlan plan = choose_plan(s);
+  const int mt = 16 * plan.ms;
+  RouteArgs r = route_args(s, logits, ws, L, mt, mt);
+  hipError_t e = launch_route(r, stream);
+  if (e != hipSuccess) return hip_fail(e);
+
+  if (s.a4) {
+    QuantArgs q;
+    q.in = x;
+    q.in_dtype = 0;
+    q.rows = s.T;
+    q.K = s.H;
+    q.in_row_stride = s.H;
+    q.codes = at<uint8_t>(ws, L.xq);
+    q.scales = at<uint8_t>(ws, L.xs);
+    e = launch_quantize(q, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.sorted = r.sorted;
+  g.counts = r.counts;
+  g.offsets = r.offsets;
+  g.route_w = r.w;
+  g.top_k = (int32_t)s.k;
+  g.E_local = (int32_t)s.El;
+  g.clamp_limit = clamp_limit;
+  // gate_up
+  g.a_bf16 = reinterpret_cast<const uint16_t*>(x);
+  g.a_codes = s.a4 ? at<uint8_t>(ws, L.xq) : nullptr;
+  g.a_scales = s.a4 ? at<uint8_t>(ws, L.xs) : nullptr;
+  g.w_codes = w13;
+  g.w_scales = w13s;
+  g.tile_off = r.tile_off1;
+  g.K = s.H;
+  g.N = 2 * s.I;
+  g.act = at<uint16_t>(ws, L.act);
+  g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
+  g.zero_n = s.ordered ? 0 : s.T * s.H;
+  e = launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
+  if (e != hipSuccess) return hip_fail(e);
+
+  if (s.a4) {
+    QuantArgs q;
+    q.in = at<uint16_t>(ws, L.act);
+    q.in_dtype = 0;
+    q.rows = s.S;
+    q.K = s.I;
+    q.in_row_stride = s.I;
+    q.codes = at<uint8_t>(ws, L.actq);
+    q.scales = at<uint8_t>(ws, L.acts);
+    e = launch_quantize(q, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+
+  // down + combine
+  g.a_bf16 = at<uint16_t>(ws, L.act);
+  g.a_codes = s.a4 ? at<uint8_t>(ws, L.actq) : nullptr;
+  g.a_scales = s.a4 ? at<uint8_t>(ws, L.acts) : nullptr;
+  g.w_codes = w2;
+  g.w_scales = w2s;
+  g.tile_off = r.tile_off2;
+  g.K = s.I;
+  g.N = s.H;
+  g.zero_buf = nullptr;
+  g.zero_n = 0;
+  g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
+  g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
+  e = launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
+  if (e != hipSuccess) return hip_fail(e);
+
+  CombineArgs c;
+  c.ybuf = g.ybuf;
+  c.out32 = g.out32;
+  c.route_w = r.w;
+  c.inv = r.inv;
+  c.T = s.T;
+  c.H = s.H;
+  c.top_k = (int32_t)s.k;
+  c.out = reinterpret_cast<uint16_t*>(out);
+  e = launch_combine(c, s.ordered, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
+}  // namespace
+
+// ==================================================================== ABI
+extern "C" {
+
+int mxfp4_moe_abi_version(void) { return MXFP4_MOE_ABI_VERSION; }
+
+int mxfp4_moe_last_hip_error(void) { return g_last_hip_error; }
+
+const char* mxfp4_moe_status_string(int status) {
+  switch (status) {
+    case MXFP4_MOE_OK: return "MXFP4_MOE_OK";
+    case MXFP4_MOE_ERR_NULL_POINTER: return "MXFP4_MOE_ERR_NULL_POINTER";
+    case MXFP4_MOE_ERR_EMPTY_SHAPE: return "MXFP4_MOE_ERR_EMPTY_SHAPE";
+    case MXFP4_MOE_ERR_SHAPE_OVERFLOW: return "MXFP4_MOE_ERR_SHAPE_OVERFLOW";
+    case MXFP4_MOE_ERR_UNSUPPORTED_SHAPE: return "MXFP4_MOE_ERR_UNSUPPORTED_SHAPE";
+    case MXFP4_MOE_ERR_BAD_TOP_K: return "MXFP4_MOE_ERR_BAD_TOP_K";
+    case MXFP4_MOE_ERR_BAD_CLAMP: return "MXFP4_MOE_ERR_BAD_CLAMP";
+    case MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL: return "MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MXFP4_MOE_ERR_MISALIGNED: return "MXFP4_MOE_ERR_MISALIGNED";
+    case MXFP4_MOE_ERR_UNSUPPORTED_DEVICE: return "MXFP4_MOE_ERR_UNSUPPORTED_DEVICE";
+    case MXFP4_MOE_ERR_HIP: return "MXFP4_MOE_ERR_HIP";
+    case MXFP4_MOE_ERR_BAD_FLAGS: return "MXFP4_MOE_ERR_BAD_FLAGS";
+    case MXFP4_MOE_ERR_BAD_ARGUMENT: return "MXFP4_MOE_ERR_BAD_ARGUMENT";
+    default: return "MXFP4_MOE_ERR_UNKNOWN";
+  }
+}
+
+int mxfp4_moe_preshuffled_bytes(const mxfp4_moe_dims* d, size_t* w13_bytes, size_t* w13_scale_bytes,
+                                size_t* w2_bytes, size_t* w2_scale_bytes) {
+  Shape s;
+  int st = check_dims(d, 1, false, &s);
+  if (st) return st;
+  if (!w13_bytes || !w13_scale_bytes || !w2_bytes || !w2_scale_bytes) return MXFP4_MOE_ERR_NULL_POINTER;
+  *w13_bytes = (size_t)(s.El * codes_per_expert(2 * s.I, s.H));
+  *w13_scale_bytes = (size_t)(s.El * scales_per_expert(2 * s.I, s.H));
+  *w2_bytes = (size_t)(s.El * codes_per_expert(s.H, s.I));
+  *w2_scale_bytes = (size_t)(s.El * scales_per_expert(s.H, s.I));
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_preshuffle(const mxfp4_moe_dims* d, const uint8_t* canon_w13, const uint8_t* canon_w13s,
+                         const uint8_t* canon_w2, const uint8_t* canon_w2s, uint8_t* w13, uint8_t* w13s,
+                         uint8_t* w2, uint8_t* w2s, hipStream_t stream) {
+  Shape s;
+  int st = check_dims(d, 1, false, &s);
+  if (st) return st;
+  if (!canon_w13 || !canon_w13s || !canon_w2 || !canon_w2s || !w13 || !w13s || !w2 || !w2s)
+    return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(canon_w13, 16) || !aligned(canon_w2, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(w13s, 4) || !aligned(w2s, 4))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  st = check_device();
+  if (st) return st;
+  PreshuffleArgs p;
+  p.canon_codes = canon_w13;
+  p.canon_scales = canon_w13s;
+  p.codes = w13;
+  p.scales = w13s;
+  p.E = s.El;
+  p.N = 2 * s.I;
+  p.K = s.H;
+  p.interleave_gate_up = 1;
+  hipError_t e = launch_preshuffle(p, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  p.canon_codes = canon_w2;
+  p.canon_scales = canon_w2s;
+  p.codes = w2;
+  p.scales = w2s;
+  p.N = s.H;
+  p.K = s.I;
+  p.interleave_gate_up = 0;
+  e = launch_preshuffle(p, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* bytes) {
+  Shape s;
+  int st = check_dims(d, top_k, true, &s);
+  if (st) return st;
+  if (!bytes) return MXFP4_MOE_ERR_NULL_POINTER;
+  *bytes = layout_of(s).total;
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                      const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
+                      int32_t top_k, float clamp_limit, void* out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  Shape s;
+  Layout L;
+  int st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, workspace,
+                              workspace_bytes, &s, &L);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  return run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream);
+}
+
+int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                            const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
+                            int32_t top_k, float clamp_limit, void* out, void* workspace,
+                            size_t workspace_bytes, void* act, uint8_t* actq, uint8_t* acts, uint8_t* xq,
+                            uint8_t* xs, hipStream_t stream) {
+  Shape s;
+  Layout L;
+  int st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, workspace,
+                              workspace_bytes, &s, &L);
+  if (st) return st;
+  if (!act) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (s.a4 && (!actq || !acts || !xq || !xs)) return MXFP4_MOE_ERR_NULL_POINTER;
+  st = check_device();
+  if (st) return st;
+  st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream);
+  if (st) return st;
+  hipError_t e = launch_copy_rows(at<uint8_t>(workspace, L.act), act, s.S * s.I * 2, stream);
+  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.actq), actq, s.S * s.I / 2, stream);
+  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.acts), acts, s.S * s.I / 32, stream);
+  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.xq), xq, s.T * s.H / 2, stream);
+  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.xs), xs, s.T * s.H / 32, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_route(const mxfp4_moe_dims* d, const float* router_logits, int32_t top_k, int32_t* ids,
+                    float* weights, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  int st = check_dims(d, top_k, true, &s);
+  if (st) return st;
+  if (!router_logits || !ids || !weights || !counts || !offsets || !sorted || !inv || !workspace)
+    return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(router_logits, 4) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(counts, 4) ||
+      !aligned(offsets, 4) || !aligned(sorted, 4) || !aligned(inv, 4) || !aligned(workspace, 256))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  Layout L = layout_of(s);
+  if (workspace_bytes < L.total) return MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL;
+  st = check_device();
+  if (st) return st;
+  if (s.T == 0) return MXFP4_MOE_OK;
+  const GemmPlan plan = choose_plan(s);
+  RouteArgs r = route_args(s, router_logits, workspace, L, 16 * plan.ms, 16 * plan.ms);
+  r.ids = ids;
+  r.w = weights;
+  r.counts = counts;
+  r.offsets = offsets;
+  r.sorted = sorted;
+  r.inv = inv;
+  hipError_t e = launch_route(r, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales, hipStream_t stream) {
+  if (in_dtype != MXFP4_MOE_DTYPE_BF16 && in_dtype != MXFP4_MOE_DTYPE_F32) return MXFP4_MOE_ERR_BAD_ARGUMENT;
+  if (rows < 0 || K < 0) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  if (K == 0) return MXFP4_MOE_ERR_EMPTY_SHAPE;
+  if (K % 32) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  int64_t n;
+  if (!mul_ok(rows, K, &n) || !mul_ok(n, 4, &n)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (!in || !codes || !scales) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(in, 16) || !aligned(codes, 16)) return MXFP4_MOE_ERR_MISALIGNED;
+  int st = check_device();
+  if (st) return st;
+  if (rows == 0) return MXFP4_MOE_OK;
+  QuantArgs q;
+  q.in = in;
+  q.in_dtype = in_dtype;
+  q.rows = rows;
+  q.K = K;
+  q.in_row_stride = K;
+  q.codes = codes;
+  q.scales = scales;
+  hipError_t e = launch_quantize(q, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
+}  // extern "C"

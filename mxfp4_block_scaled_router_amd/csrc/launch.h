@@ -1,0 +1,103 @@
+// Kernel argument blocks and launchers of the MXFP4 MoE layer (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+constexpr size_t kRouteFusedMaxLds = 48 * 1024;
+
+struct RouteArgs {
+  const float* logits;  // [T][E_global]
+  int64_t T;
+  int32_t E_global, E_local, first_local, top_k;
+  int32_t mt1, mt2;     // token-tile heights of the gate_up and down kernels
+  int32_t* ids;         // [S]
+  float* w;             // [S]
+  int32_t* lexp;        // [S]  local expert of each slot or -1
+  int32_t* rank;        // [S]  rank within its 64-slot chunk
+  int32_t* chunk_cnt;   // [ceil(S/64)][E_local]
+  int32_t* counts;      // [E_local]
+  int32_t* offsets;     // [E_local + 1]
+  int32_t* tile_off1;   // [E_local + 1]  prefix of ceil(count / mt1)
+  int32_t* tile_off2;   // [E_local + 1]  prefix of ceil(count / mt2)
+  int32_t* sorted;      // [S]
+  int32_t* inv;         // [S]
+};
+
+struct GemmArgs {
+  // activations: bf16 rows (x for gate_up, act for down) or MXFP4 rows (A4)
+  const uint16_t* a_bf16;   // gate_up: x [T][H]; down: act [S][I]
+  const uint8_t* a_codes;   // A4: [rows][K/2]
+  const uint8_t* a_scales;  // A4: [rows][K/32]
+  // preshuffled weights of all local experts
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  // routing tables
+  const int32_t* sorted;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* tile_off;
+  const float* route_w;     // [S] (down: combine weights)
+  int32_t top_k, E_local;
+  int64_t K, N;             // contraction length and weight rows (gate_up: N = 2I)
+  float clamp_limit;
+  // outputs
+  uint16_t* act;            // gate_up: bf16 [S][I]
+  float* out32;             // down (atomic combine): fp32 [T][H]
+  float* ybuf;              // down (ordered combine): fp32 [S][H]
+  // side duty: zero this fp32 buffer (grid-stride), may be null
+  float* zero_buf;
+  int64_t zero_n;
+};
+
+struct CombineArgs {
+  const float* ybuf;     // [S][H]
+  const float* out32;    // [T][H] (cast only)
+  const float* route_w;  // [S]
+  const int32_t* inv;    // [S]
+  int64_t T, H;
+  int32_t top_k;
+  uint16_t* out;         // bf16 [T][H]
+};
+
+struct QuantArgs {
+  const void* in;
+  int32_t in_dtype;      // 0 bf16, 1 f32
+  int64_t rows, K;
+  int64_t in_row_stride; // elements
+  uint8_t* codes;        // [rows][K/2]
+  uint8_t* scales;       // [rows][K/32]
+};
+
+struct PreshuffleArgs {
+  const uint8_t* canon_codes;   // [E][N][K/2]
+  const uint8_t* canon_scales;  // [E][N][K/32]
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t E, N, K;
+  int32_t interleave_gate_up;   // 1 for w13
+};
+
+// variant of the grouped GEMMs chosen by the host
+struct GemmPlan {
+  int ms;        // 16-row token subtiles per workgroup (token tile = 16 * ms)
+  int fg;        // 16-feature groups per wave
+  int nw;        // waves per workgroup
+  int direct_a;  // 1: activation operands loaded straight from global memory
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_gate_up(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
+                          hipStream_t stream);
+hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
+                       bool ordered, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t stream);
+hipError_t launch_copy_rows(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+}  // namespace mxmoe

@@ -1,0 +1,153 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+the oracle on the same seeded inputs, and compare them to the stated bars."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import mxfp4_block_scaled_router_amd as mx
+from mxfp4_block_scaled_router_amd import workloads as W
+
+TOL_REL_RMS = 2e-2        # max |gpu out - oracle out32| <= 2e-2 * rms(oracle out32)
+W_TOL = 2.0 ** -22        # router weights (different exp implementations)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def bf16_dev(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+class Case:
+    """Inputs of one parity case, on host (canonical numpy) and device."""
+
+    def __init__(self, wl: W.Workload, inp: dict | None = None, a4: bool | None = None,
+                 deterministic: bool = False):
+        self.wl = wl
+        self.a4 = wl.a4 if a4 is None else a4
+        self.deterministic = deterministic
+        self.inp = W.make_inputs(wl) if inp is None else inp
+        if "w13" not in self.inp:
+            self._quantise_student_t()
+        self.dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local,
+                                 a4=self.a4, deterministic=deterministic)
+        self.x = bf16_dev(self.inp["x"])
+        self.logits = to_dev(self.inp["logits"])
+        canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
+        self.pw = mx.mxfp4_moe_preshuffle(self.dims, *canon)
+        del canon
+
+    def _quantise_student_t(self):
+        """Student-t weights: drawn on the GPU, quantised there by the library and
+        on the host by the oracle; both codes must agree bit for bit."""
+        wl = self.wl
+        E, H, I = wl.E_local, wl.H, wl.I
+        w13 = np.empty((E, 2 * I, H // 2), np.uint8)
+        w13s = np.empty((E, 2 * I, H // 32), np.uint8)
+        w2 = np.empty((E, H, I // 2), np.uint8)
+        w2s = np.empty((E, H, I // 32), np.uint8)
+        self.quant_mismatch = 0
+        for e in range(E):
+            for which, (c_arr, s_arr) in (("w13", (w13, w13s)), ("w2", (w2, w2s))):
+                v = W.student_t_expert(wl, e, which, device="cuda")
+                gc, gs = mx.mxfp4_moe_quantize(v)
+                gc, gs = gc.cpu().numpy(), gs.cpu().numpy()
+                if e < 4 or e == E - 1:   # oracle cross-check on a few experts
+                    oc, os_ = oracle.quantize(v.cpu().numpy())
+                    self.quant_mismatch += int((oc != gc).sum() + (os_ != gs).sum())
+                c_arr[e], s_arr[e] = gc, gs
+        self.inp.update(w13=w13, w13s=w13s, w2=w2, w2s=w2s)
+
+    def run_gpu(self, debug=True):
+        wl = self.wl
+        if debug:
+            r = mx.mxfp4_moe_forward_debug(self.dims, self.x, self.logits, *self.pw, wl.top_k,
+                                           wl.clamp_limit)
+        else:
+            r = {"out": mx.mxfp4_moe_forward(self.dims, self.x, self.logits, *self.pw, wl.top_k,
+                                             wl.clamp_limit)}
+        torch.cuda.synchronize()
+        return r
+
+    def run_route(self):
+        r = mx.mxfp4_moe_route(self.dims, self.logits, self.wl.top_k)
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in r.items()}
+
+    def run_oracle(self, token_mask=None):
+        wl = self.wl
+        return oracle.moe_forward(self.inp["x"], self.inp["logits"], self.inp["w13"],
+                                  self.inp["w13s"], self.inp["w2"], self.inp["w2s"],
+                                  top_k=wl.top_k, clamp_limit=wl.clamp_limit,
+                                  E_global=wl.E_global, first_local=wl.first_local, a4=self.a4,
+                                  token_mask=token_mask, want_act=token_mask is None)
+
+
+def compare_route(g: dict, o) -> None:
+    n = int(o.offsets[-1])
+    np.testing.assert_array_equal(g["ids"], o.ids)
+    np.testing.assert_array_equal(g["counts"], o.counts)
+    np.testing.assert_array_equal(g["offsets"], o.offsets)
+    np.testing.assert_array_equal(g["sorted"][:n], o.sorted)
+    np.testing.assert_array_equal(g["inv"][: o.inv.size], o.inv)
+    dw = np.abs(g["weights"].astype(np.float64) - o.w.astype(np.float64)).max() if o.w.size else 0
+    assert dw <= W_TOL, dw
+
+
+def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray) -> dict:
+    """>= 99.9% bit-equal, every other element within 1 bf16 ulp; NaN matches NaN."""
+    n = o_act_bits.shape[0]
+    g = g_act_bits[:n]
+    gf, of = bf16_to_f32(g), bf16_to_f32(o_act_bits)
+    both_nan = np.isnan(gf) & np.isnan(of)
+    eq = (g == o_act_bits) | both_nan
+    frac = eq.mean() if eq.size else 1.0
+    # ulp distance via the ordered integer encoding
+    gi = g.astype(np.int32)
+    oi = o_act_bits.astype(np.int32)
+    gi = np.where(gi & 0x8000, 0x8000 - gi, gi)
+    oi = np.where(oi & 0x8000, 0x8000 - oi, oi)
+    ulp = np.where(eq, 0, np.abs(gi - oi))
+    assert eq.size == 0 or frac >= 0.999, frac
+    assert (ulp <= 1).all(), int(ulp.max())
+    return {"act_bit_equal": float(frac), "act_max_ulp": int(ulp.max()) if ulp.size else 0}
+
+
+def compare_out(g_out_bits: np.ndarray, o, rows=None) -> dict:
+    """max |gpu bf16 out - oracle out32| <= 2e-2 * rms(oracle out32) over the rows
+    compared (all, or the sampled tokens)."""
+    out32 = o.out32 if rows is None else o.out32[rows]
+    g = bf16_to_f32(g_out_bits if rows is None else g_out_bits[rows]).astype(np.float64)
+    ref = out32.astype(np.float64)
+    assert ref.size > 0
+    finite = np.isfinite(ref)
+    np.testing.assert_array_equal(np.isfinite(g), finite)
+    rms = float(np.sqrt(np.mean(ref[finite] ** 2))) if finite.any() else 0.0
+    err = float(np.abs(g[finite] - ref[finite]).max()) if finite.any() else 0.0
+    assert err <= TOL_REL_RMS * rms, (err, rms, err / max(rms, 1e-30))
+    gb = g_out_bits if rows is None else g_out_bits[rows]
+    ob = o.out if rows is None else o.out[rows]
+    mism = int((gb != ob).sum())
+    return {"max_err_over_rms": err / rms if rms else 0.0, "compared": int(ref.size),
+            "bf16_mismatch": mism, "max_over_rms": float(np.abs(ref[finite]).max() / rms) if rms else 0}

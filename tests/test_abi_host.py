@@ -1,0 +1,185 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and refuses each bad argument by name before touching a GPU.
+
+Pointers passed here are fake, suitably aligned integers: every refusal under
+test happens in host validation, before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_block_scaled_router_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4_moe.h")
+
+OK = 0
+NULL_POINTER, EMPTY_SHAPE, SHAPE_OVERFLOW, UNSUPPORTED_SHAPE = -1, -2, -3, -4
+BAD_TOP_K, BAD_CLAMP, WORKSPACE_TOO_SMALL, MISALIGNED = -5, -6, -7, -8
+UNSUPPORTED_DEVICE, HIP_ERR, BAD_FLAGS, BAD_ARGUMENT = -9, -10, -11, -12
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        from mxfp4_block_scaled_router_amd import build
+        build.build(verbose=False)
+    return mx.load_library()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mxfp4_moe_\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mx.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert mx.abi_version() == 1
+    src = open(HEADER).read()
+    for name, val in re.findall(r"#define (MXFP4_MOE_(?:OK|ERR_\w+)) \(?(-?\d+)\)?", src):
+        assert mx.status_string(int(val)) == name
+    assert mx.status_string(-999) == "MXFP4_MOE_ERR_UNKNOWN"
+
+
+def dims(**kw):
+    base = dict(T=16, H=512, I=256, E_global=8, E_local=8, first_local=0)
+    base.update(kw)
+    flags = kw.pop("flags", 0)
+    d = mx.Dims(base["T"], base["H"], base["I"], base["E_global"], base["E_local"],
+                base["first_local"], flags, 0)
+    return d
+
+
+def ws_status(d, k=2):
+    out = ctypes.c_size_t()
+    return mx.load_library().mxfp4_moe_workspace_bytes(ctypes.byref(d), k, ctypes.byref(out)), \
+        out.value
+
+
+@pytest.mark.parametrize("kw,k,expect", [
+    ({}, 2, OK),
+    ({"H": 0}, 2, EMPTY_SHAPE), ({"I": 0}, 2, EMPTY_SHAPE), ({"E_global": 0}, 2, EMPTY_SHAPE),
+    ({"E_local": 0}, 2, EMPTY_SHAPE), ({}, 0, EMPTY_SHAPE),
+    ({"H": 500}, 2, UNSUPPORTED_SHAPE), ({"I": 200}, 2, UNSUPPORTED_SHAPE),
+    ({"T": -1}, 2, UNSUPPORTED_SHAPE), ({"first_local": 4}, 2, UNSUPPORTED_SHAPE),
+    ({"first_local": -1}, 2, UNSUPPORTED_SHAPE), ({"E_global": 2048, "E_local": 8}, 2, UNSUPPORTED_SHAPE),
+    ({}, -1, BAD_TOP_K), ({}, 9, BAD_TOP_K), ({"E_global": 64, "E_local": 64}, 33, BAD_TOP_K),
+    ({"T": 1 << 40}, 8, SHAPE_OVERFLOW), ({"T": 1 << 60, "H": 1 << 10}, 2, SHAPE_OVERFLOW),
+    ({"first_local": (1 << 63) - 4}, 2, SHAPE_OVERFLOW),
+    ({"flags": 0x4}, 2, BAD_FLAGS),
+])
+def test_dims_refusals(lib, kw, k, expect):
+    st, _ = ws_status(dims(**kw), k)
+    assert st == expect, (mx.status_string(st), kw, k)
+
+
+def test_reserved_field_must_be_zero(lib):
+    d = dims()
+    d.reserved = 1
+    assert ws_status(d)[0] == BAD_ARGUMENT
+
+
+def test_workspace_grows_with_flags(lib):
+    _, base = ws_status(dims())
+    _, det = ws_status(dims(flags=mx.MXFP4_MOE_DETERMINISTIC))
+    _, a4 = ws_status(dims(flags=mx.MXFP4_MOE_A4))
+    assert base > 0 and det > 0 and a4 > base
+
+
+def test_null_dims(lib):
+    out = ctypes.c_size_t()
+    assert lib.mxfp4_moe_workspace_bytes(None, 2, ctypes.byref(out)) == NULL_POINTER
+    assert lib.mxfp4_moe_workspace_bytes(ctypes.byref(dims()), 2, None) == NULL_POINTER
+
+
+def test_preshuffled_bytes(lib):
+    d = dims(H=512, I=256, E_local=8)
+    w13, w13s, w2, w2s = mx.mxfp4_moe_preshuffled_bytes(d)
+    assert w13 == 8 * 512 * 256 and w2 == 8 * 512 * 128
+    # scales padded to whole 512-element K groups: one group of 256 bytes per 16 rows
+    assert w13s == 8 * (512 // 16) * 1 * 256
+    assert w2s == 8 * (512 // 16) * 1 * 256
+
+
+A = 1 << 20  # fake, 256-byte aligned "device" addresses
+
+
+def fwd(lib, d, k=2, clamp=7.0, ptrs=None, ws_bytes=None):
+    p = dict(x=A, logits=A, w13=A, w13s=A, w2=A, w2s=A, out=A, ws=A)
+    if ptrs:
+        p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = ws_status(d, k)[1] if ws_status(d, k)[0] == 0 else 0
+    V = ctypes.c_void_p
+    return lib.mxfp4_moe_forward(ctypes.byref(d), V(p["x"]), V(p["logits"]), V(p["w13"]),
+                                 V(p["w13s"]), V(p["w2"]), V(p["w2s"]), k, clamp, V(p["out"]),
+                                 V(p["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "logits", "w13", "w13s", "w2", "w2s", "out", "ws"])
+def test_forward_null_pointers(lib, name):
+    assert fwd(lib, dims(), ptrs={name: 0}) == NULL_POINTER
+
+
+@pytest.mark.parametrize("name,off", [("x", 8), ("w13", 4), ("w2s", 2), ("out", 1), ("ws", 16),
+                                      ("logits", 2)])
+def test_forward_misaligned(lib, name, off):
+    assert fwd(lib, dims(), ptrs={name: A + off}) == MISALIGNED
+
+
+@pytest.mark.parametrize("clamp", [float("nan"), 0.0, -1.0])
+def test_forward_bad_clamp(lib, clamp):
+    assert fwd(lib, dims(), clamp=clamp) == BAD_CLAMP
+
+
+def test_forward_inf_clamp_passes_validation(lib):
+    st = fwd(lib, dims(), clamp=float("inf"))
+    assert st in (OK, UNSUPPORTED_DEVICE)  # no GPU here: the device check is last
+
+
+def test_forward_workspace_too_small(lib):
+    d = dims()
+    need = ws_status(d)[1]
+    assert fwd(lib, d, ws_bytes=need - 1) == WORKSPACE_TOO_SMALL
+
+
+def test_forward_shape_refusals_come_first(lib):
+    assert fwd(lib, dims(H=0)) == EMPTY_SHAPE
+    assert fwd(lib, dims(), k=9) == BAD_TOP_K
+
+
+def test_quantize_refusals(lib):
+    V = ctypes.c_void_p
+    q = lib.mxfp4_moe_quantize
+    assert q(V(A), 2, 4, 64, V(A), V(A), None) == BAD_ARGUMENT
+    assert q(V(A), 0, 4, 0, V(A), V(A), None) == EMPTY_SHAPE
+    assert q(V(A), 0, 4, 48, V(A), V(A), None) == UNSUPPORTED_SHAPE
+    assert q(V(A), 0, -1, 64, V(A), V(A), None) == UNSUPPORTED_SHAPE
+    assert q(V(A), 0, 1 << 62, 64, V(A), V(A), None) == SHAPE_OVERFLOW
+    assert q(None, 0, 4, 64, V(A), V(A), None) == NULL_POINTER
+    assert q(V(A + 2), 0, 4, 64, V(A), V(A), None) == MISALIGNED
+
+
+def test_route_refusals(lib):
+    V = ctypes.c_void_p
+    d = dims()
+    r = lib.mxfp4_moe_route
+    args = [V(A)] * 7
+    assert r(ctypes.byref(d), V(A), 2, *args[:6], V(A), 0, None) == WORKSPACE_TOO_SMALL
+    assert r(ctypes.byref(d), None, 2, *args[:6], V(A), 1 << 30, None) == NULL_POINTER
+    assert r(ctypes.byref(d), V(A), 0, *args[:6], V(A), 1 << 30, None) == EMPTY_SHAPE
+
+
+def test_no_gpu_gives_device_refusal_not_a_crash(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert fwd(lib, dims()) == UNSUPPORTED_DEVICE

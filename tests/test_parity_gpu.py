@@ -1,0 +1,263 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Bars: routing tables bit-exact (router weights within 2^-22); the x and SwiGLU
+quantisations of the A4 path bit-exact; the bf16 SwiGLU intermediate >= 99.9%
+bit-equal with every other element within 1 bf16 ulp; the output within
+max|gpu - oracle out32| <= 2e-2 * rms(oracle out32).
+
+Sizes: the five workloads at full size (the tiny and decode ones compared
+whole; the larger ones on sampled tokens, which the oracle computes one by one)
+plus scaled-down shapes that span several tiles and ragged tails in both
+kernel variants, and the degenerate cases of the method.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp4_block_scaled_router_amd as mx
+from mxfp4_block_scaled_router_amd import workloads as W
+from tests.gpu_helpers import (Case, bits_of, compare_act, compare_out, compare_route, log,
+                               to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.load_library()   # fails loudly if the HIP library is missing
+    yield
+
+
+def scaled(name, **kw):
+    return W.WORKLOADS[name].replace(**kw)
+
+
+SMALL_CASES = {
+    "tiny": W.WORKLOADS["tiny"],
+    "decode_T1": scaled("decode", T=1),
+    "decode_T5_H256": scaled("decode", T=5, H=256, I=128, E_global=16, E_local=16, top_k=3),
+    "ep_share_small": scaled("ep_share", T=64, H=512, I=256, E_global=64, E_local=16,
+                             first_local=16),
+    "mid_lds": W.Workload("mid_lds", 256, 1024, 512, 32, 16, 8, 4, seed=77),
+    "prefill_small": scaled("prefill", T=1024, H=1024, I=384, E_global=16, E_local=16, top_k=4),
+    "dense_E1": W.Workload("dense_E1", 40, 256, 128, 1, 1, 0, 1, seed=5),
+    "all_experts": W.Workload("all_experts", 24, 256, 256, 6, 6, 0, 6, seed=6),
+    "topk32": W.Workload("topk32", 8, 128, 128, 64, 64, 0, 32, seed=7),
+    "no_clamp": W.Workload("no_clamp", 32, 512, 256, 8, 8, 0, 2, clamp_limit=float("inf"),
+                           seed=8),
+}
+A4_CASES = {
+    "a4_tiny": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
+    "a4_mid": W.WORKLOADS["a4"].replace(T=512, H=1024, I=512, E_global=16, E_local=16, top_k=4),
+}
+
+
+def _check_case(case: Case, token_mask=None):
+    log("case %s T=%d H=%d I=%d E=%d/%d k=%d a4=%d det=%d" % (
+        case.wl.name, case.wl.T, case.wl.H, case.wl.I, case.wl.E_local, case.wl.E_global,
+        case.wl.top_k, case.a4, case.deterministic))
+    g = case.run_gpu(debug=token_mask is None)
+    o = case.run_oracle(token_mask=token_mask)
+    rt = case.run_route()
+    compare_route(rt, o)
+    stats = {}
+    if token_mask is None:
+        stats.update(compare_act(bits_of(g["act"]), o.act))
+        if case.a4:
+            np.testing.assert_array_equal(g["xq"].cpu().numpy(), o.xq)
+            np.testing.assert_array_equal(g["xs"].cpu().numpy(), o.xs)
+            # the GPU's act re-quantised by the oracle must equal the GPU's actq/acts
+            n = o.n_assign
+            gact = bits_of(g["act"])[:n]
+            q, s = oracle.quantize(np.ascontiguousarray(gact))
+            np.testing.assert_array_equal(g["actq"].cpu().numpy()[:n], q)
+            np.testing.assert_array_equal(g["acts"].cpu().numpy()[:n], s)
+        stats.update(compare_out(bits_of(g["out"]), o))
+    else:
+        rows = np.nonzero(token_mask)[0]
+        stats.update(compare_out(bits_of(g["out"]), o, rows=rows))
+    log("  ok %s" % stats)
+    return g, o
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_forward_small(name):
+    _check_case(Case(SMALL_CASES[name]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_lds", "prefill_small"])
+def test_forward_deterministic(name):
+    case = Case(SMALL_CASES[name], deterministic=True)
+    g1, o = _check_case(case)
+    g2 = case.run_gpu()
+    np.testing.assert_array_equal(bits_of(g1["out"]), bits_of(g2["out"]))
+
+
+@pytest.mark.parametrize("name", list(A4_CASES))
+def test_forward_a4(name):
+    case = Case(A4_CASES[name])
+    assert case.quant_mismatch == 0
+    _check_case(case)
+
+
+def test_forward_tiny_full_and_decode_full():
+    _check_case(Case(W.WORKLOADS["tiny"]))
+    _check_case(Case(W.WORKLOADS["decode"]))
+
+
+def _sample_mask(T, n, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros(T, bool)
+    m[rng.choice(T, size=min(n, T), replace=False)] = True
+    m[0] = m[T - 1] = True
+    return m
+
+
+def test_forward_ep_share_full_sampled():
+    case = Case(W.WORKLOADS["ep_share"])
+    _check_case(case, token_mask=_sample_mask(case.wl.T, 48, 1))
+
+
+def test_ep_shares_sum_to_full_layer():
+    """Four expert-parallel shares (first_local = 0, 16, 32, 48 of 64) summed
+    equal the whole layer within the tolerance."""
+    full_wl = W.Workload("ep4", 48, 512, 256, 64, 64, 0, 8, seed=31)
+    inp = W.make_inputs(full_wl)
+    full = Case(full_wl, inp=inp)
+    o = full.run_oracle()
+    acc = np.zeros((full_wl.T, full_wl.H), np.float64)
+    for f in range(0, 64, 16):
+        sub = dict(inp)
+        for k in ("w13", "w13s", "w2", "w2s"):
+            sub[k] = inp[k][f:f + 16]
+        wl = full_wl.replace(E_local=16, first_local=f)
+        c = Case(wl, inp=sub)
+        log("share first_local=%d" % f)
+        g = c.run_gpu(debug=False)
+        acc += (g["out"].float().cpu().numpy()).astype(np.float64)
+    rms = np.sqrt(np.mean(o.out32.astype(np.float64) ** 2))
+    assert np.abs(acc - o.out32).max() <= 4 * 2e-2 * rms
+
+
+def test_forward_prefill_full_sampled():
+    case = Case(W.WORKLOADS["prefill"])
+    _check_case(case, token_mask=_sample_mask(case.wl.T, 24, 2))
+
+
+def test_forward_a4_full_sampled():
+    case = Case(W.WORKLOADS["a4"])
+    assert case.quant_mismatch == 0
+    _check_case(case, token_mask=_sample_mask(case.wl.T, 16, 3))
+
+
+def test_route_tables_full_sizes():
+    for name in ("decode", "ep_share", "prefill", "a4"):
+        wl = W.WORKLOADS[name]
+        inp = W.make_inputs(wl, weights=False)
+        dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local)
+        log("route %s" % name)
+        r = mx.mxfp4_moe_route(dims, to_dev(inp["logits"]), wl.top_k)
+        torch.cuda.synchronize()
+        r = {k: v.cpu().numpy() for k, v in r.items()}
+        ids, w = oracle.route(inp["logits"], wl.top_k)
+        counts, offsets, sorted_, inv = oracle.permute(ids, wl.first_local, wl.E_local)
+
+        class O:
+            pass
+        o = O()
+        o.ids, o.w, o.counts, o.offsets, o.sorted, o.inv = ids, w, counts, offsets, sorted_, inv
+        compare_route(r, o)
+
+
+def test_quantize_bit_exact():
+    rng = np.random.default_rng(17)
+    v = (rng.standard_normal((257, 512)) * np.exp2(rng.integers(-30, 30, size=(257, 1)))).astype(
+        np.float32)
+    v[3, 5] = np.nan
+    v[4, 70] = np.inf
+    v[5, :32] = 0.0
+    v[5, 3] = -0.0
+    v[6, :] = np.float32(2.0 ** -130)      # subnormal block
+    v[7, 40] = 3.0e38
+    # grid midpoints times powers of two
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0], np.float32)
+    v[8, :32] = np.tile(mids, 4) * 2.0 ** -3
+    for dt in ("f32", "bf16"):
+        if dt == "f32":
+            vin = v
+            gc, gs = mx.mxfp4_moe_quantize(torch.from_numpy(vin).cuda())
+            oc, os_ = oracle.quantize(vin)
+        else:
+            bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+            gc, gs = mx.mxfp4_moe_quantize(
+                torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda())
+            oc, os_ = oracle.quantize(bits)
+        np.testing.assert_array_equal(gc.cpu().numpy(), oc)
+        np.testing.assert_array_equal(gs.cpu().numpy(), os_)
+
+
+def test_quantize_every_bf16_value():
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    rows = allb.reshape(-1, 32)           # 2048 blocks, each a run of consecutive codes
+    gc, gs = mx.mxfp4_moe_quantize(torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).cuda())
+    oc, os_ = oracle.quantize(np.ascontiguousarray(rows))
+    np.testing.assert_array_equal(gc.cpu().numpy(), oc)
+    np.testing.assert_array_equal(gs.cpu().numpy(), os_)
+
+
+def test_t_zero_is_a_noop():
+    wl = W.Workload("t1", 1, 256, 128, 8, 8, 0, 2, seed=3)
+    case = Case(wl)
+    dims = mx.Dims.make(0, 256, 128, 8, 8)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    out = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp4_moe_forward(dims, x, lg, *case.pw, 2, 7.0, out=out)
+    torch.cuda.synchronize()
+
+
+def test_all_nonlocal_share_gives_zero_output():
+    wl = W.Workload("nonlocal", 20, 256, 128, 16, 4, 12, 2, seed=9)
+    inp = W.make_inputs(wl)
+    inp["logits"][:, 12:] -= 100.0          # nobody picks experts 12..15
+    case = Case(wl, inp=inp)
+    g, o = _check_case_zero(case)
+
+
+def _check_case_zero(case):
+    g = case.run_gpu()
+    o = case.run_oracle()
+    assert o.n_assign == 0
+    assert (bits_of(g["out"]) & 0x7FFF == 0).all()
+    return g, o
+
+
+def test_nan_scale_poisons_routed_rows():
+    wl = W.Workload("nan", 40, 256, 128, 8, 8, 0, 2, seed=31)
+    inp = W.make_inputs(wl)
+    inp["w13s"][3, 17, 2] = 255
+    case = Case(wl, inp=inp)
+    g = case.run_gpu()
+    o = case.run_oracle()
+    out = bits_of(g["out"])
+    outf = (out.astype(np.uint32) << 16).view(np.float32)
+    routed = (o.ids == 3).any(axis=1)
+    assert routed.any() and (~routed).any()
+    assert np.isnan(outf[routed]).all()
+    assert np.isfinite(outf[~routed]).all()
+
+
+def test_tamper_control_fails_parity():
+    """A flipped code byte of a routed expert must make the output check fail."""
+    wl = W.Workload("tamper", 32, 512, 256, 8, 8, 0, 2, seed=41)
+    inp = W.make_inputs(wl)
+    o = Case(wl, inp=inp).run_oracle()
+    e = int(o.ids[0, 0])
+    bad = dict(inp)
+    bad["w2"] = inp["w2"].copy()
+    bad["w2"][e, :, :] ^= 0x77
+    g = Case(wl, inp=bad).run_gpu(debug=False)
+    with pytest.raises(AssertionError):
+        compare_out(bits_of(g["out"]), o)
