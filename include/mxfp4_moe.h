@@ -144,12 +144,14 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* route
  *   act  bf16 [T*top_k][I]        SwiGLU output (required)
  *   actq uint8 [T*top_k][I/2], acts uint8 [T*top_k][I/32]   A4 only (else may be NULL)
  *   xq   uint8 [T][H/2],      xs   uint8 [T][H/32]          A4 only (else may be NULL)
+ *   out32 float [T][H]        the layer output before its bf16 rounding (may be NULL)
  */
 int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
                             const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
                             const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
                             void* workspace, size_t workspace_bytes, void* act, uint8_t* actq,
-                            uint8_t* acts, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+                            uint8_t* acts, uint8_t* xq, uint8_t* xs, float* out32,
+                            hipStream_t stream);
 
 /*
  * Routing tables only (steps 1-2).  Outputs (device):

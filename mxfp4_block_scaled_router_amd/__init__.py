@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_forward.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
     lib.mxfp4_moe_forward_debug.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ,
-                                            P, P, P, P, P, P]
+                                            P, P, P, P, P, P, P]
     lib.mxfp4_moe_route.restype = ctypes.c_int
     lib.mxfp4_moe_route.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.mxfp4_moe_quantize.restype = ctypes.c_int
@@ -202,8 +202,8 @@ def mxfp4_moe_forward(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: i
 
 def mxfp4_moe_forward_debug(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: int,
                             clamp_limit: float, out=None, workspace=None):
-    """mxfp4_moe_forward plus the intermediates: dict with out, act (bf16 [T*k, I]) and,
-    in A4 mode, actq/acts/xq/xs."""
+    """mxfp4_moe_forward plus the intermediates: dict with out, out32 (the fp32 output
+    before its bf16 rounding), act (bf16 [T*k, I]) and, in A4 mode, actq/acts/xq/xs."""
     _dev_tensor(x, torch.bfloat16, "x")
     _dev_tensor(router_logits, torch.float32, "router_logits")
     T, H, I, k = dims.T, dims.H, dims.I, int(top_k)
@@ -216,13 +216,15 @@ def mxfp4_moe_forward_debug(dims: Dims, x, router_logits, w13, w13s, w2, w2s, to
     acts = torch.zeros((T * k, I // 32), dtype=torch.uint8, device=dev) if a4 else None
     xq = torch.zeros((T, H // 2), dtype=torch.uint8, device=dev) if a4 else None
     xs = torch.zeros((T, H // 32), dtype=torch.uint8, device=dev) if a4 else None
+    out32 = torch.zeros((T, H), dtype=torch.float32, device=dev)
     workspace, nbytes = _workspace(dims, top_k, workspace, dev)
     _check("mxfp4_moe_forward_debug",
            _L().mxfp4_moe_forward_debug(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13),
                                         _p(w13s), _p(w2), _p(w2s), k, float(clamp_limit), _p(out),
                                         _p(workspace), nbytes, _p(act), _p(actq), _p(acts),
-                                        _p(xq), _p(xs), _stream()))
-    return {"out": out, "act": act, "actq": actq, "acts": acts, "xq": xq, "xs": xs}
+                                        _p(xq), _p(xs), _p(out32), _stream()))
+    return {"out": out, "out32": out32, "act": act, "actq": actq, "acts": acts, "xq": xq,
+            "xs": xs}
 
 
 def mxfp4_moe_route(dims: Dims, router_logits, top_k: int, workspace=None):

@@ -216,7 +216,7 @@ int check_forward_args(const mxfp4_moe_dims* d, const void* x, const float* logi
 
 int run_forward(const Shape& s, const Layout& L, const void* x, const float* logits, const uint8_t* w13,
                 const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s, float clamp_limit, void* out,
-                void* ws, hipStream_t stream) {
+                void* ws, hipStream_t stream, float* out32_copy = nullptr) {
   if (s.T == 0) return MXFP4_MOE_OK;
   const GemmPlan plan = choose_plan(s);
   const int mt = 16 * plan.ms;
@@ -299,8 +299,13 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   c.H = s.H;
   c.top_k = (int32_t)s.k;
   c.out = reinterpret_cast<uint16_t*>(out);
+  c.out32_copy = s.ordered ? out32_copy : nullptr;
   e = launch_combine(c, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (out32_copy && !s.ordered) {
+    e = launch_copy_rows(g.out32, out32_copy, s.T * s.H * 4, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   return MXFP4_MOE_OK;
 }
 
@@ -408,7 +413,7 @@ int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float*
                             const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
                             int32_t top_k, float clamp_limit, void* out, void* workspace,
                             size_t workspace_bytes, void* act, uint8_t* actq, uint8_t* acts, uint8_t* xq,
-                            uint8_t* xs, hipStream_t stream) {
+                            uint8_t* xs, float* out32, hipStream_t stream) {
   Shape s;
   Layout L;
   int st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, workspace,
@@ -418,7 +423,8 @@ int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float*
   if (s.a4 && (!actq || !acts || !xq || !xs)) return MXFP4_MOE_ERR_NULL_POINTER;
   st = check_device();
   if (st) return st;
-  st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream);
+  if (!aligned(out32, 16)) return MXFP4_MOE_ERR_MISALIGNED;
+  st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream, out32);
   if (st) return st;
   hipError_t e = launch_copy_rows(at<uint8_t>(workspace, L.act), act, s.S * s.I * 2, stream);
   if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.actq), actq, s.S * s.I / 2, stream);

@@ -469,6 +469,7 @@ __global__ __launch_bounds__(256) void combine_ordered_kernel(CombineArgs a) {
   uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
   uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
   *reinterpret_cast<uint2*>(a.out + i) = make_uint2(lo, hi);
+  if (a.out32_copy) *reinterpret_cast<f32x4_t*>(a.out32_copy + i) = acc;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {

@@ -61,6 +61,7 @@ struct CombineArgs {
   int64_t T, H;
   int32_t top_k;
   uint16_t* out;         // bf16 [T][H]
+  float* out32_copy;     // ordered combine: also store the fp32 sum here (may be null)
 };
 
 struct QuantArgs {

@@ -116,38 +116,60 @@ def compare_route(g: dict, o) -> None:
 
 
 def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray) -> dict:
-    """>= 99.9% bit-equal, every other element within 1 bf16 ulp; NaN matches NaN."""
+    """>= 99.9% bit-equal; every other element within 1 bf16 ulp, or within
+    2^-9 * rms(act) absolute where the fp32 gate/up sums cancel (their rounding
+    error is bounded by K * 2^-24 * sum|x*w|, not by the size of the result, so a
+    near-zero h may move by several bf16 ulps under another summation order).
+    NaN matches NaN."""
     n = o_act_bits.shape[0]
     g = g_act_bits[:n]
     gf, of = bf16_to_f32(g), bf16_to_f32(o_act_bits)
     both_nan = np.isnan(gf) & np.isnan(of)
     eq = (g == o_act_bits) | both_nan
-    frac = eq.mean() if eq.size else 1.0
-    # ulp distance via the ordered integer encoding
+    frac = float(eq.mean()) if eq.size else 1.0
     gi = g.astype(np.int32)
     oi = o_act_bits.astype(np.int32)
     gi = np.where(gi & 0x8000, 0x8000 - gi, gi)
     oi = np.where(oi & 0x8000, 0x8000 - oi, oi)
     ulp = np.where(eq, 0, np.abs(gi - oi))
-    assert eq.size == 0 or frac >= 0.999, frac
-    assert (ulp <= 1).all(), int(ulp.max())
-    return {"act_bit_equal": float(frac), "act_max_ulp": int(ulp.max()) if ulp.size else 0}
+    fin = np.isfinite(of)
+    rms = float(np.sqrt(np.mean(of[fin].astype(np.float64) ** 2))) if fin.any() else 0.0
+    absd = np.where(eq, 0.0, np.abs(gf.astype(np.float64) - of.astype(np.float64)))
+    far = ulp > 1
+    worst = float(absd[far].max() / rms) if far.any() and rms > 0 else 0.0
+    stats = {"act_bit_equal": frac, "act_max_ulp": int(ulp.max()) if ulp.size else 0,
+             "act_gt1ulp": int(far.sum()), "act_gt1ulp_max_abs_over_rms": worst}
+    assert eq.size == 0 or frac >= 0.999, stats
+    assert not (np.isnan(gf) ^ np.isnan(of)).any(), stats
+    assert worst <= 2.0 ** -9, stats
+    return stats
 
 
-def compare_out(g_out_bits: np.ndarray, o, rows=None) -> dict:
-    """max |gpu bf16 out - oracle out32| <= 2e-2 * rms(oracle out32) over the rows
-    compared (all, or the sampled tokens)."""
-    out32 = o.out32 if rows is None else o.out32[rows]
-    g = bf16_to_f32(g_out_bits if rows is None else g_out_bits[rows]).astype(np.float64)
-    ref = out32.astype(np.float64)
+def compare_out(g: dict, o, rows=None) -> dict:
+    """The layer output, in two parts:
+      1. the GPU's fp32 output before its bf16 rounding against the oracle's out32:
+         max |gpu32 - oracle32| <= 2e-2 * rms(oracle32) over the compared rows;
+      2. the GPU's bf16 output is exactly the round-to-nearest-even of its fp32
+         output (checked with the oracle's pinned bf16 rounding).
+    Also reported, not gated: max |gpu bf16 - oracle32| / rms and the number of
+    bf16 outputs that differ from the oracle's."""
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    g32 = sel(g["out32"].cpu().numpy()).astype(np.float64)
+    gb = sel(bits_of(g["out"]))
+    ref = sel(o.out32).astype(np.float64)
     assert ref.size > 0
     finite = np.isfinite(ref)
-    np.testing.assert_array_equal(np.isfinite(g), finite)
+    np.testing.assert_array_equal(np.isfinite(g32), finite)
     rms = float(np.sqrt(np.mean(ref[finite] ** 2))) if finite.any() else 0.0
-    err = float(np.abs(g[finite] - ref[finite]).max()) if finite.any() else 0.0
-    assert err <= TOL_REL_RMS * rms, (err, rms, err / max(rms, 1e-30))
-    gb = g_out_bits if rows is None else g_out_bits[rows]
-    ob = o.out if rows is None else o.out[rows]
-    mism = int((gb != ob).sum())
-    return {"max_err_over_rms": err / rms if rms else 0.0, "compared": int(ref.size),
-            "bf16_mismatch": mism, "max_over_rms": float(np.abs(ref[finite]).max() / rms) if rms else 0}
+    err = float(np.abs(g32[finite] - ref[finite]).max()) if finite.any() else 0.0
+    stats = {"max_err_over_rms": err / rms if rms else 0.0, "compared": int(ref.size)}
+    rounded = oracle.bf16_from_f32(np.ascontiguousarray(sel(g["out32"].cpu().numpy())))
+    stats["cast_mismatch"] = int((rounded != gb).sum())
+    gbf = bf16_to_f32(gb).astype(np.float64)
+    stats["bf16_err_over_rms"] = (float(np.abs(gbf[finite] - ref[finite]).max()) / rms
+                                  if rms else 0.0)
+    stats["bf16_mismatch"] = int((gb != sel(o.out)).sum())
+    stats["max_over_rms"] = float(np.abs(ref[finite]).max() / rms) if rms else 0.0
+    assert err <= TOL_REL_RMS * rms, stats
+    assert stats["cast_mismatch"] == 0, stats
+    return stats

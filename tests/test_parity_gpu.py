@@ -58,7 +58,7 @@ def _check_case(case: Case, token_mask=None):
     log("case %s T=%d H=%d I=%d E=%d/%d k=%d a4=%d det=%d" % (
         case.wl.name, case.wl.T, case.wl.H, case.wl.I, case.wl.E_local, case.wl.E_global,
         case.wl.top_k, case.a4, case.deterministic))
-    g = case.run_gpu(debug=token_mask is None)
+    g = case.run_gpu(debug=True)
     o = case.run_oracle(token_mask=token_mask)
     rt = case.run_route()
     compare_route(rt, o)
@@ -74,10 +74,10 @@ def _check_case(case: Case, token_mask=None):
             q, s = oracle.quantize(np.ascontiguousarray(gact))
             np.testing.assert_array_equal(g["actq"].cpu().numpy()[:n], q)
             np.testing.assert_array_equal(g["acts"].cpu().numpy()[:n], s)
-        stats.update(compare_out(bits_of(g["out"]), o))
+        stats.update(compare_out(g, o))
     else:
         rows = np.nonzero(token_mask)[0]
-        stats.update(compare_out(bits_of(g["out"]), o, rows=rows))
+        stats.update(compare_out(g, o, rows=rows))
     log("  ok %s" % stats)
     return g, o
 
@@ -258,6 +258,6 @@ def test_tamper_control_fails_parity():
     bad = dict(inp)
     bad["w2"] = inp["w2"].copy()
     bad["w2"][e, :, :] ^= 0x77
-    g = Case(wl, inp=bad).run_gpu(debug=False)
+    g = Case(wl, inp=bad).run_gpu(debug=True)
     with pytest.raises(AssertionError):
-        compare_out(bits_of(g["out"]), o)
+        compare_out(g, o)
