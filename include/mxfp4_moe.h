@@ -154,6 +154,20 @@ int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float*
                             hipStream_t stream);
 
 /*
+ * mxfp4_moe_forward that also records five caller-created events on `stream`
+ * around its phases, for timing: events[0] before routing, events[1] after
+ * routing (and, A4, the x quantisation), events[2] after gate_up + SwiGLU (and,
+ * A4, the SwiGLU quantisation), events[3] after down + combine, events[4] after
+ * the output cast (or ordered combine).  The computation is that of
+ * mxfp4_moe_forward.
+ */
+int mxfp4_moe_forward_timed(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                            const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                            const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
+                            void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                            hipStream_t stream);
+
+/*
  * Routing tables only (steps 1-2).  Outputs (device):
  *   ids int32 [T][top_k] (rank order), weights float [T][top_k],
  *   counts int32 [E_local], offsets int32 [E_local+1] (offsets[E_local] = N_assign),

@@ -53,8 +53,8 @@ class Dims(ctypes.Structure):
 
 EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
-            "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_route",
-            "mxfp4_moe_quantize")
+            "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
+            "mxfp4_moe_route", "mxfp4_moe_quantize")
 
 
 def load_library(path: str = LIB_PATH):
@@ -85,6 +85,9 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
     lib.mxfp4_moe_forward_debug.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ,
                                             P, P, P, P, P, P, P]
+    lib.mxfp4_moe_forward_timed.restype = ctypes.c_int
+    lib.mxfp4_moe_forward_timed.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ,
+                                            P, P]
     lib.mxfp4_moe_route.restype = ctypes.c_int
     lib.mxfp4_moe_route.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.mxfp4_moe_quantize.restype = ctypes.c_int
@@ -197,6 +200,29 @@ def mxfp4_moe_forward(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: i
            _L().mxfp4_moe_forward(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13), _p(w13s),
                                   _p(w2), _p(w2s), int(top_k), float(clamp_limit), _p(out),
                                   _p(workspace), nbytes, _stream()))
+    return out
+
+
+PHASES = ("route", "gate_up", "down", "combine")
+
+
+def mxfp4_moe_forward_timed(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: int,
+                            clamp_limit: float, events, out=None, workspace=None):
+    """mxfp4_moe_forward recording five torch.cuda.Event objects (created with
+    enable_timing=True) around its phases on the current stream; phase i lasts
+    events[i].elapsed_time(events[i+1]) for the names in PHASES."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    if len(events) != 5:
+        raise ValueError("need five events")
+    if out is None:
+        out = torch.empty((dims.T, dims.H), dtype=torch.bfloat16, device=x.device)
+    workspace, nbytes = _workspace(dims, top_k, workspace, x.device)
+    handles = (ctypes.c_void_p * 5)(*[ev.cuda_event for ev in events])
+    _check("mxfp4_moe_forward_timed",
+           _L().mxfp4_moe_forward_timed(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13),
+                                        _p(w13s), _p(w2), _p(w2s), int(top_k), float(clamp_limit),
+                                        _p(out), _p(workspace), nbytes, handles, _stream()))
     return out
 
 

@@ -216,8 +216,13 @@ int check_forward_args(const mxfp4_moe_dims* d, const void* x, const float* logi
 
 int run_forward(const Shape& s, const Layout& L, const void* x, const float* logits, const uint8_t* w13,
                 const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s, float clamp_limit, void* out,
-                void* ws, hipStream_t stream, float* out32_copy = nullptr) {
+                void* ws, hipStream_t stream, float* out32_copy = nullptr,
+                hipEvent_t* events = nullptr) {
   if (s.T == 0) return MXFP4_MOE_OK;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(events[i], stream) : hipSuccess;
+  };
+  if (hipError_t me = mark(0); me != hipSuccess) return hip_fail(me);
   const GemmPlan plan = choose_plan(s);
   const int mt = 16 * plan.ms;
   RouteArgs r = route_args(s, logits, ws, L, mt, mt);
@@ -236,6 +241,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     e = launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e);
 
   GemmArgs g;
   memset(&g, 0, sizeof(g));
@@ -273,6 +279,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     e = launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e);
 
   // down + combine
   g.a_bf16 = at<uint16_t>(ws, L.act);
@@ -289,6 +296,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
   e = launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e);
 
   CombineArgs c;
   c.ybuf = g.ybuf;
@@ -302,6 +310,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   c.out32_copy = s.ordered ? out32_copy : nullptr;
   e = launch_combine(c, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e);
   if (out32_copy && !s.ordered) {
     e = launch_copy_rows(g.out32, out32_copy, s.T * s.H * 4, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -407,6 +416,24 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* route
   st = check_device();
   if (st) return st;
   return run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream);
+}
+
+int mxfp4_moe_forward_timed(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                            const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
+                            int32_t top_k, float clamp_limit, void* out, void* workspace,
+                            size_t workspace_bytes, hipEvent_t* events, hipStream_t stream) {
+  Shape s;
+  Layout L;
+  int st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, workspace,
+                              workspace_bytes, &s, &L);
+  if (st) return st;
+  if (!events) return MXFP4_MOE_ERR_NULL_POINTER;
+  for (int i = 0; i < 5; ++i)
+    if (!events[i]) return MXFP4_MOE_ERR_NULL_POINTER;
+  st = check_device();
+  if (st) return st;
+  return run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream, nullptr,
+                     events);
 }
 
 int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
