@@ -62,7 +62,8 @@ extern "C" {
 #define MXFP4_MOE_ERR_EMPTY_SHAPE (-2)         /* H, I, E_global, E_local or top_k is 0 */
 #define MXFP4_MOE_ERR_SHAPE_OVERFLOW (-3)      /* a byte or element count overflows */
 #define MXFP4_MOE_ERR_UNSUPPORTED_SHAPE (-4)   /* H or I not a multiple of 128, negative
-                                                  sizes, or local range outside E_global */
+                                                  sizes, E_global > 512, or local range
+                                                  outside E_global */
 #define MXFP4_MOE_ERR_BAD_TOP_K (-5)           /* top_k < 1, > E_global or > 32 */
 #define MXFP4_MOE_ERR_BAD_CLAMP (-6)           /* clamp_limit NaN or <= 0 (+inf = no clamp) */
 #define MXFP4_MOE_ERR_WORKSPACE_TOO_SMALL (-7) /* workspace_bytes below the required size */

@@ -52,7 +52,7 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   int64_t last;
   if (!add_ok(d->first_local, d->E_local, &last)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
   if (last > d->E_global) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
-  if (d->E_global > 1024 || d->E_local > 1024) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->E_global > 512) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;  // router: 32 logits per lane of a 16-lane row
   s->T = d->T;
   s->H = d->H;
   s->I = d->I;
@@ -84,7 +84,11 @@ int check_clamp(float L) {
 GemmPlan choose_plan(const Shape& s) {
   // expected rows per local expert ~ T*k / E_global
   GemmPlan p;
-  if (s.S <= 16 * s.Eg) {
+  // the K-split kernels address activations through 32-bit buffer offsets and
+  // use one wave per 512 elements of K (at most 16 waves)
+  const bool ksplit_ok = s.T * s.H * 2 < (int64_t(1) << 30) && s.S * s.I * 2 < (int64_t(1) << 30) &&
+                         s.H <= 8192 && s.I <= 8192 && (s.I / 16) % 4 == 0 && (s.H / 32) % 4 == 0;
+  if (s.S <= 16 * s.Eg && ksplit_ok) {
     p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
   } else {
     p.ms = 4; p.fg = 2; p.nw = 4; p.direct_a = 0;
@@ -99,7 +103,7 @@ int64_t max_tiles(const Shape& s, int mt) {
 
 // ---------------------------------------------------------------- workspace
 struct Layout {
-  size_t ids, w, lexp, rank, sorted, inv, chunk_cnt, counts, offsets, tile1, tile2;
+  size_t ids, w, lexp, rank, sorted, inv, chunk_cnt, counts, offsets, tile1, tile2, tiles1, tiles2;
   size_t act, out32, ybuf, xq, xs, actq, acts;
   size_t total;
 };
@@ -122,6 +126,12 @@ Layout layout_of(const Shape& s) {
   L.offsets = take((El + 1) * 4);
   L.tile1 = take((El + 1) * 4);
   L.tile2 = take((El + 1) * 4);
+  {
+    const GemmPlan p = choose_plan(s);
+    const size_t nt = (size_t)max_tiles(s, 16 * p.ms);
+    L.tiles1 = take(nt * 16);
+    L.tiles2 = take(nt * 16);
+  }
   L.act = take(S * (size_t)s.I * 2);
   L.out32 = s.ordered ? 0 : take((size_t)s.T * (size_t)s.H * 4);
   L.ybuf = s.ordered ? take(S * (size_t)s.H * 4) : 0;
@@ -191,6 +201,8 @@ RouteArgs route_args(const Shape& s, const float* logits, void* ws, const Layout
   r.offsets = at<int32_t>(ws, L.offsets);
   r.tile_off1 = at<int32_t>(ws, L.tile1);
   r.tile_off2 = at<int32_t>(ws, L.tile2);
+  r.tiles1 = at<int4>(ws, L.tiles1);
+  r.tiles2 = at<int4>(ws, L.tiles2);
   r.sorted = at<int32_t>(ws, L.sorted);
   r.inv = at<int32_t>(ws, L.inv);
   return r;
@@ -254,17 +266,20 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.clamp_limit = clamp_limit;
   // gate_up
   g.a_bf16 = reinterpret_cast<const uint16_t*>(x);
+  g.a_rows = s.T;
   g.a_codes = s.a4 ? at<uint8_t>(ws, L.xq) : nullptr;
   g.a_scales = s.a4 ? at<uint8_t>(ws, L.xs) : nullptr;
   g.w_codes = w13;
   g.w_scales = w13s;
   g.tile_off = r.tile_off1;
+  g.tiles = r.tiles1;
   g.K = s.H;
   g.N = 2 * s.I;
   g.act = at<uint16_t>(ws, L.act);
   g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.zero_n = s.ordered ? 0 : s.T * s.H;
-  e = launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
+  e = plan.ms == 1 ? launch_gate_up_ksplit(g, max_tiles(s, mt), s.a4, stream)
+                   : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
 
   if (s.a4) {
@@ -283,18 +298,21 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
 
   // down + combine
   g.a_bf16 = at<uint16_t>(ws, L.act);
+  g.a_rows = s.S;
   g.a_codes = s.a4 ? at<uint8_t>(ws, L.actq) : nullptr;
   g.a_scales = s.a4 ? at<uint8_t>(ws, L.acts) : nullptr;
   g.w_codes = w2;
   g.w_scales = w2s;
   g.tile_off = r.tile_off2;
+  g.tiles = r.tiles2;
   g.K = s.I;
   g.N = s.H;
   g.zero_buf = nullptr;
   g.zero_n = 0;
   g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
-  e = launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
+  e = plan.ms == 1 ? launch_down_ksplit(g, max_tiles(s, mt), s.a4, s.ordered, stream)
+                   : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(e);
 

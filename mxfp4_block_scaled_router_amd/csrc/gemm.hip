@@ -34,19 +34,12 @@ struct Tile {
 };
 
 __device__ __forceinline__ bool find_tile(const GemmArgs& a, int tile, int MT, Tile* out) {
-  const int E = a.E_local;
-  if (tile >= a.tile_off[E]) return false;
-  int lo = 0, hi = E;  // tile_off[lo] <= tile < tile_off[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.tile_off[mid] <= tile) lo = mid;
-    else hi = mid;
-  }
-  int64_t m0 = (int64_t)(tile - a.tile_off[lo]) * MT;
-  int cnt = a.counts[lo];
-  out->e = lo;
-  out->rows = (int)((cnt - m0) < MT ? (cnt - m0) : MT);
-  out->p0 = a.offsets[lo] + m0;
+  const int n = a.tile_off[a.E_local];
+  const int4 ti = a.tiles[tile < n ? tile : 0];
+  if (tile >= n) return false;
+  out->e = ti.x;
+  out->rows = ti.y;
+  out->p0 = ti.z;
   return true;
 }
 

@@ -23,6 +23,8 @@ struct RouteArgs {
   int32_t* offsets;     // [E_local + 1]
   int32_t* tile_off1;   // [E_local + 1]  prefix of ceil(count / mt1)
   int32_t* tile_off2;   // [E_local + 1]  prefix of ceil(count / mt2)
+  int4* tiles1;         // [tile bound 1]  {expert, rows, first sorted position, 0}
+  int4* tiles2;         // [tile bound 2]
   int32_t* sorted;      // [S]
   int32_t* inv;         // [S]
 };
@@ -32,6 +34,7 @@ struct GemmArgs {
   const uint16_t* a_bf16;   // gate_up: x [T][H]; down: act [S][I]
   const uint8_t* a_codes;   // A4: [rows][K/2]
   const uint8_t* a_scales;  // A4: [rows][K/32]
+  int64_t a_rows;           // rows of the activation tensor (T for x, S for act)
   // preshuffled weights of all local experts
   const uint8_t* w_codes;
   const uint8_t* w_scales;
@@ -39,7 +42,8 @@ struct GemmArgs {
   const int32_t* sorted;
   const int32_t* counts;
   const int32_t* offsets;
-  const int32_t* tile_off;
+  const int32_t* tile_off;  // [E_local + 1]; tile_off[E_local] = number of tiles
+  const int4* tiles;        // {expert, rows, first sorted position, 0} per tile
   const float* route_w;     // [S] (down: combine weights)
   int32_t top_k, E_local;
   int64_t K, N;             // contraction length and weight rows (gate_up: N = 2I)
@@ -95,6 +99,9 @@ hipError_t launch_gate_up(const GemmArgs& a, const GemmPlan& p, int64_t max_tile
                           hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
                        bool ordered, hipStream_t stream);
+hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
+hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered,
+                              hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t stream);

@@ -8,6 +8,9 @@
 // picks are exp(l_j - l_max) / sum_i exp(l_i - l_max), computed in fp64 and
 // rounded once to fp32 -- the softmax normaliser cancels in the renormalisation.
 //
+// Top-k: 16 lanes (one DPP row) per token, each holding every 16th logit; k
+// rounds of a 16-lane argmax on (orderable logit, inverted id) keys.
+//
 // Permutation: slot s = t*k + j.  Slots are cut into 64-slot chunks; one wave
 // per chunk finds each slot's rank among the chunk's earlier slots with the same
 // expert (ballot over matching lanes) and the chunk's per-expert counts.  A
@@ -21,107 +24,135 @@ namespace mxmoe {
 
 namespace {
 
-constexpr int kMaxEPL = 16;  // logits per lane: E_global <= 1024
-
 __device__ __forceinline__ uint32_t orderable(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
+// DPP row (16-lane) butterflies: quad [1,0,3,2], quad [2,3,0,1], half mirror,
+// mirror.  Each pairs every lane with a distinct partner, so after the four
+// steps every lane of the row holds the row's reduction.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
+  uint32_t oh = dpp<CTRL>(hi), ol = dpp<CTRL>(lo);
+  bool take = (oh > hi) || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+__device__ __forceinline__ void row16_max_u64(uint32_t& hi, uint32_t& lo) {
+  max_step<kDppXor1>(hi, lo);
+  max_step<kDppXor2>(hi, lo);
+  max_step<kDppHalfMirror>(hi, lo);
+  max_step<kDppMirror>(hi, lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
   return v;
 }
 
-// Top-k of one token's logits by one wave.  Writes ids/w and the local expert
-// of each slot (or -1) to lexp.
-template <int EPL>
-__device__ void topk_token(const float* __restrict__ logits, int64_t t, int E, int k, int first_local,
-                           int E_local, int32_t* __restrict__ ids, float* __restrict__ w,
-                           int32_t* __restrict__ lexp) {
-  const int lane = lane_id();
-  uint64_t key[EPL];
-  float val[EPL];
-  const float* row = logits + t * (int64_t)E;
+// Top-k of token t by the 16-lane row of this lane.  lexp_out[s - slot_base]
+// receives the local expert (or -1) of each of the token's k slots s.
+template <int VPL>
+__device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, int64_t slot_base) {
+  const int r = lane_id() & 15;
+  const int E = a.E_global, k = a.top_k;
+  const float* row = a.logits + t * (int64_t)E;
+  uint32_t khi[VPL], klo[VPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    int e = i * 64 + lane;
-    float v = e < E ? row[e] : 0.0f;
-    val[i] = v;
-    key[i] = e < E ? (((uint64_t)orderable(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e)) : 0;
+  for (int i = 0; i < VPL; ++i) {
+    int e = r + 16 * i;
+    bool in = e < E;
+    float v = in ? row[e] : 0.0f;
+    khi[i] = in ? orderable(v) : 0u;
+    klo[i] = in ? 0xFFFFFFFFu - (uint32_t)e : 0u;
   }
-  int my_id = -1;      // pick j held by lane j
-  float my_logit = 0.0f;
+  uint32_t p0hi = 0, p0lo = 0, p1hi = 0, p1lo = 0;  // picks r and r + 16
+  uint32_t maxhi = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint32_t bh = 0, bl = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    int id = (int)(0xFFFFFFFFu - (uint32_t)best);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (i * 64 + lane == id) key[i] = 0;
-    if (lane == j) my_id = id;
-  }
-  // gather the picked logits to lanes 0..k-1 (owner lane of id = id % 64, slot id / 64)
-  {
-    int src_lane = my_id >= 0 ? (my_id & 63) : 0;
-    int src_slot = my_id >= 0 ? (my_id >> 6) : 0;
-    float cand = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      float v = __shfl(val[i], src_lane, 64);
-      if (i == src_slot) cand = v;
+    for (int i = 0; i < VPL; ++i) {
+      bool take = (khi[i] > bh) || (khi[i] == bh && klo[i] > bl);
+      bh = take ? khi[i] : bh;
+      bl = take ? klo[i] : bl;
     }
-    my_logit = cand;
+    row16_max_u64(bh, bl);
+    const uint32_t id = 0xFFFFFFFFu - bl;
+    if ((int)(id & 15) == r) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if ((uint32_t)i == (id >> 4)) khi[i] = klo[i] = 0u;
+    }
+    if (j == 0) maxhi = bh;
+    if (j == r) { p0hi = bh; p0lo = bl; }
+    if (j == r + 16) { p1hi = bh; p1lo = bl; }
   }
-  double m = __shfl((double)my_logit, 0, 64);  // pick 0 holds the largest logit
-  double ex = (lane < k) ? exp((double)my_logit - m) : 0.0;
-  double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 64);
-  if (lane < k) {
-    int64_t s = t * k + lane;
-    ids[s] = my_id;
-    w[s] = (float)(ex / sum);
-    int le = my_id - first_local;
-    lexp[s] = (le >= 0 && le < E_local) ? le : -1;
+  const double m = (double)from_orderable(maxhi);
+  const bool has0 = r < k, has1 = r + 16 < k;
+  const double e0 = has0 ? exp((double)from_orderable(p0hi) - m) : 0.0;
+  const double e1 = has1 ? exp((double)from_orderable(p1hi) - m) : 0.0;
+  const double sum = row16_sum_f64(e0 + e1);
+  const int64_t s0 = t * k;
+  if (has0) {
+    int id = (int)(0xFFFFFFFFu - p0lo);
+    a.ids[s0 + r] = id;
+    a.w[s0 + r] = (float)(e0 / sum);
+    int le = id - a.first_local;
+    lexp_out[s0 + r - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
+  }
+  if (has1) {
+    int id = (int)(0xFFFFFFFFu - p1lo);
+    a.ids[s0 + r + 16] = id;
+    a.w[s0 + r + 16] = (float)(e1 / sum);
+    int le = id - a.first_local;
+    lexp_out[s0 + r + 16 - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
   }
 }
 
-template <int EPL>
-__device__ void topk_dispatch_body(const RouteArgs& a, int64_t t) {
-  topk_token<EPL>(a.logits, t, a.E_global, a.top_k, a.first_local, a.E_local, a.ids, a.w, a.lexp);
-}
-
-__device__ void topk_any(const RouteArgs& a, int64_t t) {
-  int epl = (a.E_global + 63) / 64;
-  if (epl <= 1) topk_dispatch_body<1>(a, t);
-  else if (epl <= 2) topk_dispatch_body<2>(a, t);
-  else if (epl <= 4) topk_dispatch_body<4>(a, t);
-  else if (epl <= 8) topk_dispatch_body<8>(a, t);
-  else topk_dispatch_body<kMaxEPL>(a, t);
+__device__ void topk_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, int64_t slot_base) {
+  const int vpl = (a.E_global + 15) / 16;
+  if (vpl <= 1) topk_row<1>(a, t, lexp_out, slot_base);
+  else if (vpl <= 2) topk_row<2>(a, t, lexp_out, slot_base);
+  else if (vpl <= 4) topk_row<4>(a, t, lexp_out, slot_base);
+  else if (vpl <= 8) topk_row<8>(a, t, lexp_out, slot_base);
+  else if (vpl <= 16) topk_row<16>(a, t, lexp_out, slot_base);
+  else topk_row<32>(a, t, lexp_out, slot_base);
 }
 
 // Rank of each slot of chunk c among the chunk's slots with the same local
-// expert, and the chunk's per-expert counts (cnt_row has E_local entries, zeroed
-// beforehand; only experts present in the chunk are written).  One wave.
-__device__ void chunk_ranks(const RouteArgs& a, int64_t c, int32_t* cnt_row, int32_t* __restrict__ rank) {
+// expert, and the chunk's per-expert counts (cnt_row zeroed beforehand; only
+// experts present in the chunk are written).  One wave.
+__device__ void chunk_ranks(int64_t S, int64_t c, const int32_t* lexp, int32_t* cnt_row, int32_t* rank) {
   const int lane = lane_id();
-  const int64_t S = a.T * (int64_t)a.top_k;
-  int64_t s = c * 64 + lane;
-  int e = s < S ? a.lexp[s] : -1;
+  const int64_t s = c * 64 + lane;
+  const int e = s < S ? lexp[s] : -1;
   uint64_t remaining = __ballot(e >= 0);
   int my_rank = 0;
   while (remaining) {
-    int leader = __ffsll((unsigned long long)remaining) - 1;
-    int le = __shfl(e, leader, 64);
-    uint64_t mask = __ballot(e == le);
+    const int leader = __builtin_ctzll(remaining);
+    const int le = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t mask = __ballot(e == le);
     if (e == le) my_rank = __popcll(mask & ((1ull << lane) - 1ull));
     if (lane == leader) cnt_row[le] = __popcll(mask);
     remaining &= ~mask;
@@ -129,91 +160,52 @@ __device__ void chunk_ranks(const RouteArgs& a, int64_t c, int32_t* cnt_row, int
   if (s < S) rank[s] = my_rank;
 }
 
-// Exclusive scan over experts of v (one value per expert, E_local <= 1024) in a
-// workgroup; returns through out[] (E_local + 1 entries, out[E_local] = total).
-// Must be called by all threads of the workgroup.
-__device__ void wg_exclusive_scan(const int32_t* v, int32_t* out, int n, int32_t* lds_tmp) {
-  // simple: thread 0..n-1 copy, then a Hillis-Steele scan in LDS
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int i = tid; i < n; i += nt) lds_tmp[i] = v[i];
-  __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    int32_t add[4];
-    int q = 0;
-    for (int i = tid; i < n; i += nt) add[q++] = (i >= off) ? lds_tmp[i - off] : 0;
-    __syncthreads();
-    q = 0;
-    for (int i = tid; i < n; i += nt) lds_tmp[i] += add[q++];
-    __syncthreads();
-  }
-  for (int i = tid; i < n; i += nt) out[i + 1] = lds_tmp[i];
-  if (tid == 0) out[0] = 0;
-  __syncthreads();
-}
-
-// Per (chunk, expert) bases, counts, offsets and tile offsets.  One workgroup
-// of 1024 threads (16 waves).  cnt[c][e] (global or LDS) holds chunk counts and
-// is overwritten with the chunk's base within the expert.
-__device__ void scan_chunks(const RouteArgs& a, int32_t* cnt, int64_t nchunk, int32_t* lds_wave_sum,
-                            int32_t* lds_tmp, int32_t* lds_counts) {
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  const int nwaves = blockDim.x / 64;
-  const int E = a.E_local;
-  int64_t per = (nchunk + nwaves - 1) / nwaves;
-  int64_t c0 = wave * per, c1 = c0 + per < nchunk ? c0 + per : nchunk;
-  // pass 1: per-wave sums per expert (lane = expert, in strides of 64)
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    int e = e0 + lane;
-    int32_t sum = 0;
-    if (e < E)
-      for (int64_t c = c0; c < c1; ++c) sum += cnt[c * E + e];
-    if (e < E) lds_wave_sum[wave * E + e] = sum;
-  }
-  __syncthreads();
-  // exclusive scan over waves per expert; totals = counts
-  for (int e = tid; e < E; e += blockDim.x) {
-    int32_t run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      int32_t v = lds_wave_sum[w * E + e];
-      lds_wave_sum[w * E + e] = run;
-      run += v;
+// Exclusive scan of v[0..n) (the per-expert counts) by one wave: out[0..n],
+// out[n] = total (also to out_lds when given), and for the two token-tile
+// heights mt1/mt2 the prefix of ceil(v/mt) (t1/t2) and the flat tile tables
+// tiles1/tiles2: tile i -> {expert, rows, first sorted position, 0}.
+__device__ void wave_scan_experts(const int32_t* v, int n, int32_t* out, int32_t* out_lds, int mt1,
+                                  int32_t* t1, int4* tiles1, int mt2, int32_t* t2, int4* tiles2) {
+  const int lane = lane_id();
+  const int per = (n + 63) / 64;
+  const int b = lane * per;
+  int32_t s0 = 0, s1 = 0, s2 = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      int32_t c = v[b + i];
+      s0 += c;
+      s1 += (c + mt1 - 1) / mt1;
+      s2 += (c + mt2 - 1) / mt2;
     }
-    lds_counts[e] = run;
-    a.counts[e] = run;
+  // inclusive wave prefix of the lane totals
+  int32_t i0 = s0, i1 = s1, i2 = s2;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int32_t a0 = __shfl_up(i0, off, 64), a1 = __shfl_up(i1, off, 64), a2 = __shfl_up(i2, off, 64);
+    if (lane >= off) { i0 += a0; i1 += a1; i2 += a2; }
   }
-  __syncthreads();
-  // pass 2: chunk bases
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    int e = e0 + lane;
-    if (e < E) {
-      int32_t run = lds_wave_sum[wave * E + e];
-      for (int64_t c = c0; c < c1; ++c) {
-        int32_t v = cnt[c * E + e];
-        cnt[c * E + e] = run;
-        run += v;
-      }
+  int32_t r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      const int e = b + i;
+      const int32_t c = v[e];
+      out[e] = r0;
+      if (out_lds) out_lds[e] = r0;
+      t1[e] = r1;
+      t2[e] = r2;
+      for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt1, ++j)
+        tiles1[r1 + j] = make_int4(e, c - m0 < mt1 ? c - m0 : mt1, r0 + m0, 0);
+      for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt2, ++j)
+        tiles2[r2 + j] = make_int4(e, c - m0 < mt2 ? c - m0 : mt2, r0 + m0, 0);
+      r0 += c;
+      r1 += (c + mt1 - 1) / mt1;
+      r2 += (c + mt2 - 1) / mt2;
     }
-  }
-  // offsets and tile offsets
-  wg_exclusive_scan(lds_counts, a.offsets, E, lds_tmp);
-  for (int t = 0; t < 2; ++t) {
-    int mt = t == 0 ? a.mt1 : a.mt2;
-    int32_t* dst = t == 0 ? a.tile_off1 : a.tile_off2;
-    for (int e = tid; e < E; e += blockDim.x) lds_tmp[e + 1024] = (lds_counts[e] + mt - 1) / mt;
-    __syncthreads();
-    wg_exclusive_scan(lds_tmp + 1024, dst, E, lds_tmp);
-  }
-}
-
-__device__ void scatter_slot(const RouteArgs& a, int64_t s, const int32_t* cnt, const int32_t* offsets) {
-  int e = a.lexp[s];
-  if (e >= 0) {
-    int32_t pos = offsets[e] + cnt[(s / 64) * a.E_local + e] + a.rank[s];
-    a.sorted[pos] = (int32_t)s;
-    a.inv[s] = pos;
-  } else {
-    a.inv[s] = -1;
+  if (lane == 63) {
+    out[n] = i0;
+    if (out_lds) out_lds[n] = i0;
+    t1[n] = i1;
+    t2[n] = i2;
   }
 }
 
@@ -221,81 +213,165 @@ __device__ void scatter_slot(const RouteArgs& a, int64_t s, const int32_t* cnt, 
 
 // ---------------------------------------------------------------- kernels
 
-// Whole routing in one workgroup (small T*k): LDS holds the chunk counts.
-__global__ __launch_bounds__(1024) void route_fused_kernel(RouteArgs a) {
+// Whole routing in one workgroup of 512 threads, for small T*k*E (decode):
+// LDS holds the slot experts, ranks, chunk counts, counts and offsets.
+__global__ __launch_bounds__(512) void route_small_kernel(RouteArgs a) {
   extern __shared__ int32_t lds[];
   const int nwaves = blockDim.x / 64;
-  const int wave = threadIdx.x / 64;
+  const int wave = threadIdx.x / 64, lane = lane_id();
   const int64_t S = a.T * (int64_t)a.top_k;
   const int64_t nchunk = (S + 63) / 64;
-  int32_t* cnt = lds;                                  // [nchunk][E_local]
-  int32_t* wave_sum = cnt + nchunk * a.E_local;        // [16][E_local]
-  int32_t* counts = wave_sum + 16 * a.E_local;         // [E_local]
-  int32_t* tmp = counts + a.E_local;                   // [2048]
-  for (int64_t i = threadIdx.x; i < nchunk * a.E_local; i += blockDim.x) cnt[i] = 0;
-  for (int64_t t = wave; t < a.T; t += nwaves) topk_any(a, t);
-  __threadfence_block();
+  const int E = a.E_local;
+  int32_t* lexp = lds;                   // [S]
+  int32_t* rank = lexp + S;              // [S]
+  int32_t* cnt = rank + S;               // [nchunk][E]
+  int32_t* counts = cnt + nchunk * E;    // [E]
+  int32_t* offs = counts + E;            // [E + 1]
+  for (int64_t i = threadIdx.x; i < nchunk * E; i += blockDim.x) cnt[i] = 0;
+  for (int64_t t = wave * 4 + (lane >> 4); t < a.T; t += nwaves * 4) topk_any(a, t, lexp, 0);
   __syncthreads();
-  for (int64_t c = wave; c < nchunk; c += nwaves) chunk_ranks(a, c, cnt + c * a.E_local, a.rank);
-  __threadfence_block();
+  for (int64_t c = wave; c < nchunk; c += nwaves) chunk_ranks(S, c, lexp, cnt + c * E, rank);
   __syncthreads();
-  scan_chunks(a, cnt, nchunk, wave_sum, tmp, counts);
+  // per expert: running sum over chunks -> chunk bases; totals -> counts
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t run = 0;
+    for (int64_t c = 0; c < nchunk; ++c) {
+      int32_t v = cnt[c * E + e];
+      cnt[c * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+    a.counts[e] = run;
+  }
   __syncthreads();
-  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) scatter_slot(a, s, cnt, a.offsets);
+  if (wave == 0)
+    wave_scan_experts(counts, E, a.offsets, offs, a.mt1, a.tile_off1, a.tiles1, a.mt2, a.tile_off2, a.tiles2);
+  __syncthreads();
+  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = lexp[s];
+    if (e >= 0) {
+      const int32_t pos = offs[e] + cnt[(s / 64) * E + e] + rank[s];
+      a.sorted[pos] = (int32_t)s;
+      a.inv[s] = pos;
+    } else {
+      a.inv[s] = -1;
+    }
+  }
 }
 
-// Multi-kernel routing for large T*k.
-__global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
-  const int64_t S = a.T * (int64_t)a.top_k;
-  const int64_t n_cnt = ((S + 63) / 64) * a.E_local;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_cnt;
-       i += (int64_t)gridDim.x * blockDim.x)
-    a.chunk_cnt[i] = 0;
-  int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
-  if (t < a.T) topk_any(a, t);
+// ---- two-kernel routing for larger T*k*E
+// (1) top-k and chunk ranks: a workgroup of 256 threads (16 rows of 16 lanes)
+// takes `tpb` tokens, tpb*k a multiple of 64, so its slots are whole chunks.
+__global__ __launch_bounds__(256) void route_topk_chunk_kernel(RouteArgs a, int tpb) {
+  extern __shared__ int32_t lds[];
+  const int wave = threadIdx.x / 64, lane = lane_id();
+  const int E = a.E_local, k = a.top_k;
+  const int64_t S = a.T * (int64_t)k;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t s0 = t0 * k;
+  const int nslot = tpb * k;
+  const int nch = nslot / 64;
+  int32_t* lexp = lds;  // [nslot], indexed by slot - s0
+  for (int i = threadIdx.x; i < nslot; i += blockDim.x) lexp[i] = -1;
+  for (int64_t i = threadIdx.x; i < (int64_t)nch * E; i += blockDim.x) {
+    const int64_t c = s0 / 64 + i / E;
+    if (c * 64 < S) a.chunk_cnt[c * E + i % E] = 0;
+  }
+  __syncthreads();
+  for (int64_t t = t0 + threadIdx.x / 16; t < t0 + tpb && t < a.T; t += blockDim.x / 16)
+    topk_any(a, t, lexp, s0);
+  __syncthreads();
+  for (int c = wave; c < nch; c += blockDim.x / 64) {
+    const int64_t gc = s0 / 64 + c;
+    if (gc * 64 >= S) break;
+    chunk_ranks(S - s0, c, lexp, a.chunk_cnt + gc * E, a.rank + s0);
+  }
+  for (int i = threadIdx.x; i < nslot; i += blockDim.x)
+    if (s0 + i < S) a.lexp[s0 + i] = lexp[i];
 }
 
-__global__ __launch_bounds__(256) void route_chunk_kernel(RouteArgs a) {
-  const int64_t S = a.T * (int64_t)a.top_k;
-  int64_t c = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
-  if (c * 64 < S) chunk_ranks(a, c, a.chunk_cnt + c * a.E_local, a.rank);
-}
-
-__global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
+// (2) one workgroup of 1024 threads: chunk bases (waves split the chunks, lanes
+// the experts), counts, offsets, tile tables, then the scatter.
+__global__ __launch_bounds__(1024) void route_scan_scatter_kernel(RouteArgs a) {
   extern __shared__ int32_t lds[];
   const int64_t S = a.T * (int64_t)a.top_k;
   const int64_t nchunk = (S + 63) / 64;
-  int32_t* wave_sum = lds;                        // [16][E_local]
-  int32_t* counts = wave_sum + 16 * a.E_local;    // [E_local]
-  int32_t* tmp = counts + a.E_local;              // [2048]
-  scan_chunks(a, a.chunk_cnt, nchunk, wave_sum, tmp, counts);
+  const int E = a.E_local;
+  const int nwaves = blockDim.x / 64;
+  const int wave = threadIdx.x / 64, lane = lane_id();
+  int32_t* wave_sum = lds;                   // [16][E]
+  int32_t* counts = wave_sum + nwaves * E;   // [E]
+  int32_t* offs = counts + E;                // [E + 1]
+  int32_t* cnt = a.chunk_cnt;
+  const int64_t per = (nchunk + nwaves - 1) / nwaves;
+  const int64_t c0 = wave * per, c1 = c0 + per < nchunk ? c0 + per : nchunk;
+  for (int e = lane; e < E; e += 64) {
+    int32_t sum = 0;
+    for (int64_t c = c0; c < c1; ++c) sum += cnt[c * E + e];
+    wave_sum[wave * E + e] = sum;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      int32_t v = wave_sum[w * E + e];
+      wave_sum[w * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+    a.counts[e] = run;
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) {
+    int32_t run = wave_sum[wave * E + e];
+    for (int64_t c = c0; c < c1; ++c) {
+      int32_t v = cnt[c * E + e];
+      cnt[c * E + e] = run;
+      run += v;
+    }
+  }
+  if (wave == 0)
+    wave_scan_experts(counts, E, a.offsets, offs, a.mt1, a.tile_off1, a.tiles1, a.mt2, a.tile_off2, a.tiles2);
+  __threadfence_block();
+  __syncthreads();
+  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = a.lexp[s];
+    if (e >= 0) {
+      const int32_t pos = offs[e] + cnt[(s / 64) * E + e] + a.rank[s];
+      a.sorted[pos] = (int32_t)s;
+      a.inv[s] = pos;
+    } else {
+      a.inv[s] = -1;
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
-  const int64_t S = a.T * (int64_t)a.top_k;
-  int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < S) scatter_slot(a, s, a.chunk_cnt, a.offsets);
+namespace {
+size_t small_lds_bytes(int64_t S, int64_t E) {
+  const int64_t nchunk = (S + 63) / 64;
+  return (size_t)(2 * S + nchunk * E + 2 * E + 1) * sizeof(int32_t);
 }
-
-size_t route_fused_lds_bytes(int64_t S, int64_t E_local) {
-  int64_t nchunk = (S + 63) / 64;
-  return (size_t)(nchunk * E_local + 16 * E_local + E_local + 2048) * sizeof(int32_t);
-}
+int64_t gcd64(int64_t x, int64_t y) { return y ? gcd64(y, x % y) : x; }
+}  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int64_t S = a.T * (int64_t)a.top_k;
   if (S == 0) return hipSuccess;
-  size_t fused_lds = route_fused_lds_bytes(S, a.E_local);
-  if (fused_lds <= kRouteFusedMaxLds) {
-    hipLaunchKernelGGL(route_fused_kernel, dim3(1), dim3(1024), fused_lds, stream, a);
+  const int64_t work = a.T * ((a.E_global + 15) / 16) * a.top_k;  // per-lane compare rounds
+  const size_t lds = small_lds_bytes(S, a.E_local);
+  if (lds <= kRouteFusedMaxLds && work <= 8192) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), lds, stream, a);
     return hipGetLastError();
   }
-  const int64_t nchunk = (S + 63) / 64;
-  hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(route_chunk_kernel, dim3((unsigned)((nchunk + 3) / 4)), dim3(256), 0, stream, a);
-  size_t scan_lds = (size_t)(16 * a.E_local + a.E_local + 2048) * sizeof(int32_t);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), scan_lds, stream, a);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, stream, a);
+  // tokens per workgroup: a multiple of 64/gcd(64,k) (whole chunks), at least 16
+  int64_t unit = 64 / gcd64(64, a.top_k);
+  int64_t tpb = unit;
+  while (tpb < 16) tpb += unit;
+  const int64_t nblk = (a.T + tpb - 1) / tpb;
+  hipLaunchKernelGGL(route_topk_chunk_kernel, dim3((unsigned)nblk), dim3(256),
+                     (size_t)(tpb * a.top_k) * sizeof(int32_t), stream, a, (int)tpb);
+  const size_t scan_lds = (size_t)(16 * a.E_local + 2 * a.E_local + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL(route_scan_scatter_kernel, dim3(1), dim3(1024), scan_lds, stream, a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,7 @@ def ws_status(d, k=2):
     ({"H": 500}, 2, UNSUPPORTED_SHAPE), ({"I": 200}, 2, UNSUPPORTED_SHAPE),
     ({"T": -1}, 2, UNSUPPORTED_SHAPE), ({"first_local": 4}, 2, UNSUPPORTED_SHAPE),
     ({"first_local": -1}, 2, UNSUPPORTED_SHAPE), ({"E_global": 2048, "E_local": 8}, 2, UNSUPPORTED_SHAPE),
+    ({"E_global": 513, "E_local": 8}, 2, UNSUPPORTED_SHAPE), ({"E_global": 512, "E_local": 8}, 2, OK),
     ({}, -1, BAD_TOP_K), ({}, 9, BAD_TOP_K), ({"E_global": 64, "E_local": 64}, 33, BAD_TOP_K),
     ({"T": 1 << 40}, 8, SHAPE_OVERFLOW), ({"T": 1 << 60, "H": 1 << 10}, 2, SHAPE_OVERFLOW),
     ({"first_local": (1 << 63) - 4}, 2, SHAPE_OVERFLOW),
