@@ -104,6 +104,7 @@ int64_t max_tiles(const Shape& s, int mt) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, w, lexp, rank, sorted, inv, chunk_cnt, counts, offsets, tile1, tile2, tiles1, tiles2;
+  size_t pos_tok, pos_w, tile_tok;
   size_t act, out32, ybuf, xq, xs, actq, acts;
   size_t total;
 };
@@ -131,7 +132,10 @@ Layout layout_of(const Shape& s) {
     const size_t nt = (size_t)max_tiles(s, 16 * p.ms);
     L.tiles1 = take(nt * 16);
     L.tiles2 = take(nt * 16);
+    L.tile_tok = p.ms == 1 ? take(nt * 16 * 4) : 0;
   }
+  L.pos_tok = take(S * 4);
+  L.pos_w = take(S * 4);
   L.act = take(S * (size_t)s.I * 2);
   L.out32 = s.ordered ? 0 : take((size_t)s.T * (size_t)s.H * 4);
   L.ybuf = s.ordered ? take(S * (size_t)s.H * 4) : 0;
@@ -203,6 +207,9 @@ RouteArgs route_args(const Shape& s, const float* logits, void* ws, const Layout
   r.tile_off2 = at<int32_t>(ws, L.tile2);
   r.tiles1 = at<int4>(ws, L.tiles1);
   r.tiles2 = at<int4>(ws, L.tiles2);
+  r.pos_tok = at<int32_t>(ws, L.pos_tok);
+  r.pos_w = at<float>(ws, L.pos_w);
+  r.tile_tok = L.tile_tok ? at<int32_t>(ws, L.tile_tok) : nullptr;
   r.sorted = at<int32_t>(ws, L.sorted);
   r.inv = at<int32_t>(ws, L.inv);
   return r;
@@ -261,6 +268,9 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.counts = r.counts;
   g.offsets = r.offsets;
   g.route_w = r.w;
+  g.pos_tok = r.pos_tok;
+  g.pos_w = r.pos_w;
+  g.tile_tok = r.tile_tok;
   g.top_k = (int32_t)s.k;
   g.E_local = (int32_t)s.El;
   g.clamp_limit = clamp_limit;

@@ -1,16 +1,21 @@
 // Grouped GEMMs for token tiles of at most 16 rows (decode and small expert
-// segments): the weight stream is the whole cost, so each workgroup takes one
-// (expert tile, 16-feature block) and splits K across its waves.  Every wave
-// issues all of its loads -- the packed weight blocks of its K range and the
-// matching activation operands -- before its first MFMA, so a resident
-// workgroup keeps its whole weight tile in flight; partial sums meet in LDS
-// and are added in a fixed wave order (deterministic).
+// segments): the weight stream is the whole cost.  The work is a list of units
+// (expert tile, 16-feature block), all of the same weight size; a persistent
+// grid of resident workgroups takes equal contiguous shares of that list, so
+// every workgroup streams from the start of the kernel to its end and none is
+// left running alone in a tail.  Inside a workgroup K is split across the
+// waves; each wave keeps a ring of D unit slices in flight (unit u+D-1 loads
+// while unit u is computed) across unit and tile boundaries; partial sums meet
+// in LDS and are added in a fixed wave order (deterministic).
 //
 // Weight unpack and the MX block scale are applied once per weight element
 // per step, in registers (campaign page "glm53-mxfp4-mi355x", section "Serving
 // throughput": that per-element cost is what MXFP4 adds).
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -21,15 +26,22 @@ namespace {
 
 __device__ __forceinline__ u32x4_t ldg16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
-__device__ __forceinline__ bool tile_of(const GemmArgs& a, int tile, int* e, int* rows, int64_t* p0) {
-  const int n = a.tile_off[a.E_local];
-  const int4 ti = a.tiles[tile < n ? tile : 0];   // independent of n: both loads in flight together
-  if (tile >= n) return false;
-  *e = ti.x;
-  *rows = ti.y;
-  *p0 = ti.z;
-  return true;
+// Tile-table reads are wave-uniform and the table is constant while these
+// kernels run, so they go through the constant address space (scalar loads,
+// counted apart from the vector loads of the weight stream).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int tile_count(const GemmArgs& a) {
+  return ((const_i32*)a.tile_off)[a.E_local];
 }
+__device__ __forceinline__ int4 tile_entry(const GemmArgs& a, int t) {
+  const_i32* p = (const_i32*)a.tiles + 4 * (int64_t)t;
+  return make_int4(p[0], p[1], p[2], p[3]);
+}
+
+// A scale dword holds the scales of 4 k-tiles (one per byte).  With KPW
+// dividing 4 a wave's k-tiles [w*KPW, w*KPW + KPW) lie in one dword.
+template <int KPW>
+constexpr bool kOneScaleWord = (4 % KPW) == 0;
 
 // One wave's slice of one weight unit: NG row groups x KPW k-tiles (packed
 // codes) plus the scale dwords covering those k-tiles.
@@ -53,76 +65,84 @@ struct ASlice<KPW, true> {
   uint32_t as[KPW];
 };
 
-// k-tiles past KT are clamped to KT-1 (a valid address: no branch around a
-// load) and contribute zero in compute_slice.
+// Weight slices are buffer loads against a descriptor that spans the unit's NG
+// adjacent row groups; a unit past the workgroup's share gets an empty
+// descriptor, whose loads return zeros without touching memory.  Loads carry
+// the non-temporal hint (the stream is read once per step).  k-tiles past KT
+// are clamped to KT-1 and contribute zero in compute_slice.
+constexpr int kNonTemporal = 2;
 template <int NG, int KPW>
-__device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, const uint8_t* const (&wc)[NG],
-                                            const uint8_t* const (&wsb)[NG], int kt0, int KT) {
+__device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t group_bytes, uint32_t group_sbytes, int kt0, int KT) {
   const int lane = lane_id();
 #pragma unroll
   for (int c = 0; c < KPW; ++c)
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      int kt = kt0 + c < KT ? kt0 + c : KT - 1;
-      t.w[c][gi] = ld_stream16(wc[gi] + (int64_t)kt * 1024 + lane * 16);
+      const int kt = kt0 + c < KT ? kt0 + c : KT - 1;
+      const uint32_t off = gi * group_bytes + (uint32_t)kt * 1024u + (uint32_t)lane * 16u;
+      t.w[c][gi] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kNonTemporal));
     }
+  int q0 = kt0 >> 2;
+  int q1 = (kt0 + KPW - 1) >> 2;
+  const int qmax = (KT - 1) >> 2;
+  q0 = q0 < qmax ? q0 : qmax;
+  q1 = q1 < qmax ? q1 : qmax;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    int q0 = kt0 >> 2;
-    int q1 = (kt0 + KPW - 1) >> 2;
-    int qmax = (KT - 1) >> 2;
-    q0 = q0 < qmax ? q0 : qmax;
-    q1 = q1 < qmax ? q1 : qmax;
-    t.sd[gi][0] = ld_stream4(wsb[gi] + (int64_t)q0 * 256 + lane * 4);
-    t.sd[gi][1] = ld_stream4(wsb[gi] + (int64_t)q1 * 256 + lane * 4);
+    const uint32_t base = gi * group_sbytes + (uint32_t)lane * 4u;
+    t.sd[gi][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q0 * 256u, 0, kNonTemporal);
+    if constexpr (!kOneScaleWord<KPW>)
+      t.sd[gi][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q1 * 256u, 0, kNonTemporal);
   }
 }
 
 // Activation operands are buffer loads: a lane whose tile row is past the
-// segment end passes an offset at the end of the buffer, which the buffer
-// range check turns into zeros without touching memory -- so the loads need no
-// branch and only valid rows generate traffic.
+// segment end, and every k-tile past K, uses an offset at or past the end of
+// the buffer (oob, soob = its size), which the buffer range check turns into
+// zeros without touching memory -- so the loads need no branch, their values
+// need no select (a select would force a wait right after the load), and only
+// valid rows generate traffic.
 template <int KPW>
 __device__ __forceinline__ void load_aslice(ASlice<KPW, false>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
-                                            __amdgpu_buffer_rsrc_t, uint32_t, int kt0, int KT) {
+                                            uint32_t oob, __amdgpu_buffer_rsrc_t, uint32_t, uint32_t, int kt0,
+                                            int KT) {
   const int g = lane_id() >> 4;
 #pragma unroll
   for (int c = 0; c < KPW; ++c)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      int kt = kt0 + c < KT ? kt0 + c : KT - 1;
-      uint32_t off = off0 + (uint32_t)(kt * kTileK + 32 * g + 8 * m) * 2u;
-      u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      t.av[c][m] = (kt0 + c < KT) ? v : z;
+      const uint32_t off = kt0 + c < KT ? off0 + (uint32_t)((kt0 + c) * kTileK + 32 * g + 8 * m) * 2u : oob;
+      t.av[c][m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
 }
 template <int KPW>
 __device__ __forceinline__ void load_aslice(ASlice<KPW, true>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
-                                            __amdgpu_buffer_rsrc_t rss, uint32_t soff0, int kt0, int KT) {
+                                            uint32_t oob, __amdgpu_buffer_rsrc_t rss, uint32_t soff0,
+                                            uint32_t soob, int kt0, int KT) {
   const int g = lane_id() >> 4;
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
-    int kt = kt0 + c < KT ? kt0 + c : KT - 1;
-    u32x4_t v = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + (uint32_t)(4 * kt + g) * 16u, 0, 0));
-    uint32_t sv = __builtin_amdgcn_raw_buffer_load_b8(rss, soff0 + (uint32_t)(4 * kt + g), 0, 0);
-    u32x4_t z = {0u, 0u, 0u, 0u};
-    t.av[c] = (kt0 + c < KT) ? v : z;
-    t.as[c] = sv;
+    const bool kin = kt0 + c < KT;
+    const uint32_t off = kin ? off0 + (uint32_t)(4 * (kt0 + c) + g) * 16u : oob;
+    const uint32_t soff = kin ? soff0 + (uint32_t)(4 * (kt0 + c) + g) : soob;
+    t.av[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    t.as[c] = __builtin_amdgcn_raw_buffer_load_b8(rss, soff, 0, 0);
   }
 }
 
 // acc[g] += A(16 rows x this wave's K range) * W(row group g)^T.  Every k-tile
 // slot runs (no branch); slots past K contribute zero through both operands.
-template <int NG, int KPW>
+// FULL: the caller has checked that all KPW k-tiles are inside K, so no
+// operand needs the zeroing select.
+template <bool FULL, int NG, int KPW>
 __device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const ASlice<KPW, false>& at, int kt0,
                                               int KT, f32x4_t (&acc)[NG]) {
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
-    const bool kin = kt0 + c < KT;
+    const bool kin = FULL || kt0 + c < KT;
     const int kt = kin ? kt0 + c : KT - 1;
-    const int which = ((kt >> 2) == (kt0 >> 2)) ? 0 : 1;
+    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       float sc = e8m0_scale_operand((wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu);
@@ -137,14 +157,14 @@ __device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const A
     }
   }
 }
-template <int NG, int KPW>
+template <bool FULL, int NG, int KPW>
 __device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const ASlice<KPW, true>& at, int kt0,
                                               int KT, f32x4_t (&acc)[NG]) {
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
-    const bool kin = kt0 + c < KT;
+    const bool kin = FULL || kt0 + c < KT;
     const int kt = kin ? kt0 + c : KT - 1;
-    const int which = ((kt >> 2) == (kt0 >> 2)) ? 0 : 1;
+    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       uint32_t sb = (wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu;
@@ -185,236 +205,340 @@ __device__ __forceinline__ bool reduce_to_wave0(f32x4_t (&acc)[NG], float* red, 
 
 }  // namespace
 
-// gate_up for tiles of <= 16 rows.  grid: x = tile upper bound, y = I / (16*FPW).
-// A workgroup keeps one token tile (its activation operands load once) and
-// walks FPW blocks of 16 gate + 16 up features with a D-deep ring of weight
-// slices: block f+D-1 is loading while block f is computed.  Wave w takes
-// k-tiles [w*KPW, w*KPW + KPW).
-template <int KPW, int FPW, int D, bool A4>
+// Units are numbered tile-major, u = tile * FB + feature block.  A share is
+// cut at tile boundaries into segments; each segment loads its tile's
+// activation operands once, then walks its units with a ring of D weight
+// slices: unit u+D-1 loads while unit u is computed.  Slots past the segment
+// end load through an empty descriptor (no traffic).  Nothing loaded is
+// carried from one segment to the next, so no loaded register has to be
+// copied at a join (such a copy waits for every load in flight).
+__device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue) {
+  *ub = U * blockIdx.x / gridDim.x;
+  *ue = U * (blockIdx.x + 1) / gridDim.x;
+}
+
+// gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
+// up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
+template <int KPW, int D, bool A4>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
   extern __shared__ float red[];  // [2][waves][2][64][4]
   if (a.zero_buf) {
-    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
-    const int64_t tid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
     for (int64_t i = tid; i < a.zero_n / 4; i += nthreads) reinterpret_cast<f32x4_t*>(a.zero_buf)[i] = z;
   }
-  int e, rows;
-  int64_t p0;
-  if (!tile_of(a, blockIdx.x, &e, &rows, &p0)) return;
   const int lane = lane_id();
+  const int r = lane & 15;
   const int wave = threadIdx.x >> 6;
   const int NW = blockDim.x >> 6;
   const int64_t H = a.K, I = a.N / 2;
   const int KT = (int)(H / kTileK);
   const int kt0 = wave * KPW;
-  const int64_t fb0 = (int64_t)blockIdx.y * FPW;
-  const uint8_t* ebase = a.w_codes + (int64_t)e * codes_per_expert(a.N, H);
-  const uint8_t* esb = a.w_scales + (int64_t)e * scales_per_expert(a.N, H);
-  auto load_unit = [&](int f, WSlice<2, KPW>& w) {
-    const int64_t fgi = fb0 + f;
-    const uint8_t* wc[2] = {ebase + codes_tile_offset(2 * fgi, 0, H), ebase + codes_tile_offset(2 * fgi + 1, 0, H)};
-    const uint8_t* wsb[2] = {esb + scales_group_offset(2 * fgi, 0, H), esb + scales_group_offset(2 * fgi + 1, 0, H)};
-    load_wslice(w, wc, wsb, kt0, KT);
-  };
-  WSlice<2, KPW> wt[D];
+  const bool full = kt0 + KPW <= KT;  // all of this wave's k-tiles inside K
+  const int FB = (int)(I / 16);
+  int64_t ub, ue;
+  share_of((int64_t)tile_count(a) * FB, &ub, &ue);
+  const uint32_t gbytes = (uint32_t)(16 * (H / 2));
+  const uint32_t gsbytes = (uint32_t)(scale_groups(H) * 256);
+  const int64_t cpe = codes_per_expert(a.N, H), spe = scales_per_expert(a.N, H);
+  // LDS partial buffers alternate strictly from unit to unit (padding slots
+  // included), so a buffer is rewritten only after the barrier that follows
+  // wave 0's reads of it
+  int phase = 0;
+  for (int64_t sb = ub; sb < ue;) {
+    const int t = (int)(sb / FB);
+    const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
+    const int4 ti = tile_entry(a, t);
+    const int rows = ti.y;
+    const int64_t p0 = ti.z;
+    const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
+    const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
+    const int fb0 = (int)(sb - (int64_t)t * FB);
+    const int nu = (int)(se - sb);
+    auto load_unit = [&](int i, WSlice<2, KPW>& w) {
+      const int fb = fb0 + i;
+      const bool ok = i < nu;
+      load_wslice(w, make_rsrc(ecodes + codes_tile_offset(2 * fb, 0, H), ok ? 2 * gbytes : 0u),
+                  make_rsrc(escales + scales_group_offset(2 * fb, 0, H), ok ? 2 * gsbytes : 0u), gbytes, gsbytes,
+                  kt0, KT);
+    };
+    WSlice<2, KPW> wt[D];
 #pragma unroll
-  for (int f = 0; f < D - 1 && f < FPW; ++f) load_unit(f, wt[f]);
-  const int r = lane & 15;
-  const bool valid = r < rows;
-  const int64_t tok = a.sorted[p0 + (valid ? r : 0)] / a.top_k;
-  ASlice<KPW, A4> at;
-  if constexpr (A4) {
-    const uint32_t nb = (uint32_t)(a.a_rows * (H / 2)), ns = (uint32_t)(a.a_rows * (H / 32));
-    load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * (H / 2)) : nb, make_rsrc(a.a_scales, ns),
-                valid ? (uint32_t)(tok * (H / 32)) : ns, kt0, KT);
-  } else {
-    const uint32_t nb = (uint32_t)(a.a_rows * H * 2);
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
-    load_aslice(at, rs, valid ? (uint32_t)(tok * H * 2) : nb, rs, 0u, kt0, KT);
-  }
-#pragma unroll
-  for (int f = 0; f < FPW; ++f) {
-    if (f + D - 1 < FPW) load_unit(f + D - 1, wt[(f + D - 1) % D]);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    compute_slice(wt[f % D], at, kt0, KT, acc);
-    float* rb = red + (f & 1) * (NW * 2 * 64 * 4);
-    if (reduce_to_wave0<2>(acc, rb, NW)) {
-      const int64_t n = (fb0 + f) * 16 + r;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int row = 4 * (lane >> 4) + q;
-        if (row < rows) {
-          float v = swiglu_clamped(acc[0][q], acc[1][q], a.clamp_limit);
-          a.act[(p0 + row) * I + n] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
+    for (int j = 0; j < D - 1; ++j) load_unit(j, wt[j]);
+    // this lane's tile row and its token (garbage past the tile's rows: unused)
+    const int32_t tok_raw = a.tile_tok[(int64_t)t * 16 + r];
+    const bool valid = r < rows;
+    const int64_t tok = valid ? tok_raw : 0;
+    ASlice<KPW, A4> at;
+    if constexpr (A4) {
+      const uint32_t nb = (uint32_t)(a.a_rows * (H / 2)), ns = (uint32_t)(a.a_rows * (H / 32));
+      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * (H / 2)) : nb, nb,
+                  make_rsrc(a.a_scales, ns), valid ? (uint32_t)(tok * (H / 32)) : ns, ns, kt0, KT);
+    } else {
+      const uint32_t nb = (uint32_t)(a.a_rows * H * 2);
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
+      load_aslice(at, rs, valid ? (uint32_t)(tok * H * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
     }
-  }
-}
-
-// down + combine for tiles of <= 16 rows.  grid: x = tile upper bound,
-// y = H / (16*NG*FPW); same walk over FPW blocks of 16*NG output features.
-template <int KPW, int NG, int FPW, int D, bool A4, bool ORDERED>
-__global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
-  extern __shared__ float red[];  // [2][waves][NG][64][4]
-  int e, rows;
-  int64_t p0;
-  if (!tile_of(a, blockIdx.x, &e, &rows, &p0)) return;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int NW = blockDim.x >> 6;
-  const int64_t I = a.K, H = a.N;
-  const int KT = (int)(I / kTileK);
-  const int kt0 = wave * KPW;
-  const int64_t fb0 = (int64_t)blockIdx.y * FPW;
-  const uint8_t* ebase = a.w_codes + (int64_t)e * codes_per_expert(H, I);
-  const uint8_t* esb = a.w_scales + (int64_t)e * scales_per_expert(H, I);
-  auto load_unit = [&](int f, WSlice<NG, KPW>& w) {
-    const uint8_t* wc[NG];
-    const uint8_t* wsb[NG];
+    for (int i0 = 0; i0 < nu; i0 += D) {
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      wc[gi] = ebase + codes_tile_offset((fb0 + f) * NG + gi, 0, I);
-      wsb[gi] = esb + scales_group_offset((fb0 + f) * NG + gi, 0, I);
-    }
-    load_wslice(w, wc, wsb, kt0, KT);
-  };
-  WSlice<NG, KPW> wt[D];
+      for (int j = 0; j < D; ++j) {
+        const int i = i0 + j;
+        load_unit(i + D - 1, wt[(j + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (full)
+          compute_slice<true>(wt[j], at, kt0, KT, acc);
+        else
+          compute_slice<false>(wt[j], at, kt0, KT, acc);
+        float* rb = red + (phase++ & 1) * (NW * 2 * 64 * 4);
+        if (reduce_to_wave0<2>(acc, rb, NW) && i < nu) {
+          const int64_t nn = (int64_t)(fb0 + i) * 16 + r;
 #pragma unroll
-  for (int f = 0; f < D - 1 && f < FPW; ++f) load_unit(f, wt[f]);
-  const int r = lane & 15;
-  const bool valid = r < rows;
-  const int64_t pr = p0 + r;
-  ASlice<KPW, A4> at;
-  if constexpr (A4) {
-    const uint32_t nb = (uint32_t)(a.a_rows * (I / 2)), ns = (uint32_t)(a.a_rows * (I / 32));
-    load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * (I / 2)) : nb, make_rsrc(a.a_scales, ns),
-                valid ? (uint32_t)(pr * (I / 32)) : ns, kt0, KT);
-  } else {
-    const uint32_t nb = (uint32_t)(a.a_rows * I * 2);
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
-    load_aslice(at, rs, valid ? (uint32_t)(pr * I * 2) : nb, rs, 0u, kt0, KT);
-  }
-  // combine operands of this lane's four rows
-  int64_t tok[4];
-  float wgt[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 4 * (lane >> 4) + q;
-    const int32_t slot = a.sorted[p0 + (row < rows ? row : 0)];
-    tok[q] = slot / a.top_k;
-    wgt[q] = a.route_w[slot];
-  }
-#pragma unroll
-  for (int f = 0; f < FPW; ++f) {
-    if (f + D - 1 < FPW) load_unit(f + D - 1, wt[(f + D - 1) % D]);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4_t acc[NG];
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) acc[gi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    compute_slice(wt[f % D], at, kt0, KT, acc);
-    float* rb = red + (f & 1) * (NW * NG * 64 * 4);
-    if (reduce_to_wave0<NG>(acc, rb, NW)) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 4 * (lane >> 4) + q;
-        if (row < rows) {
-          const int64_t p = p0 + row;
-#pragma unroll
-          for (int gi = 0; gi < NG; ++gi) {
-            const int64_t n = ((fb0 + f) * NG + gi) * 16 + r;
-            if constexpr (ORDERED) {
-              a.ybuf[p * H + n] = acc[gi][q];
-            } else {
-              float prod = wgt[q] * acc[gi][q];
-              unsafeAtomicAdd(a.out32 + tok[q] * H + n, prod);
+          for (int q = 0; q < 4; ++q) {
+            const int row = 4 * (lane >> 4) + q;
+            if (row < rows) {
+              const float v = swiglu_clamped(acc[0][q], acc[1][q], a.clamp_limit);
+              a.act[(p0 + row) * I + nn] = (uint16_t)f32_to_bf16_bits(v);
             }
           }
         }
       }
     }
+    sb = se;
+  }
+}
+
+// down + combine: unit = (tile, 16*NG output features).  Atomic combine adds
+// weight * y into out32[token]; ORDERED writes y per sorted position to ybuf.
+template <int KPW, int NG, int D, bool A4, bool ORDERED>
+__global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
+  extern __shared__ float red[];  // [2][waves][NG][64][4]
+  const int lane = lane_id();
+  const int r = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  const int NW = blockDim.x >> 6;
+  const int64_t I = a.K, H = a.N;
+  const int KT = (int)(I / kTileK);
+  const int kt0 = wave * KPW;
+  const bool full = kt0 + KPW <= KT;
+  const int FB = (int)(H / (16 * NG));
+  int64_t ub, ue;
+  share_of((int64_t)tile_count(a) * FB, &ub, &ue);
+  const uint32_t gbytes = (uint32_t)(16 * (I / 2));
+  const uint32_t gsbytes = (uint32_t)(scale_groups(I) * 256);
+  const int64_t cpe = codes_per_expert(H, I), spe = scales_per_expert(H, I);
+  // LDS partial buffers alternate strictly from unit to unit (padding slots
+  // included), so a buffer is rewritten only after the barrier that follows
+  // wave 0's reads of it
+  int phase = 0;
+  for (int64_t sb = ub; sb < ue;) {
+    const int t = (int)(sb / FB);
+    const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
+    const int4 ti = tile_entry(a, t);
+    const int rows = ti.y;
+    const int64_t p0 = ti.z;
+    const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
+    const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
+    const int fb0 = (int)(sb - (int64_t)t * FB);
+    const int nu = (int)(se - sb);
+    auto load_unit = [&](int i, WSlice<NG, KPW>& w) {
+      const int fb = fb0 + i;
+      const bool ok = i < nu;
+      load_wslice(w, make_rsrc(ecodes + codes_tile_offset(fb * NG, 0, I), ok ? NG * gbytes : 0u),
+                  make_rsrc(escales + scales_group_offset(fb * NG, 0, I), ok ? NG * gsbytes : 0u), gbytes, gsbytes,
+                  kt0, KT);
+    };
+    WSlice<NG, KPW> wt[D];
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load_unit(j, wt[j]);
+    const bool valid = r < rows;
+    const int64_t pr = p0 + r;
+    ASlice<KPW, A4> at;
+    if constexpr (A4) {
+      const uint32_t nb = (uint32_t)(a.a_rows * (I / 2)), ns = (uint32_t)(a.a_rows * (I / 32));
+      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * (I / 2)) : nb, nb,
+                  make_rsrc(a.a_scales, ns), valid ? (uint32_t)(pr * (I / 32)) : ns, ns, kt0, KT);
+    } else {
+      const uint32_t nb = (uint32_t)(a.a_rows * I * 2);
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
+      load_aslice(at, rs, valid ? (uint32_t)(pr * I * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
+    }
+    // token and router weight of this lane's four output rows
+    int64_t tok[4];
+    float wgt[4];
+    if constexpr (!ORDERED) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 4 * (lane >> 4) + q;
+        const int64_t pp = p0 + (row < rows ? row : 0);
+        tok[q] = a.pos_tok[pp];
+        wgt[q] = a.pos_w[pp];
+      }
+    }
+    for (int i0 = 0; i0 < nu; i0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int i = i0 + j;
+        load_unit(i + D - 1, wt[(j + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t acc[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) acc[gi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if (full)
+          compute_slice<true>(wt[j], at, kt0, KT, acc);
+        else
+          compute_slice<false>(wt[j], at, kt0, KT, acc);
+        float* rb = red + (phase++ & 1) * (NW * NG * 64 * 4);
+        if (reduce_to_wave0<NG>(acc, rb, NW) && i < nu) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = 4 * (lane >> 4) + q;
+            if (row < rows) {
+#pragma unroll
+              for (int gi = 0; gi < NG; ++gi) {
+                const int64_t nn = ((int64_t)(fb0 + i) * NG + gi) * 16 + r;
+                if constexpr (ORDERED) {
+                  a.ybuf[(p0 + row) * H + nn] = acc[gi][q];
+                } else {
+                  unsafeAtomicAdd(a.out32 + tok[q] * H + nn, wgt[q] * acc[gi][q]);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    sb = se;
   }
 }
 
 // ------------------------------------------------------------------ launchers
 //
-// Variants: (KPW, FPW, D) = k-tiles per wave, feature blocks per workgroup,
-// weight ring depth.  Default: KPW 4 (5 or 8 when K needs it to fit 8 waves),
-// FPW 4, D 2 -- the fastest of the measured set on the decode shape.
-// MXFP4_MOE_DECODE_VARIANT (tests and benchmarks only) picks another, e.g.
-// "k2d3f8" = KPW 2, FPW 8, D 3.
+// Variants: (KPW, D) = k-tiles per wave, weight ring depth.  Default: KPW 4
+// (5 or 8 when K needs it to fit 8 waves), D 2.  MXFP4_MOE_DECODE_VARIANT
+// (tests and benchmarks only) picks another, "k<KPW>d<D>" with KPW 2 or 4
+// and D 2, 3, 4 or 6.
+// MXFP4_MOE_DECODE_WGS_PER_CU caps the resident workgroups per CU.
 namespace {
 struct Variant {
-  int kpw, fpw, d;
+  int kpw, d;
 };
 
 Variant pick(int64_t K) {
   const int64_t KT = K / kTileK;
-  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 4, 2};
+  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 2};
   if (const char* env = getenv("MXFP4_MOE_DECODE_VARIANT")) {
-    if (!strcmp(env, "k4d2") && KT <= 32) v = {4, 4, 2};
-    else if (!strcmp(env, "k4d3") && KT <= 32) v = {4, 4, 3};
-    else if (!strcmp(env, "k2d2") && KT <= 16) v = {2, 4, 2};
-    else if (!strcmp(env, "k2d3f8") && KT <= 16) v = {2, 8, 3};
+    int kpw = 0, d = 0;
+    if (sscanf(env, "k%dd%d", &kpw, &d) == 2 && (kpw == 2 || kpw == 4) && (d == 2 || d == 3 || d == 4 || d == 6) &&
+        (KT + kpw - 1) / kpw <= 8)
+      v = {kpw, d};
   }
   return v;
 }
 
-template <int KPW, int FPW, int D>
-hipError_t gate_up_v(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
-  const int nw = (int)((a.K / kTileK + KPW - 1) / KPW);
-  const int64_t fb = a.N / 2 / 16;
-  if (nw > 8 || fb % FPW) return hipErrorInvalidValue;
-  dim3 grid((unsigned)max_tiles, (unsigned)(fb / FPW));
-  size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
-  if (a4) hipLaunchKernelGGL((gate_up_ksplit_kernel<KPW, FPW, D, true>), grid, dim3(nw * 64), lds, s, a);
-  else hipLaunchKernelGGL((gate_up_ksplit_kernel<KPW, FPW, D, false>), grid, dim3(nw * 64), lds, s, a);
+// Workgroups of this kernel that are resident at once on the current device
+// (occupancy x CUs), cached per (device, kernel, block, LDS).
+struct GridKey {
+  int dev;
+  const void* fn;
+  int block;
+  size_t lds;
+  int grid;
+};
+std::mutex g_grid_mu;
+GridKey g_grid_cache[64];
+int g_grid_n = 0;
+
+hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(g_grid_mu);
+    for (int i = 0; i < g_grid_n; ++i) {
+      const GridKey& k = g_grid_cache[i];
+      if (k.dev == dev && k.fn == fn && k.block == block && k.lds == lds) {
+        *grid = k.grid;
+        return hipSuccess;
+      }
+    }
+  }
+  int cus = 0, per_cu = 0;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds)) != hipSuccess) return e;
+  if (const char* env = getenv("MXFP4_MOE_DECODE_WGS_PER_CU")) {
+    const int cap = atoi(env);
+    if (cap > 0 && cap < per_cu) per_cu = cap;
+  }
+  if (per_cu < 1) per_cu = 1;
+  *grid = cus * per_cu;
+  std::lock_guard<std::mutex> lk(g_grid_mu);
+  if (g_grid_n < 64) g_grid_cache[g_grid_n++] = GridKey{dev, fn, block, lds, *grid};
+  return hipSuccess;
+}
+
+template <typename Kernel>
+hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, const GemmArgs& a,
+                             hipStream_t s) {
+  int grid = 0;
+  hipError_t e = resident_grid(reinterpret_cast<const void*>(kernel), nw * 64, lds, &grid);
+  if (e != hipSuccess) return e;
+  if ((int64_t)grid > max_units) grid = (int)max_units;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int KPW, int FPW, int D>
+template <int KPW, int D>
+hipError_t gate_up_v(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+  const int nw = (int)((a.K / kTileK + KPW - 1) / KPW);
+  const int64_t fb = a.N / 2 / 16;
+  if (nw > 8) return hipErrorInvalidValue;
+  const size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
+  return a4 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, true>, nw, lds, max_tiles * fb, a, s)
+            : launch_persistent(gate_up_ksplit_kernel<KPW, D, false>, nw, lds, max_tiles * fb, a, s);
+}
+
+template <int KPW, int D>
 hipError_t down_v(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
   constexpr int NG = 2;
   const int nw = (int)((a.K / kTileK + KPW - 1) / KPW);
   const int64_t fb = a.N / 16 / NG;
-  if (nw > 8 || fb % FPW) return hipErrorInvalidValue;
-  dim3 grid((unsigned)max_tiles, (unsigned)(fb / FPW));
-  size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
+  if (nw > 8) return hipErrorInvalidValue;
+  const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
+  const int64_t mu = max_tiles * fb;
   if (a4) {
-    if (ordered) hipLaunchKernelGGL((down_ksplit_kernel<KPW, NG, FPW, D, true, true>), grid, dim3(nw * 64), lds, s, a);
-    else hipLaunchKernelGGL((down_ksplit_kernel<KPW, NG, FPW, D, true, false>), grid, dim3(nw * 64), lds, s, a);
-  } else {
-    if (ordered) hipLaunchKernelGGL((down_ksplit_kernel<KPW, NG, FPW, D, false, true>), grid, dim3(nw * 64), lds, s, a);
-    else hipLaunchKernelGGL((down_ksplit_kernel<KPW, NG, FPW, D, false, false>), grid, dim3(nw * 64), lds, s, a);
+    return ordered ? launch_persistent(down_ksplit_kernel<KPW, NG, D, true, true>, nw, lds, mu, a, s)
+                   : launch_persistent(down_ksplit_kernel<KPW, NG, D, true, false>, nw, lds, mu, a, s);
   }
-  return hipGetLastError();
+  return ordered ? launch_persistent(down_ksplit_kernel<KPW, NG, D, false, true>, nw, lds, mu, a, s)
+                 : launch_persistent(down_ksplit_kernel<KPW, NG, D, false, false>, nw, lds, mu, a, s);
 }
 }  // namespace
+
+#define MXMOE_DECODE_VARIANTS(F) \
+  F(2, 2) F(2, 3) F(2, 4) F(2, 6) F(4, 2) F(4, 3) F(4, 4) F(4, 6)
 
 hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const Variant v = pick(a.K);
-  if (v.kpw == 2 && v.fpw == 4 && v.d == 3) return gate_up_v<2, 4, 3>(a, max_tiles, a4, s);
-  if (v.kpw == 2 && v.fpw == 4 && v.d == 2) return gate_up_v<2, 4, 2>(a, max_tiles, a4, s);
-  if (v.kpw == 2 && v.fpw == 8) return gate_up_v<2, 8, 3>(a, max_tiles, a4, s);
-  if (v.kpw == 4 && v.d == 2) return gate_up_v<4, 4, 2>(a, max_tiles, a4, s);
-  if (v.kpw == 4) return gate_up_v<4, 4, 3>(a, max_tiles, a4, s);
-  if (v.kpw == 5) return gate_up_v<5, 4, 2>(a, max_tiles, a4, s);
-  return gate_up_v<8, 4, 2>(a, max_tiles, a4, s);
+#define F(KPW, D) \
+  if (v.kpw == KPW && v.d == D) return gate_up_v<KPW, D>(a, max_tiles, a4, s);
+  MXMOE_DECODE_VARIANTS(F)
+#undef F
+  if (v.kpw == 5) return gate_up_v<5, 2>(a, max_tiles, a4, s);
+  return gate_up_v<8, 2>(a, max_tiles, a4, s);
 }
 
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const Variant v = pick(a.K);
-  if (v.kpw == 2 && v.fpw == 4 && v.d == 3) return down_v<2, 4, 3>(a, max_tiles, a4, ordered, s);
-  if (v.kpw == 2 && v.fpw == 4 && v.d == 2) return down_v<2, 4, 2>(a, max_tiles, a4, ordered, s);
-  if (v.kpw == 2 && v.fpw == 8) return down_v<2, 8, 3>(a, max_tiles, a4, ordered, s);
-  if (v.kpw == 4 && v.d == 2) return down_v<4, 4, 2>(a, max_tiles, a4, ordered, s);
-  if (v.kpw == 4) return down_v<4, 4, 3>(a, max_tiles, a4, ordered, s);
-  if (v.kpw == 5) return down_v<5, 4, 2>(a, max_tiles, a4, ordered, s);
-  return down_v<8, 4, 2>(a, max_tiles, a4, ordered, s);
+#define F(KPW, D) \
+  if (v.kpw == KPW && v.d == D) return down_v<KPW, D>(a, max_tiles, a4, ordered, s);
+  MXMOE_DECODE_VARIANTS(F)
+#undef F
+  if (v.kpw == 5) return down_v<5, 2>(a, max_tiles, a4, ordered, s);
+  return down_v<8, 2>(a, max_tiles, a4, ordered, s);
 }
 
 }  // namespace mxmoe

@@ -27,6 +27,11 @@ struct RouteArgs {
   int4* tiles2;         // [tile bound 2]
   int32_t* sorted;      // [S]
   int32_t* inv;         // [S]
+  // per sorted position: token and router weight (what the down epilogue needs)
+  int32_t* pos_tok;     // [S]
+  float* pos_w;         // [S]
+  // per tile of height mt1 (== mt2 when set): the token of each of its rows
+  int32_t* tile_tok;    // [tile bound][16], or null
 };
 
 struct GemmArgs {
@@ -45,6 +50,9 @@ struct GemmArgs {
   const int32_t* tile_off;  // [E_local + 1]; tile_off[E_local] = number of tiles
   const int4* tiles;        // {expert, rows, first sorted position, 0} per tile
   const float* route_w;     // [S] (down: combine weights)
+  const int32_t* pos_tok;   // [S] token of sorted position p
+  const float* pos_w;       // [S] router weight of sorted position p
+  const int32_t* tile_tok;  // [tile bound][16] token of each row of a 16-row tile
   int32_t top_k, E_local;
   int64_t K, N;             // contraction length and weight rows (gate_up: N = 2I)
   float clamp_limit;
