@@ -69,32 +69,41 @@ struct ASlice<KPW, true> {
 // adjacent row groups; a unit past the workgroup's share gets an empty
 // descriptor, whose loads return zeros without touching memory.  Loads carry
 // the non-temporal hint (the stream is read once per step).  k-tiles past KT
-// are clamped to KT-1 and contribute zero in compute_slice.
+// are clamped to KT-1 and contribute zero in compute_refill.
 constexpr int kNonTemporal = 2;
 template <int NG, int KPW>
-__device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                            uint32_t group_bytes, uint32_t group_sbytes, int kt0, int KT) {
-  const int lane = lane_id();
+__device__ __forceinline__ void load_wcodes(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, uint32_t group_bytes,
+                                            int c, int kt0, int KT) {
+  const int kt = kt0 + c < KT ? kt0 + c : KT - 1;
+  const uint32_t off = (uint32_t)kt * 1024u + (uint32_t)lane_id() * 16u;
 #pragma unroll
-  for (int c = 0; c < KPW; ++c)
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const int kt = kt0 + c < KT ? kt0 + c : KT - 1;
-      const uint32_t off = gi * group_bytes + (uint32_t)kt * 1024u + (uint32_t)lane * 16u;
-      t.w[c][gi] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, kNonTemporal));
-    }
+  for (int gi = 0; gi < NG; ++gi)
+    t.w[c][gi] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, gi * group_bytes + off, 0, kNonTemporal));
+}
+template <int NG, int KPW>
+__device__ __forceinline__ void load_wscales(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rs, uint32_t group_sbytes,
+                                             int kt0, int KT) {
   int q0 = kt0 >> 2;
   int q1 = (kt0 + KPW - 1) >> 2;
   const int qmax = (KT - 1) >> 2;
   q0 = q0 < qmax ? q0 : qmax;
   q1 = q1 < qmax ? q1 : qmax;
+  const uint32_t lo = (uint32_t)lane_id() * 4u;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const uint32_t base = gi * group_sbytes + (uint32_t)lane * 4u;
+    const uint32_t base = gi * group_sbytes + lo;
     t.sd[gi][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q0 * 256u, 0, kNonTemporal);
     if constexpr (!kOneScaleWord<KPW>)
       t.sd[gi][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q1 * 256u, 0, kNonTemporal);
   }
+}
+template <int NG, int KPW>
+__device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t group_bytes, uint32_t group_sbytes, int kt0, int KT) {
+#pragma unroll
+  for (int c = 0; c < KPW; ++c) load_wcodes(t, rc, group_bytes, c, kt0, KT);
+  load_wscales(t, rs, group_sbytes, kt0, KT);
 }
 
 // Activation operands are buffer loads: a lane whose tile row is past the
@@ -131,35 +140,46 @@ __device__ __forceinline__ void load_aslice(ASlice<KPW, true>& t, __amdgpu_buffe
   }
 }
 
-// acc[g] += A(16 rows x this wave's K range) * W(row group g)^T.  Every k-tile
-// slot runs (no branch); slots past K contribute zero through both operands.
-// FULL: the caller has checked that all KPW k-tiles are inside K, so no
-// operand needs the zeroing select.
-template <bool FULL, int NG, int KPW>
-__device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const ASlice<KPW, false>& at, int kt0,
-                                              int KT, f32x4_t (&acc)[NG]) {
+// acc[g] += A(16 rows x this wave's K range) * W(row group g)^T, k-tile by
+// k-tile, and as each k-tile's registers are consumed, refill(c) loads the
+// same k-tile of a later unit into them (refill(-1): the scale dwords, which
+// are decoded into per-k-tile operands first).  The weight stream thus keeps
+// a steady amount in flight without a second register copy of the slice.
+// Slots past K contribute zero through both operands; FULL (every wave's
+// k-tiles inside K) drops the zeroing selects.
+template <bool FULL, int NG, int KPW, typename Refill>
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, false>& at, int kt0, int KT,
+                                               f32x4_t (&acc)[NG], Refill&& refill) {
+  float sc[KPW][NG];
+#pragma unroll
+  for (int c = 0; c < KPW; ++c) {
+    const int kt = FULL || kt0 + c < KT ? kt0 + c : KT - 1;
+    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) sc[c][gi] = e8m0_scale_operand((wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu);
+  }
+  refill(-1);
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
     const bool kin = FULL || kt0 + c < KT;
-    const int kt = kin ? kt0 + c : KT - 1;
-    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      float sc = e8m0_scale_operand((wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        u32x4_t b = __builtin_bit_cast(u32x4_t, unpack8_e2m1(wt.w[c][gi][m], sc));
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        b = kin ? b : z;
+        u32x4_t b = __builtin_bit_cast(u32x4_t, unpack8_e2m1(wt.w[c][gi][m], sc[c][gi]));
+        if constexpr (!FULL) b = kin ? b : (u32x4_t){0u, 0u, 0u, 0u};
         acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, at.av[c][m]),
                                                           __builtin_bit_cast(bf16x8_t, b), acc[gi], 0, 0, 0);
       }
     }
+    refill(c);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
-template <bool FULL, int NG, int KPW>
-__device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const ASlice<KPW, true>& at, int kt0,
-                                              int KT, f32x4_t (&acc)[NG]) {
+template <bool FULL, int NG, int KPW, typename Refill>
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, true>& at, int kt0, int KT,
+                                               f32x4_t (&acc)[NG], Refill&& refill) {
+  uint32_t sbyte[KPW][NG];
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
     const bool kin = FULL || kt0 + c < KT;
@@ -167,14 +187,25 @@ __device__ __forceinline__ void compute_slice(const WSlice<NG, KPW>& wt, const A
     const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      uint32_t sb = (wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu;
-      sb = kin ? sb : 127u;
-      i32x8_t A = {(int)at.av[c][0], (int)at.av[c][1], (int)at.av[c][2], (int)at.av[c][3], 0, 0, 0, 0};
-      u32x4_t wb = kin ? wt.w[c][gi] : (u32x4_t){0u, 0u, 0u, 0u};
-      i32x8_t B = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], 0, 0, 0, 0};
-      acc[gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[gi], 4, 4, 0, (int)at.as[c], 0,
-                                                                 (int)sb);
+      const uint32_t sb = (wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu;
+      sbyte[c][gi] = kin ? sb : 127u;
     }
+  }
+  refill(-1);
+#pragma unroll
+  for (int c = 0; c < KPW; ++c) {
+    const bool kin = FULL || kt0 + c < KT;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const i32x8_t A = {(int)at.av[c][0], (int)at.av[c][1], (int)at.av[c][2], (int)at.av[c][3], 0, 0, 0, 0};
+      u32x4_t wb = wt.w[c][gi];
+      if constexpr (!FULL) wb = kin ? wb : (u32x4_t){0u, 0u, 0u, 0u};
+      const i32x8_t B = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], 0, 0, 0, 0};
+      acc[gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[gi], 4, 4, 0, (int)at.as[c], 0,
+                                                                 (int)sbyte[c][gi]);
+    }
+    refill(c);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -208,8 +239,9 @@ __device__ __forceinline__ bool reduce_to_wave0(f32x4_t (&acc)[NG], float* red, 
 // Units are numbered tile-major, u = tile * FB + feature block.  A share is
 // cut at tile boundaries into segments; each segment loads its tile's
 // activation operands once, then walks its units with a ring of D weight
-// slices: unit u+D-1 loads while unit u is computed.  Slots past the segment
-// end load through an empty descriptor (no traffic).  Nothing loaded is
+// slices: unit i sits in slot i % D and, k-tile by k-tile as it is computed,
+// unit i + D is loaded into the same slot.  Slots past the segment end load
+// through an empty descriptor (no traffic).  Nothing loaded is
 // carried from one segment to the next, so no loaded register has to be
 // copied at a join (such a copy waits for every load in flight).
 __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue) {
@@ -219,7 +251,7 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue) {
 
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
 // up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
-template <int KPW, int D, bool A4>
+template <int KPW, int D, bool A4, bool FULL>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
   extern __shared__ float red[];  // [2][waves][2][64][4]
   if (a.zero_buf) {
@@ -235,7 +267,6 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
   const int64_t H = a.K, I = a.N / 2;
   const int KT = (int)(H / kTileK);
   const int kt0 = wave * KPW;
-  const bool full = kt0 + KPW <= KT;  // all of this wave's k-tiles inside K
   const int FB = (int)(I / 16);
   int64_t ub, ue;
   share_of((int64_t)tile_count(a) * FB, &ub, &ue);
@@ -265,7 +296,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
     };
     WSlice<2, KPW> wt[D];
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) load_unit(j, wt[j]);
+    for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
     // this lane's tile row and its token (garbage past the tile's rows: unused)
     const int32_t tok_raw = a.tile_tok[(int64_t)t * 16 + r];
     const bool valid = r < rows;
@@ -280,17 +311,26 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
       __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
       load_aslice(at, rs, valid ? (uint32_t)(tok * H * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
     }
-    for (int i0 = 0; i0 < nu; i0 += D) {
+    // one rotation of the ring: units i0 .. i0+D-1.  The first rotation is
+    // peeled so that the loop is entered with the same loads in flight as at
+    // its back edge (a shared wait would otherwise drain the whole stream).
+    auto rotation = [&](int i0) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
-        load_unit(i + D - 1, wt[(j + D - 1) % D]);
-        __builtin_amdgcn_sched_barrier(0);
+        // unit i sits in slot j; unit i + D refills it as it is consumed
+        const int fbn = fb0 + i + D;
+        const bool okn = i + D < nu;
+        const __amdgpu_buffer_rsrc_t rcn = make_rsrc(ecodes + codes_tile_offset(2 * fbn, 0, H), okn ? 2 * gbytes : 0u);
+        const __amdgpu_buffer_rsrc_t rsn =
+            make_rsrc(escales + scales_group_offset(2 * fbn, 0, H), okn ? 2 * gsbytes : 0u);
         f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        if (full)
-          compute_slice<true>(wt[j], at, kt0, KT, acc);
-        else
-          compute_slice<false>(wt[j], at, kt0, KT, acc);
+        compute_refill<FULL>(wt[j], at, kt0, KT, acc, [&](int part) {
+          if (part < 0)
+            load_wscales(wt[j], rsn, gsbytes, kt0, KT);
+          else
+            load_wcodes(wt[j], rcn, gbytes, part, kt0, KT);
+        });
         float* rb = red + (phase++ & 1) * (NW * 2 * 64 * 4);
         if (reduce_to_wave0<2>(acc, rb, NW) && i < nu) {
           const int64_t nn = (int64_t)(fb0 + i) * 16 + r;
@@ -304,14 +344,16 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
           }
         }
       }
-    }
+    };
+    rotation(0);
+    for (int i0 = D; i0 < nu; i0 += D) rotation(i0);
     sb = se;
   }
 }
 
 // down + combine: unit = (tile, 16*NG output features).  Atomic combine adds
 // weight * y into out32[token]; ORDERED writes y per sorted position to ybuf.
-template <int KPW, int NG, int D, bool A4, bool ORDERED>
+template <int KPW, int NG, int D, bool A4, bool ORDERED, bool FULL>
 __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   extern __shared__ float red[];  // [2][waves][NG][64][4]
   const int lane = lane_id();
@@ -321,7 +363,6 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   const int64_t I = a.K, H = a.N;
   const int KT = (int)(I / kTileK);
   const int kt0 = wave * KPW;
-  const bool full = kt0 + KPW <= KT;
   const int FB = (int)(H / (16 * NG));
   int64_t ub, ue;
   share_of((int64_t)tile_count(a) * FB, &ub, &ue);
@@ -351,7 +392,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
     };
     WSlice<NG, KPW> wt[D];
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) load_unit(j, wt[j]);
+    for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
     const bool valid = r < rows;
     const int64_t pr = p0 + r;
     ASlice<KPW, A4> at;
@@ -376,19 +417,25 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
         wgt[q] = a.pos_w[pp];
       }
     }
-    for (int i0 = 0; i0 < nu; i0 += D) {
+    auto rotation = [&](int i0) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
-        load_unit(i + D - 1, wt[(j + D - 1) % D]);
-        __builtin_amdgcn_sched_barrier(0);
+        const int fbn = fb0 + i + D;
+        const bool okn = i + D < nu;
+        const __amdgpu_buffer_rsrc_t rcn =
+            make_rsrc(ecodes + codes_tile_offset(fbn * NG, 0, I), okn ? NG * gbytes : 0u);
+        const __amdgpu_buffer_rsrc_t rsn =
+            make_rsrc(escales + scales_group_offset(fbn * NG, 0, I), okn ? NG * gsbytes : 0u);
         f32x4_t acc[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) acc[gi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        if (full)
-          compute_slice<true>(wt[j], at, kt0, KT, acc);
-        else
-          compute_slice<false>(wt[j], at, kt0, KT, acc);
+        compute_refill<FULL>(wt[j], at, kt0, KT, acc, [&](int part) {
+          if (part < 0)
+            load_wscales(wt[j], rsn, gsbytes, kt0, KT);
+          else
+            load_wcodes(wt[j], rcn, gbytes, part, kt0, KT);
+        });
         float* rb = red + (phase++ & 1) * (NW * NG * 64 * 4);
         if (reduce_to_wave0<NG>(acc, rb, NW) && i < nu) {
 #pragma unroll
@@ -408,18 +455,20 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
           }
         }
       }
-    }
+    };
+    rotation(0);
+    for (int i0 = D; i0 < nu; i0 += D) rotation(i0);
     sb = se;
   }
 }
 
 // ------------------------------------------------------------------ launchers
 //
-// Variants: (KPW, D) = k-tiles per wave, weight ring depth.  Default: KPW 4
-// (5 or 8 when K needs it to fit 8 waves), D 2.  MXFP4_MOE_DECODE_VARIANT
-// (tests and benchmarks only) picks another, "k<KPW>d<D>" with KPW 2 or 4
-// and D 2, 3, 4 or 6.
-// MXFP4_MOE_DECODE_WGS_PER_CU caps the resident workgroups per CU.
+// Variants: (KPW, D) = k-tiles per wave, ring slots (units ahead).  Default:
+// KPW 4 (5 or 8 when K needs it to fit 8 waves), D 1.
+// MXFP4_MOE_DECODE_VARIANT (tests and benchmarks only) picks another,
+// "k<KPW>d<D>" with KPW 2 or 4 and D 1 or 2.  MXFP4_MOE_DECODE_WGS_PER_CU
+// caps the resident workgroups per CU.
 namespace {
 struct Variant {
   int kpw, d;
@@ -427,10 +476,10 @@ struct Variant {
 
 Variant pick(int64_t K) {
   const int64_t KT = K / kTileK;
-  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 2};
+  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 1};
   if (const char* env = getenv("MXFP4_MOE_DECODE_VARIANT")) {
     int kpw = 0, d = 0;
-    if (sscanf(env, "k%dd%d", &kpw, &d) == 2 && (kpw == 2 || kpw == 4) && (d == 2 || d == 3 || d == 4 || d == 6) &&
+    if (sscanf(env, "k%dd%d", &kpw, &d) == 2 && (kpw == 2 || kpw == 4) && (d == 1 || d == 2) &&
         (KT + kpw - 1) / kpw <= 8)
       v = {kpw, d};
   }
@@ -447,7 +496,7 @@ struct GridKey {
   int grid;
 };
 std::mutex g_grid_mu;
-GridKey g_grid_cache[64];
+GridKey g_grid_cache[128];
 int g_grid_n = 0;
 
 hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
@@ -474,7 +523,7 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
   if (per_cu < 1) per_cu = 1;
   *grid = cus * per_cu;
   std::lock_guard<std::mutex> lk(g_grid_mu);
-  if (g_grid_n < 64) g_grid_cache[g_grid_n++] = GridKey{dev, fn, block, lds, *grid};
+  if (g_grid_n < 128) g_grid_cache[g_grid_n++] = GridKey{dev, fn, block, lds, *grid};
   return hipSuccess;
 }
 
@@ -489,56 +538,62 @@ hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_unit
   return hipGetLastError();
 }
 
-template <int KPW, int D>
-hipError_t gate_up_v(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
-  const int nw = (int)((a.K / kTileK + KPW - 1) / KPW);
-  const int64_t fb = a.N / 2 / 16;
+template <int KPW, int D, bool A4>
+hipError_t gate_up_v(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  const int KT = (int)(a.K / kTileK);
+  const int nw = (KT + KPW - 1) / KPW;
   if (nw > 8) return hipErrorInvalidValue;
+  const int64_t mu = max_tiles * (a.N / 2 / 16);
   const size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
-  return a4 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, true>, nw, lds, max_tiles * fb, a, s)
-            : launch_persistent(gate_up_ksplit_kernel<KPW, D, false>, nw, lds, max_tiles * fb, a, s);
+  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true>, nw, lds, mu, a, s)
+                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false>, nw, lds, mu, a, s);
+}
+
+template <int KPW, int D, bool A4, bool ORDERED>
+hipError_t down_v(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  constexpr int NG = 2;
+  const int KT = (int)(a.K / kTileK);
+  const int nw = (KT + KPW - 1) / KPW;
+  if (nw > 8) return hipErrorInvalidValue;
+  const int64_t mu = max_tiles * (a.N / 16 / NG);
+  const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
+  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, true>, nw, lds, mu, a, s)
+                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, false>, nw, lds, mu, a, s);
 }
 
 template <int KPW, int D>
-hipError_t down_v(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
-  constexpr int NG = 2;
-  const int nw = (int)((a.K / kTileK + KPW - 1) / KPW);
-  const int64_t fb = a.N / 16 / NG;
-  if (nw > 8) return hipErrorInvalidValue;
-  const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
-  const int64_t mu = max_tiles * fb;
-  if (a4) {
-    return ordered ? launch_persistent(down_ksplit_kernel<KPW, NG, D, true, true>, nw, lds, mu, a, s)
-                   : launch_persistent(down_ksplit_kernel<KPW, NG, D, true, false>, nw, lds, mu, a, s);
-  }
-  return ordered ? launch_persistent(down_ksplit_kernel<KPW, NG, D, false, true>, nw, lds, mu, a, s)
-                 : launch_persistent(down_ksplit_kernel<KPW, NG, D, false, false>, nw, lds, mu, a, s);
+hipError_t gate_up_kd(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+  return a4 ? gate_up_v<KPW, D, true>(a, max_tiles, s) : gate_up_v<KPW, D, false>(a, max_tiles, s);
+}
+template <int KPW, int D>
+hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
+  if (a4) return ordered ? down_v<KPW, D, true, true>(a, max_tiles, s) : down_v<KPW, D, true, false>(a, max_tiles, s);
+  return ordered ? down_v<KPW, D, false, true>(a, max_tiles, s) : down_v<KPW, D, false, false>(a, max_tiles, s);
 }
 }  // namespace
 
-#define MXMOE_DECODE_VARIANTS(F) \
-  F(2, 2) F(2, 3) F(2, 4) F(2, 6) F(4, 2) F(4, 3) F(4, 4) F(4, 6)
+#define MXMOE_DECODE_VARIANTS(F) F(2, 1) F(2, 2) F(4, 1) F(4, 2)
 
 hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const Variant v = pick(a.K);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return gate_up_v<KPW, D>(a, max_tiles, a4, s);
+  if (v.kpw == KPW && v.d == D) return gate_up_kd<KPW, D>(a, max_tiles, a4, s);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return gate_up_v<5, 2>(a, max_tiles, a4, s);
-  return gate_up_v<8, 2>(a, max_tiles, a4, s);
+  if (v.kpw == 5) return gate_up_kd<5, 1>(a, max_tiles, a4, s);
+  return gate_up_kd<8, 1>(a, max_tiles, a4, s);
 }
 
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const Variant v = pick(a.K);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return down_v<KPW, D>(a, max_tiles, a4, ordered, s);
+  if (v.kpw == KPW && v.d == D) return down_kd<KPW, D>(a, max_tiles, a4, ordered, s);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return down_v<5, 2>(a, max_tiles, a4, ordered, s);
-  return down_v<8, 2>(a, max_tiles, a4, ordered, s);
+  if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, a4, ordered, s);
+  return down_kd<8, 1>(a, max_tiles, a4, ordered, s);
 }
 
 }  // namespace mxmoe
