@@ -5,6 +5,7 @@
 // Refusing an empty or overflowing shape by name before any size is used
 // follows the loader rule of TensorFold PR #1050 (review and commit notes:
 // EmptyShape / ShapeOverflow via checked arithmetic).
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -90,8 +91,12 @@ GemmPlan choose_plan(const Shape& s) {
                          s.H <= 8192 && s.I <= 8192 && (s.I / 16) % 4 == 0 && (s.H / 32) % 4 == 0;
   if (s.S <= 16 * s.Eg && ksplit_ok) {
     p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
-  } else {
+  } else if (const char* env = getenv("MXFP4_MOE_PREFILL_KERNEL"); env && !strcmp(env, "lds")) {
+    // 64-token tiles with register-fed weights (kept for comparison)
     p.ms = 4; p.fg = 2; p.nw = 4; p.direct_a = 0;
+  } else {
+    // 128-token x 256-weight-row tiles staged through LDS
+    p.ms = 8; p.fg = 0; p.nw = 4; p.direct_a = 0;
   }
   return p;
 }
@@ -288,8 +293,9 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.act = at<uint16_t>(ws, L.act);
   g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.zero_n = s.ordered ? 0 : s.T * s.H;
-  e = plan.ms == 1 ? launch_gate_up_ksplit(g, max_tiles(s, mt), s.a4, stream)
-                   : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
+  e = plan.ms == 1   ? launch_gate_up_ksplit(g, max_tiles(s, mt), s.a4, stream)
+      : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.a4, stream)
+                     : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
 
   if (s.a4) {
@@ -321,8 +327,9 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.zero_n = 0;
   g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
-  e = plan.ms == 1 ? launch_down_ksplit(g, max_tiles(s, mt), s.a4, s.ordered, stream)
-                   : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
+  e = plan.ms == 1   ? launch_down_ksplit(g, max_tiles(s, mt), s.a4, s.ordered, stream)
+      : plan.ms == 8 ? launch_down_tile(g, max_tiles(s, mt), s.a4, s.ordered, stream)
+                     : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(e);
 

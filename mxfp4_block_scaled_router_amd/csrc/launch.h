@@ -108,6 +108,9 @@ hipError_t launch_gate_up(const GemmArgs& a, const GemmPlan& p, int64_t max_tile
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
                        bool ordered, hipStream_t stream);
 hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
+// 128-token x 256-weight-row tiles, LDS ring fed by global->LDS copies (tile.hip)
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t stream);
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
