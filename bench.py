@@ -170,6 +170,7 @@ def main():
         dims.flags |= mx.MXFP4_MOE_DETERMINISTIC
     k = wl.top_k
     ws = torch.empty(mx.mxfp4_moe_workspace_bytes(dims, k), dtype=torch.uint8, device="cuda")
+    plan = mx.mxfp4_moe_plan(dims, k)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
 
     # routing statistics (same logits every step)
@@ -216,7 +217,8 @@ def main():
         "route": T * wl.E_global * 4 + T * k * 8,
         "gate_up": touched * w13_b + T * H * 2 + n_assign * I * 2,
         "down": touched * w2_b + n_assign * I * 2 + T * H * 2,
-        "combine": T * H * 4 + T * H * 2,
+        # ordered gather reads every local slot's y row; atomic path casts out32
+        "combine": (n_assign * H * 4 if plan["ordered_combine"] else T * H * 4) + T * H * 2,
     }
     flops = {"route": 0, "gate_up": 2 * n_assign * 2 * I * H, "down": 2 * n_assign * H * I,
              "combine": 0}
@@ -262,7 +264,8 @@ def main():
             " A4" if wl.a4 else ""), "T": T, "H": H, "I": I, "E_local": wl.E_local,
             "E_global": wl.E_global, "top_k": k, "touched_experts": touched,
             "local_assignments": n_assign, "weight_copies_rotated": len(banks),
-            "bank_bytes": bank_bytes, "combine": "ordered" if args.deterministic else "atomic",
+            "bank_bytes": bank_bytes, "combine": "ordered" if plan["ordered_combine"] else "atomic",
+            "tile_rows": plan["tile_rows"],
             "parallelism": "single GPU"},
         "roofline": roof,
         "step": {"hbm_bytes": step_bytes, "hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -129,6 +129,16 @@ int mxfp4_moe_preshuffle(const mxfp4_moe_dims* d, const uint8_t* canon_w13,
 int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* bytes);
 
 /*
+ * How mxfp4_moe_forward will run these dims and top_k (a pure host query):
+ * *tile_rows = token rows per GEMM tile (16: K split across waves, for
+ * decode-sized calls; 128: LDS-staged large tiles); *ordered_combine = 1 when
+ * the combine gathers slot-ordered y rows (deterministic), 0 when it adds
+ * into an fp32 buffer with atomics.  The large-tile plan always gathers.
+ * Errors as mxfp4_moe_workspace_bytes; NULL outputs -> NULL_POINTER.
+ */
+int mxfp4_moe_plan(const mxfp4_moe_dims* d, int32_t top_k, int32_t* tile_rows, int32_t* ordered_combine);
+
+/*
  * The layer.  x: bf16 [T][H]; router_logits: float [T][E_global]; weights from
  * mxfp4_moe_preshuffle; out: bf16 [T][H] (tokens with no local assignment get
  * +0).  clamp_limit: L > 0 or +inf.  When T == 0, x, router_logits and out may

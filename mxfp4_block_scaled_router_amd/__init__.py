@@ -54,7 +54,7 @@ class Dims(ctypes.Structure):
 EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
             "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
-            "mxfp4_moe_route", "mxfp4_moe_quantize")
+            "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_plan")
 
 
 def load_library(path: str = LIB_PATH):
@@ -80,6 +80,9 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_preshuffle.argtypes = [D, P, P, P, P, P, P, P, P, P]
     lib.mxfp4_moe_workspace_bytes.restype = ctypes.c_int
     lib.mxfp4_moe_workspace_bytes.argtypes = [D, I32, PSZ]
+    PI32 = ctypes.POINTER(ctypes.c_int32)
+    lib.mxfp4_moe_plan.restype = ctypes.c_int
+    lib.mxfp4_moe_plan.argtypes = [D, I32, PI32, PI32]
     lib.mxfp4_moe_forward.restype = ctypes.c_int
     lib.mxfp4_moe_forward.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]
     lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
@@ -138,6 +141,15 @@ def mxfp4_moe_workspace_bytes(dims: Dims, top_k: int) -> int:
     _check("mxfp4_moe_workspace_bytes",
            _L().mxfp4_moe_workspace_bytes(ctypes.byref(dims), int(top_k), ctypes.byref(out)))
     return out.value
+
+
+def mxfp4_moe_plan(dims: Dims, top_k: int) -> dict:
+    """How forward runs these dims: token rows per GEMM tile and whether the
+    combine is the slot-ordered gather."""
+    rows, ordered = ctypes.c_int32(), ctypes.c_int32()
+    _check("mxfp4_moe_plan", _L().mxfp4_moe_plan(ctypes.byref(dims), int(top_k), ctypes.byref(rows),
+                                                  ctypes.byref(ordered)))
+    return {"tile_rows": rows.value, "ordered_combine": bool(ordered.value)}
 
 
 def mxfp4_moe_preshuffled_bytes(dims: Dims):

@@ -37,6 +37,8 @@ struct Shape {
   bool a4, ordered;
 };
 
+GemmPlan choose_plan(const Shape& s);
+
 int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!d) return MXFP4_MOE_ERR_NULL_POINTER;
   if (d->reserved != 0) return MXFP4_MOE_ERR_BAD_ARGUMENT;
@@ -73,6 +75,9 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!mul_ok(s->S, s->H, &tmp) || !mul_ok(tmp, 4, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
   int64_t per;
   if (!mul_ok(2 * s->I, s->H, &per) || !mul_ok(per, s->El, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  // the large-tile GEMMs always use the slot-ordered combine: with many rows
+  // per call, writing y and gathering it beats fp32 atomics into out32
+  if (choose_plan(*s).ms == 8) s->ordered = true;
   return MXFP4_MOE_OK;
 }
 
@@ -436,6 +441,16 @@ int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* by
   if (st) return st;
   if (!bytes) return MXFP4_MOE_ERR_NULL_POINTER;
   *bytes = layout_of(s).total;
+  return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_plan(const mxfp4_moe_dims* d, int32_t top_k, int32_t* tile_rows, int32_t* ordered_combine) {
+  Shape s;
+  int st = check_dims(d, top_k, true, &s);
+  if (st) return st;
+  if (!tile_rows || !ordered_combine) return MXFP4_MOE_ERR_NULL_POINTER;
+  *tile_rows = 16 * choose_plan(s).ms;
+  *ordered_combine = s.ordered ? 1 : 0;
   return MXFP4_MOE_OK;
 }
 

@@ -465,6 +465,48 @@ __global__ __launch_bounds__(256) void combine_ordered_kernel(CombineArgs a) {
   if (a.out32_copy) *reinterpret_cast<f32x4_t*>(a.out32_copy + i) = acc;
 }
 
+// Same sum, one workgroup per token: the token's slot positions and weights
+// are scalar loads, and every thread issues the loads of all KMAX slot rows of
+// its columns before adding them in increasing j (a slot past k or without a
+// local expert loads row 0 and is skipped).
+typedef const __attribute__((address_space(4))) int32_t c_i32;
+typedef const __attribute__((address_space(4))) float c_f32;
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_gather_kernel(CombineArgs a) {
+  const int64_t t = blockIdx.x;
+  const int k = a.top_k;
+  int32_t pos[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int64_t s = t * k + (j < k ? j : 0);
+    pos[j] = j < k ? ((c_i32*)a.inv)[s] : -1;
+    w[j] = ((c_f32*)a.route_w)[s];
+  }
+  const int64_t H = a.H;
+  for (int64_t c = threadIdx.x * 4; c < H; c += 4 * blockDim.x) {
+    f32x4_t y[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      y[j] = *reinterpret_cast<const f32x4_t*>(a.ybuf + (int64_t)(pos[j] >= 0 ? pos[j] : 0) * H + c);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (pos[j] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float prod = w[j] * y[j][q];
+        acc[q] = acc[q] + prod;
+      }
+    }
+    const int64_t i = t * H + c;
+    uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+    uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(a.out + i) = make_uint2(lo, hi);
+    if (a.out32_copy) *reinterpret_cast<f32x4_t*>(a.out32_copy + i) = acc;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -539,7 +581,10 @@ hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t s) {
   const int64_t n4 = a.T * a.H / 4;
   if (n4 == 0) return hipSuccess;
   dim3 grid((unsigned)((n4 + 255) / 256));
-  if (ordered) hipLaunchKernelGGL(combine_ordered_kernel, grid, dim3(256), 0, s, a);
+  if (ordered && a.top_k <= 8 && a.T <= INT32_MAX)
+    hipLaunchKernelGGL(combine_gather_kernel<8>, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  else if (ordered)
+    hipLaunchKernelGGL(combine_ordered_kernel, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(cast_out_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -101,6 +101,19 @@ def test_null_dims(lib):
     assert lib.mxfp4_moe_workspace_bytes(ctypes.byref(dims()), 2, None) == NULL_POINTER
 
 
+def test_plan_query(lib):
+    # decode-sized call: 16-row K-split tiles, atomic combine unless deterministic
+    assert mx.mxfp4_moe_plan(dims(), 2) == {"tile_rows": 16, "ordered_combine": False}
+    det = mx.mxfp4_moe_plan(dims(flags=mx.MXFP4_MOE_DETERMINISTIC), 2)
+    assert det == {"tile_rows": 16, "ordered_combine": True}
+    # many rows per expert: large tiles, always the slot-ordered gather
+    big = mx.mxfp4_moe_plan(dims(T=4096, E_global=8, E_local=8), 2)
+    assert big == {"tile_rows": 128, "ordered_combine": True}
+    out = ctypes.c_int32()
+    assert lib.mxfp4_moe_plan(ctypes.byref(dims()), 2, None, ctypes.byref(out)) == NULL_POINTER
+    assert lib.mxfp4_moe_plan(ctypes.byref(dims(H=0)), 2, ctypes.byref(out), ctypes.byref(out)) == EMPTY_SHAPE
+
+
 def test_preshuffled_bytes(lib):
     d = dims(H=512, I=256, E_local=8)
     w13, w13s, w2, w2s = mx.mxfp4_moe_preshuffled_bytes(d)
