@@ -1,36 +1,45 @@
 // Grouped GEMMs for token tiles of up to 128 rows (prefill and the A4 path):
-// the MFMA work is the cost, so a workgroup owns a 128-token x 256-weight-row
-// output tile of one expert and streams K through LDS.
+// the MFMA work is the cost, so a workgroup owns a 128-token x NT-weight-row
+// output tile of one expert (NT = 16 NRG, NRG = 32 by default) and streams K
+// through LDS.
 //
 //   gate_up:  h = W13_e x_t, fused with the clamped SwiGLU -> act (bf16)
 //   down:     y = W2_e a, fused with the weighted combine (fp32 atomics into
 //             out32, or y rows for the ordered gather)
 //
-// Staging.  Each k-tile (128 of K) of the activation rows and of the 16
-// preshuffled weight row groups (codes and the scale dwords that cover it)
-// is copied straight from global memory into an LDS ring of STAGES slots by
-// the gfx950 global->LDS load (a wave's instruction writes 64 x 16 bytes, lane
-// i at slot + 16 i, from any per-lane address), so staging costs no registers.
-// Every wave issues the same number of copies per k-tile; before using slot
-// kt a wave waits until only the later stages' copies are outstanding, and one
-// barrier per k-tile then publishes the slot to the whole workgroup and frees
-// the slot the next copy writes (it was read in the previous iteration).
+// Staging.  Each k-tile (128 of K) of the activation rows and of the NRG
+// preshuffled weight row groups is copied straight from global memory into
+// an LDS ring of STAGES slots by the gfx950 global->LDS load (a wave's
+// instruction writes 64 x 16 bytes, lane i at slot + 16 i, from any per-lane
+// address), so staging costs no registers.  The weight scale dwords (one per
+// lane and row group covers 4 k-tiles) are not staged: each wave loads its
+// own into registers, a quarter of the next 4-k-tile group per k-tile.  Every
+// wave issues the same loads in the same order per k-tile (scale loads, then
+// copies); before using slot kt a wave waits until only the later stages'
+// loads are outstanding, and one barrier per k-tile then publishes the slot
+// to the whole workgroup and frees the slot the next copy writes (it was
+// read in the previous iteration).
 //
 // Bank conflicts.  The activation rows are stored with their 16-byte chunks
 // XOR-swizzled by the row (bf16: chunk c of row r at c ^ (r & 15); MXFP4:
 // block c at c ^ ((r >> 2) & 3)), chosen through the per-lane source address
 // of the copy, so the 16 lanes that read one MFMA operand hit 16 distinct
-// 16-byte bank groups.  Weight codes and scales are read lane-contiguously.
+// 16-byte bank groups.  Weight codes are read lane-contiguously.
 //
 // MFMA layout: as in the other GEMMs (lane l: row l%16, MX block l/16 of the
 // k-tile; K element 8m+e of the block feeds bf16 MFMA m).  Eight waves form a
 // 2 x 4 grid (two per SIMD, so one wave's unpacking overlaps the other's
-// MFMAs); wave (wm, wn) owns rows 64 wm.. and weight row groups 4 wn..4 wn+3.
+// MFMAs); wave (wm, wn) owns rows 64 wm.. and weight row groups WN wn..
+// (WN = NRG/4).  A wider tile moves fewer activation bytes and takes fewer
+// barriers per MFMA.
 //
-// Schedule.  Work items (row tile, 256-row weight block) are numbered
+// Schedule.  Work items (row tile, NT-row weight block) are numbered
 // tile-major; workgroup b runs on XCD b % 8 (round-robin dispatch), and each
 // XCD takes a contiguous eighth of the items, so the workgroups resident on one
 // XCD share activation tiles and weight blocks in that XCD's L2.
+#include <stdlib.h>
+#include <string.h>
+
 #include <mutex>
 
 #include "common.h"
@@ -43,29 +52,33 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
-constexpr int kMT = 128;        // token rows per tile
-constexpr int kNT = 256;        // weight rows per tile
-constexpr int kNRG = kNT / 16;  // weight row groups per tile
-constexpr int kWaves = 8;       // 2 (rows) x 4 (weight row groups)
+constexpr int kMT = 128;  // token rows per tile
+constexpr int kWaves = 8;  // 2 (rows) x 4 (weight row groups)
 constexpr int kThreads = 64 * kWaves;
 
-template <bool AFP4>
+template <bool AFP4, int NRG_>
 struct Cfg {
+  static constexpr int NRG = NRG_;                              // weight row groups per tile
+  static constexpr int NT = 16 * NRG;
+  static constexpr int WN = NRG / 4;                            // row groups per wave
   static constexpr int A_BYTES = AFP4 ? kMT * 64 : kMT * 256;  // activation k-tile
   static constexpr int AS_BYTES = AFP4 ? kMT * 4 : 0;           // activation scale bytes
-  static constexpr int B_BYTES = kNRG * 1024;                   // weight codes
-  static constexpr int BS_BYTES = kNRG * 256;                   // weight scale dwords
-  static constexpr int A_OFF = 0, AS_OFF = A_BYTES, B_OFF = A_BYTES + AS_BYTES, BS_OFF = B_OFF + B_BYTES;
-  static constexpr int STAGE = BS_OFF + BS_BYTES;
-  static constexpr int STAGES = AFP4 ? 4 : 3;
+  static constexpr int B_BYTES = NRG * 1024;                    // weight codes
+  static constexpr int A_OFF = 0, AS_OFF = A_BYTES, B_OFF = A_BYTES + AS_BYTES;
+  static constexpr int STAGE = B_OFF + B_BYTES;
+  static constexpr int ROWS_BYTES = kMT * 4;  // int32 [kMT]: A row index of each tile row
+  static constexpr int STAGES_FIT = (160 * 1024 - ROWS_BYTES) / STAGE;
+  static constexpr int STAGES = STAGES_FIT > 4 ? 4 : STAGES_FIT;
   static constexpr int A_CP = A_BYTES / 1024 / kWaves;  // copies per wave per k-tile
-  static constexpr int AS_CP = AFP4 ? 1 : 0;  // 2 copies, made by the even and the odd waves alike
-  static constexpr int B_CP = kNRG / kWaves;
-  static constexpr int CP = A_CP + AS_CP + 2 * B_CP;
-  static constexpr int ROWS_OFF = STAGES * STAGE;  // int32 [kMT]: A row index of each tile row
-  static constexpr int LDS = ROWS_OFF + kMT * 4;
-  static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert((STAGES - 2) * CP < 64, "vmcnt range");
+  static constexpr int AS_CP = AFP4 ? 1 : 0;            // 2 copies, made by even and odd waves alike
+  static constexpr int B_CP = NRG / kWaves;
+  static constexpr int CP = A_CP + AS_CP + B_CP;
+  static constexpr int SCP = WN / 4;                    // scale dword loads per wave per k-tile
+  static constexpr int ROWS_OFF = STAGES * STAGE;
+  static constexpr int LDS = ROWS_OFF + ROWS_BYTES;
+  static_assert(STAGES >= 2 && LDS <= 160 * 1024, "LDS budget");
+  static_assert(WN % 4 == 0 && NRG % kWaves == 0, "tile shape");
+  static_assert((STAGES - 2) * (CP + SCP) + SCP < 64, "vmcnt range");
 };
 
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding:
@@ -74,6 +87,22 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// wait_vm<later * CP + since * SCP>() for later, since in [0, S-2] (S <= 4)
+template <int CP, int SCP, int S>
+__device__ __forceinline__ void wait_slot(int later, int since) {
+  static_assert(S >= 2 && S <= 4, "stages");
+  if constexpr (S == 2) {
+    wait_vm<0>();
+  } else {
+#define MXMOE_W(L, T) \
+  if (later == L && since == T) { wait_vm<L * CP + T * SCP>(); return; }
+    MXMOE_W(0, 0) MXMOE_W(0, 1) MXMOE_W(1, 0) MXMOE_W(1, 1)
+    if constexpr (S == 4) { MXMOE_W(0, 2) MXMOE_W(1, 2) MXMOE_W(2, 0) MXMOE_W(2, 1) MXMOE_W(2, 2) }
+#undef MXMOE_W
+    wait_vm<0>();  // not reached
+  }
 }
 
 __device__ __forceinline__ void copy16(const void* src, uint8_t* lds_dst) {
@@ -91,7 +120,7 @@ struct TileItem {
 
 // Item of this workgroup, or false.  XCD x = blockIdx % 8 takes items
 // [x * per, x * per + per).
-__device__ __forceinline__ bool tile_item(const GemmArgs& a, int ntl, TileItem* it) {
+__device__ __forceinline__ bool tile_item(const GemmArgs& a, int ntl, int nt, TileItem* it) {
   const int n = ((const_i32*)a.tile_off)[a.E_local];
   const int items = n * ntl;
   const int per = (items + 7) / 8;
@@ -104,7 +133,7 @@ __device__ __forceinline__ bool tile_item(const GemmArgs& a, int ntl, TileItem* 
   it->e = ti[0];
   it->rows = ti[1];
   it->p0 = ti[2];
-  it->n0 = (item - t * ntl) * kNT;
+  it->n0 = (item - t * ntl) * nt;
   return true;
 }
 
@@ -116,12 +145,13 @@ __device__ __forceinline__ void zero_duty(const GemmArgs& a) {
   for (int64_t i = tid; i < a.zero_n / 4; i += nthreads) reinterpret_cast<f32x4_t*>(a.zero_buf)[i] = z;
 }
 
-// The k-loop: acc[rb][cb] += A(rows 64 wm + 16 rb ..) * W(row group 8 wn + cb)^T
-// over all of K.  rowidx: LDS table of the A-matrix row of each tile row.
-template <bool AFP4>
+// The k-loop: acc[rb][cb] += A(rows 64 wm + 16 rb ..) * W(row group WN wn + cb)^T
+// over all of K.  rowidx (LDS): the A-matrix row of each tile row.
+template <bool AFP4, int NRG>
 __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
-                                              uint8_t* lds, f32x4_t (&acc)[4][4]) {
-  using C = Cfg<AFP4>;
+                                              uint8_t* lds, f32x4_t (&acc)[4][NRG / 4]) {
+  using C = Cfg<AFP4, NRG>;
+  constexpr int WN = C::WN;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -150,21 +180,26 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
       a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
     }
     const int row = 64 * (wave & 1) + lane;
-    as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);  // waves 2.. repeat waves 0/1 (same bytes)
+    as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);
   }
   const int64_t cpe = codes_per_expert(N, K), spe = scales_per_expert(N, K);
   const uint8_t* ecodes = a.w_codes + (int64_t)it.e * cpe;
   const uint8_t* escales = a.w_scales + (int64_t)it.e * spe;
   const int nrg = (int)(N / 16);
-  const uint8_t* b_src[C::B_CP];
-  const uint8_t* bs_src[C::B_CP];
-#pragma unroll
-  for (int jj = 0; jj < C::B_CP; ++jj) {
-    int rg = it.n0 / 16 + wave * C::B_CP + jj;
-    rg = rg < nrg ? rg : nrg - 1;  // partial weight block: repeat the last group (not stored)
-    b_src[jj] = ecodes + codes_tile_offset(rg, 0, K) + lane * 16;
-    bs_src[jj] = escales + scales_group_offset(rg, 0, K) + lane * 4;
-  }
+  auto clamp_rg = [&](int rg) { return rg < nrg ? rg : nrg - 1; };  // partial block: repeat (not stored)
+  // weight copies and scale loads: one per-lane pointer each plus wave-uniform
+  // row-group offsets
+  const uint8_t* b_lane = ecodes + lane * 16;
+  const uint8_t* s_lane = escales + lane * 4;
+  auto b_off = [&](int jj) -> int64_t {
+    return codes_tile_offset(clamp_rg(it.n0 / 16 + wave * C::B_CP + jj), 0, K);
+  };
+  // this wave's scale dwords: row group WN wn + cb, 4-k-tile group q
+  const int NQ = (KT + 3) / 4;
+  auto sload = [&](int cb, int q) -> uint32_t {
+    const int64_t off = scales_group_offset(clamp_rg(it.n0 / 16 + wn * WN + cb), q < NQ ? q : NQ - 1, K);
+    return *reinterpret_cast<const uint32_t*>(s_lane + off);
+  };
 
   auto issue = [&](int kt, uint8_t* slot) {
 #pragma unroll
@@ -176,26 +211,29 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
 #pragma unroll
     for (int jj = 0; jj < C::B_CP; ++jj) {
       const int q = wave * C::B_CP + jj;
-      copy16(b_src[jj] + (int64_t)kt * 1024, slot + C::B_OFF + q * 1024);
-      copy4(bs_src[jj] + (int64_t)(kt >> 2) * 256, slot + C::BS_OFF + q * 256);
+      copy16(b_lane + b_off(jj) + (int64_t)kt * 1024, slot + C::B_OFF + q * 1024);
     }
   };
 
+  // scale dwords of the current 4-k-tile group and of the next one; k-tile
+  // kt loads quarter kt % 4 of group kt/4 + 1
+  uint32_t scur[WN], snxt[WN];
+#pragma unroll
+  for (int cb = 0; cb < WN; ++cb) scur[cb] = sload(cb, 0);
+
   auto compute = [&](int kt, const uint8_t* slot) {
     const int g = lane >> 4;
-    u32x4_t bw[4];
-    uint32_t sbyte[4];
+    u32x4_t bw[WN];
+    uint32_t sbyte[WN];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int q = wn * 4 + cb;
-      bw[cb] = *reinterpret_cast<const u32x4_t*>(slot + C::B_OFF + q * 1024 + lane * 16);
-      const uint32_t sd = *reinterpret_cast<const uint32_t*>(slot + C::BS_OFF + q * 256 + lane * 4);
-      sbyte[cb] = (sd >> (8 * (kt & 3))) & 0xFFu;
+    for (int cb = 0; cb < WN; ++cb) {
+      bw[cb] = *reinterpret_cast<const u32x4_t*>(slot + C::B_OFF + (wn * WN + cb) * 1024 + lane * 16);
+      sbyte[cb] = (scur[cb] >> (8 * (kt & 3))) & 0xFFu;
     }
     if constexpr (!AFP4) {
-      float sc[4];
+      float sc[WN];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) sc[cb] = e8m0_scale_operand(sbyte[cb]);
+      for (int cb = 0; cb < WN; ++cb) sc[cb] = e8m0_scale_operand(sbyte[cb]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         bf16x8_t av[4];
@@ -207,7 +245,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
               bf16x8_t, *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 256 + phys * 16));
         }
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < WN; ++cb) {
           const bf16x8_t bv = unpack8_e2m1(bw[cb][m], sc[cb]);
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
@@ -215,7 +253,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
         }
       }
     } else {
-      i32x8_t A[4], B[4];
+      i32x8_t A[4];
       uint32_t as[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -226,14 +264,13 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
         as[rb] = slot[C::AS_OFF + row * 4 + g];
       }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        B[cb] = (i32x8_t){(int)bw[cb][0], (int)bw[cb][1], (int)bw[cb][2], (int)bw[cb][3], 0, 0, 0, 0};
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < WN; ++cb) {
+        const i32x8_t B = {(int)bw[cb][0], (int)bw[cb][1], (int)bw[cb][2], (int)bw[cb][3], 0, 0, 0, 0};
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rb], B[cb], acc[rb][cb], 4, 4, 0,
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rb], B, acc[rb][cb], 4, 4, 0,
                                                                          (int)as[rb], 0, (int)sbyte[cb]);
+      }
     }
   };
 
@@ -247,52 +284,76 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     for (int j = 0; j < S; ++j) {
       const int kt = kt0 + j;
       if (kt >= KT) break;
-      // this wave's copies of k-tile kt are done once only the later stages'
-      // copies (at most S-2 of them) are outstanding
+      // loads issued after slot kt's copies: the copies of the later stages
+      // already issued (at most S-2) and the scale loads of the steps since
+      // (at most S-2 steps; fewer in the first ones)
       const int later = KT - 1 - kt < S - 2 ? KT - 1 - kt : S - 2;
-      if (later >= S - 2) wait_vm<(S - 2) * C::CP>();
-      else if (later == 2) wait_vm<2 * C::CP>();
-      else if (later == 1) wait_vm<C::CP>();
-      else wait_vm<0>();
+      const int since = kt < S - 2 ? kt : S - 2;
+      wait_slot<C::CP, C::SCP, S>(later, since);
       __builtin_amdgcn_s_barrier();
+      // a new 4-k-tile group starts: its scale dwords came in over the
+      // previous group's k-tiles
+      if ((kt & 3) == 0 && kt > 0) {
+#pragma unroll
+        for (int cb = 0; cb < WN; ++cb) scur[cb] = snxt[cb];
+      }
+      // quarter kt % 4 of the next group's scale dwords (before the copies,
+      // so waiting for a slot never waits for a newer scale load)
+#pragma unroll
+      for (int i = 0; i < C::SCP; ++i) {
+        const int cb = (kt & 3) * C::SCP + i;
+        snxt[cb] = sload(cb, (kt >> 2) + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       if (kt + S - 1 < KT) issue(kt + S - 1, lds + ((j + S - 1) % S) * C::STAGE);
       compute(kt, lds + j * C::STAGE);
     }
   }
 }
 
+// Tile width: NRG weight row groups (MXFP4_MOE_TILE_NRG, tests and benchmarks
+// only, selects 16; default 32).
+int tile_nrg() {
+  static const int v = [] {
+    const char* e = getenv("MXFP4_MOE_TILE_NRG");
+    return e && !strcmp(e, "16") ? 16 : 32;
+  }();
+  return v;
+}
+
 }  // namespace
 
-// gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 256.
-template <bool AFP4>
+// gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
+template <bool AFP4, int NRG>
 __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AFP4>;
+  using C = Cfg<AFP4, NRG>;
+  constexpr int WN = C::WN;
   zero_duty(a);
   const int64_t H = a.K, I = a.N / 2;
-  const int ntl = (int)((a.N + kNT - 1) / kNT);
+  const int ntl = (int)((a.N + C::NT - 1) / C::NT);
   TileItem it;
-  if (!tile_item(a, ntl, &it)) return;
+  if (!tile_item(a, ntl, C::NT, &it)) return;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
   for (int r = threadIdx.x; r < kMT; r += blockDim.x)
     rowidx[r] = a.sorted[it.p0 + (r < it.rows ? r : 0)] / a.top_k;  // token of the tile row
   __syncthreads();
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][WN];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AFP4>(a, it, H, a.N, lds, acc);
+    for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  tile_mainloop<AFP4, NRG>(a, it, H, a.N, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int nrg = (int)(a.N / 16);
   // row groups (2f, 2f+1) of the wave hold gate and up of feature group
-  // (n0/16 + 4 wn + 2f) / 2
+  // (n0/16 + WN wn + 2f) / 2
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int rg = it.n0 / 16 + wn * 4 + 2 * f;
+  for (int f = 0; f < WN / 2; ++f) {
+    const int rg = it.n0 / 16 + wn * WN + 2 * f;
     if (rg >= nrg) break;
     const int64_t n = (int64_t)(rg / 2) * 16 + (lane & 15);
 #pragma unroll
@@ -309,24 +370,25 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
 }
 
 // down + combine.
-template <bool AFP4, bool ORDERED>
+template <bool AFP4, bool ORDERED, int NRG>
 __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AFP4>;
+  using C = Cfg<AFP4, NRG>;
+  constexpr int WN = C::WN;
   const int64_t I = a.K, H = a.N;
-  const int ntl = (int)((a.N + kNT - 1) / kNT);
+  const int ntl = (int)((a.N + C::NT - 1) / C::NT);
   TileItem it;
-  if (!tile_item(a, ntl, &it)) return;
+  if (!tile_item(a, ntl, C::NT, &it)) return;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
   for (int r = threadIdx.x; r < kMT; r += blockDim.x)
     rowidx[r] = (int32_t)(it.p0 + (r < it.rows ? r : 0));  // sorted position of the tile row
   __syncthreads();
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][WN];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AFP4>(a, it, I, H, lds, acc);
+    for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  tile_mainloop<AFP4, NRG>(a, it, I, H, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -345,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
         wgt = a.pos_w[p];
       }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int64_t n = (int64_t)(it.n0 / 16 + wn * 4 + cb) * 16 + (lane & 15);
+      for (int cb = 0; cb < WN; ++cb) {
+        const int64_t n = (int64_t)(it.n0 / 16 + wn * WN + cb) * 16 + (lane & 15);
         if (n >= H) break;
         if constexpr (ORDERED) {
           a.ybuf[p * H + n] = acc[rb][cb][r];
@@ -359,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------ launchers
 namespace {
-int64_t tile_grid(int64_t max_tiles, int64_t N) {
-  const int64_t items = max_tiles * ((N + kNT - 1) / kNT);
+int64_t tile_grid(int64_t max_tiles, int64_t N, int nt) {
+  const int64_t items = max_tiles * ((N + nt - 1) / nt);
   return 8 * ((items + 7) / 8);
 }
 
@@ -375,28 +437,38 @@ hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a
                                (int)lds);
   });
   if (attr != hipSuccess) return attr;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+template <int NRG>
+hipError_t gate_up_nrg(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
+  return a4 ? launch_lds(tile_gate_up_kernel<true, NRG>, grid, Cfg<true, NRG>::LDS, a, s)
+            : launch_lds(tile_gate_up_kernel<false, NRG>, grid, Cfg<false, NRG>::LDS, a, s);
+}
+
+template <int NRG>
+hipError_t down_nrg(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
+  if (a4)
+    return ordered ? launch_lds(tile_down_kernel<true, true, NRG>, grid, Cfg<true, NRG>::LDS, a, s)
+                   : launch_lds(tile_down_kernel<true, false, NRG>, grid, Cfg<true, NRG>::LDS, a, s);
+  return ordered ? launch_lds(tile_down_kernel<false, true, NRG>, grid, Cfg<false, NRG>::LDS, a, s)
+                 : launch_lds(tile_down_kernel<false, false, NRG>, grid, Cfg<false, NRG>::LDS, a, s);
 }
 }  // namespace
 
 hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const int64_t grid = tile_grid(max_tiles, a.N);
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  return a4 ? launch_lds(tile_gate_up_kernel<true>, grid, Cfg<true>::LDS, a, s)
-            : launch_lds(tile_gate_up_kernel<false>, grid, Cfg<false>::LDS, a, s);
+  return tile_nrg() == 16 ? gate_up_nrg<16>(a, max_tiles, a4, s) : gate_up_nrg<32>(a, max_tiles, a4, s);
 }
 
 hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const int64_t grid = tile_grid(max_tiles, a.N);
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  if (a4)
-    return ordered ? launch_lds(tile_down_kernel<true, true>, grid, Cfg<true>::LDS, a, s)
-                   : launch_lds(tile_down_kernel<true, false>, grid, Cfg<true>::LDS, a, s);
-  return ordered ? launch_lds(tile_down_kernel<false, true>, grid, Cfg<false>::LDS, a, s)
-                 : launch_lds(tile_down_kernel<false, false>, grid, Cfg<false>::LDS, a, s);
+  return tile_nrg() == 16 ? down_nrg<16>(a, max_tiles, a4, ordered, s)
+                          : down_nrg<32>(a, max_tiles, a4, ordered, s);
 }
 
 }  // namespace mxmoe
