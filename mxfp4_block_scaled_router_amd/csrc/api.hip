@@ -87,6 +87,13 @@ int check_clamp(float L) {
 }
 
 // ---------------------------------------------------------------- plans
+// MXFP4_MOE_ROUTE_KERNEL=1 (benchmarks only) keeps the separate routing kernel
+// where the decode gate_up kernel would route the tokens itself
+bool separate_route_kernel() {
+  const char* env = getenv("MXFP4_MOE_ROUTE_KERNEL");
+  return env && !strcmp(env, "1");
+}
+
 GemmPlan choose_plan(const Shape& s) {
   // expected rows per local expert ~ T*k / E_global
   GemmPlan p;
@@ -255,7 +262,9 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   const GemmPlan plan = choose_plan(s);
   const int mt = 16 * plan.ms;
   RouteArgs r = route_args(s, logits, ws, L, mt, mt);
-  hipError_t e = launch_route(r, stream);
+  // few tokens on the 16-row plan: the gate_up kernel routes them itself
+  const bool fused_route = plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) && !separate_route_kernel();
+  hipError_t e = fused_route ? hipSuccess : launch_route(r, stream);
   if (e != hipSuccess) return hip_fail(e);
 
   if (s.a4) {
@@ -298,7 +307,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.act = at<uint16_t>(ws, L.act);
   g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.zero_n = s.ordered ? 0 : s.T * s.H;
-  e = plan.ms == 1   ? launch_gate_up_ksplit(g, max_tiles(s, mt), s.a4, stream)
+  e = plan.ms == 1   ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.a4, stream)
       : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.a4, stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);

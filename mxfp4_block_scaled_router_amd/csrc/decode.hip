@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace mxmoe {
 
@@ -251,9 +252,12 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue) {
 
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
 // up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
-template <int KPW, int D, bool A4, bool FULL>
-__global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
-  extern __shared__ float red[];  // [2][waves][2][64][4]
+// ROUTE: every workgroup first routes the tokens itself (route_block, tables in
+// LDS after the partial buffers; workgroup 0 also writes the global tables that
+// the down and combine kernels read), so no routing kernel runs before this one.
+template <int KPW, int D, bool A4, bool FULL, bool ROUTE>
+__global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteArgs ra) {
+  extern __shared__ float red[];  // [2][waves][2][64][4], then (ROUTE) the routing tables
   if (a.zero_buf) {
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -268,8 +272,19 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
   const int KT = (int)(H / kTileK);
   const int kt0 = wave * KPW;
   const int FB = (int)(I / 16);
+  RouteLds rl;
+  int ntiles;
+  if constexpr (ROUTE) {
+    const int64_t S = ra.T * (int64_t)ra.top_k;
+    const int64_t bound = (ra.E_local < S ? ra.E_local : S) + S / 16;
+    rl = route_lds(reinterpret_cast<int32_t*>(red + 2 * NW * 2 * 64 * 4), S, ra.E_local, bound);
+    route_block<kFusedRouteMaxVpl>(ra, rl, blockIdx.x == 0);
+    ntiles = __builtin_amdgcn_readfirstlane(rl.t1[ra.E_local]);
+  } else {
+    ntiles = tile_count(a);
+  }
   int64_t ub, ue;
-  share_of((int64_t)tile_count(a) * FB, &ub, &ue);
+  share_of((int64_t)ntiles * FB, &ub, &ue);
   const uint32_t gbytes = (uint32_t)(16 * (H / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(H) * 256);
   const int64_t cpe = codes_per_expert(a.N, H), spe = scales_per_expert(a.N, H);
@@ -280,7 +295,14 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
   for (int64_t sb = ub; sb < ue;) {
     const int t = (int)(sb / FB);
     const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
-    const int4 ti = tile_entry(a, t);
+    int4 ti;
+    if constexpr (ROUTE) {
+      const int4 v = rl.tiles[t];
+      ti = make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), 0);
+    } else {
+      ti = tile_entry(a, t);
+    }
     const int rows = ti.y;
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
@@ -298,8 +320,12 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
     // this lane's tile row and its token (garbage past the tile's rows: unused)
-    const int32_t tok_raw = a.tile_tok[(int64_t)t * 16 + r];
     const bool valid = r < rows;
+    int32_t tok_raw;
+    if constexpr (ROUTE)
+      tok_raw = rl.ptok[p0 + (valid ? r : 0)];
+    else
+      tok_raw = a.tile_tok[(int64_t)t * 16 + r];
     const int64_t tok = valid ? tok_raw : 0;
     ASlice<KPW, A4> at;
     if constexpr (A4) {
@@ -527,26 +553,35 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
   return hipSuccess;
 }
 
-template <typename Kernel>
-hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, const GemmArgs& a,
-                             hipStream_t s) {
+template <typename Kernel, typename... Args>
+hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, hipStream_t s,
+                             const Args&... args) {
   int grid = 0;
   hipError_t e = resident_grid(reinterpret_cast<const void*>(kernel), nw * 64, lds, &grid);
   if (e != hipSuccess) return e;
   if ((int64_t)grid > max_units) grid = (int)max_units;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), lds, s, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), lds, s, args...);
   return hipGetLastError();
 }
 
 template <int KPW, int D, bool A4>
-hipError_t gate_up_v(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+hipError_t gate_up_v(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, hipStream_t s) {
   const int KT = (int)(a.K / kTileK);
   const int nw = (KT + KPW - 1) / KPW;
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 2 / 16);
-  const size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
-  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true>, nw, lds, mu, a, s)
-                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false>, nw, lds, mu, a, s);
+  size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
+  if (r) {
+    const int64_t S = r->T * (int64_t)r->top_k;
+    const int64_t bound = (r->E_local < S ? r->E_local : S) + S / 16;
+    lds += (size_t)route_block_words(S, r->E_local, bound) * sizeof(int32_t);
+    if (lds > kRouteFusedMaxLds) return hipErrorInvalidValue;
+    return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true, true>, nw, lds, mu, s, a, *r)
+                         : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false, true>, nw, lds, mu, s, a, *r);
+  }
+  const RouteArgs none{};
+  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true, false>, nw, lds, mu, s, a, none)
+                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false, false>, nw, lds, mu, s, a, none);
 }
 
 template <int KPW, int D, bool A4, bool ORDERED>
@@ -557,13 +592,13 @@ hipError_t down_v(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 16 / NG);
   const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
-  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, true>, nw, lds, mu, a, s)
-                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, false>, nw, lds, mu, a, s);
+  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, true>, nw, lds, mu, s, a)
+                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, false>, nw, lds, mu, s, a);
 }
 
 template <int KPW, int D>
-hipError_t gate_up_kd(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
-  return a4 ? gate_up_v<KPW, D, true>(a, max_tiles, s) : gate_up_v<KPW, D, false>(a, max_tiles, s);
+hipError_t gate_up_kd(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, bool a4, hipStream_t s) {
+  return a4 ? gate_up_v<KPW, D, true>(a, r, max_tiles, s) : gate_up_v<KPW, D, false>(a, r, max_tiles, s);
 }
 template <int KPW, int D>
 hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
@@ -574,15 +609,16 @@ hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, 
 
 #define MXMOE_DECODE_VARIANTS(F) F(2, 1) F(2, 2) F(4, 1) F(4, 2)
 
-hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, bool a4,
+                                 hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   const Variant v = pick(a.K);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return gate_up_kd<KPW, D>(a, max_tiles, a4, s);
+  if (v.kpw == KPW && v.d == D) return gate_up_kd<KPW, D>(a, route, max_tiles, a4, s);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return gate_up_kd<5, 1>(a, max_tiles, a4, s);
-  return gate_up_kd<8, 1>(a, max_tiles, a4, s);
+  if (v.kpw == 5) return gate_up_kd<5, 1>(a, route, max_tiles, a4, s);
+  return gate_up_kd<8, 1>(a, route, max_tiles, a4, s);
 }
 
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {

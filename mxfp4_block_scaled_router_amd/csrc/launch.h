@@ -8,6 +8,8 @@
 namespace mxmoe {
 
 constexpr size_t kRouteFusedMaxLds = 48 * 1024;
+// the decode gate_up kernel routes tokens itself only for E_global <= 16 x this
+constexpr int kFusedRouteMaxVpl = 8;
 
 struct RouteArgs {
   const float* logits;  // [T][E_global]
@@ -103,11 +105,17 @@ struct GemmPlan {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+// whether the routing of a is small enough for the decode gate_up kernel to
+// route the tokens itself in each workgroup
+bool route_fusable(const RouteArgs& a);
 hipError_t launch_gate_up(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
                           hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
                        bool ordered, hipStream_t stream);
-hipError_t launch_gate_up_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
+// route non-null: every workgroup routes the tokens itself first (no routing
+// kernel before it); only when route_fusable(*route)
+hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, bool a4,
+                                 hipStream_t stream);
 // 128-token x 256-weight-row tiles, LDS ring fed by global->LDS copies (tile.hip)
 hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
 hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t stream);

@@ -1,0 +1,361 @@
+// Device side of the router and the token permutation, shared by the routing
+// kernels and by the decode gate_up kernel, which routes a few tokens itself
+// at its start.  Helpers have internal linkage (one copy per source file).
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace mxmoe {
+
+namespace {
+
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
+
+// DPP row (16-lane) butterflies: quad [1,0,3,2], quad [2,3,0,1], half mirror,
+// mirror.  Each pairs every lane with a distinct partner, so after the four
+// steps every lane of the row holds the row's reduction.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return v;
+}
+
+// Keys: orderable logit in the high word, inverted expert id in the low word,
+// so a larger key is a larger logit or, on a tie, the lower id; every real key
+// is nonzero and no two are equal.  Sorted descending within the lane
+// (bitonic network over the lane's N keys).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ stride;
+        if (l > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t x = k[i], y = k[l];
+          const bool sw = desc ? (x < y) : (x > y);
+          k[i] = sw ? y : x;
+          k[l] = sw ? x : y;
+        }
+      }
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_step_u64(uint64_t v) {
+  const uint64_t o = dpp_u64<CTRL>(v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t row16_max_key(uint64_t v) {
+  v = max_step_u64<kDppXor1>(v);
+  v = max_step_u64<kDppXor2>(v);
+  v = max_step_u64<kDppHalfMirror>(v);
+  return max_step_u64<kDppMirror>(v);
+}
+
+// Top-k of token t by the 16-lane row of this lane.  lexp_out[s - slot_base]
+// receives the local expert (or -1) of each of the token's k slots s; with
+// write_global the ids and weights also go to a.ids and a.w.
+// Each lane holds logits r, r + 16, ... as sorted keys; a round takes the
+// row's largest head (16-lane butterfly) and the one lane that holds it pops.
+template <int VPL>
+__device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
+                         bool write_global) {
+  const int r = lane_id() & 15;
+  const int E = a.E_global, k = a.top_k;
+  const float* row = a.logits + t * (int64_t)E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = r + 16 * i;
+    const bool in = e < E;
+    const float v = in ? row[e] : 0.0f;
+    key[i] = in ? ((uint64_t)orderable(v) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  sort_desc<VPL>(key);
+  uint64_t p0 = 0, p1 = 0, mx = 0;  // picks r and r + 16, first pick
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = row16_max_key(key[0]);
+    const bool pop = key[0] == best;
+#pragma unroll
+    for (int i = 0; i + 1 < VPL; ++i) key[i] = pop ? key[i + 1] : key[i];
+    key[VPL - 1] = pop ? 0ull : key[VPL - 1];
+    if (j == 0) mx = best;
+    if (j == r) p0 = best;
+    if (j == r + 16) p1 = best;
+  }
+  const uint32_t maxhi = (uint32_t)(mx >> 32);
+  const uint32_t p0hi = (uint32_t)(p0 >> 32), p0lo = (uint32_t)p0;
+  const uint32_t p1hi = (uint32_t)(p1 >> 32), p1lo = (uint32_t)p1;
+  const double m = (double)from_orderable(maxhi);
+  const bool has0 = r < k, has1 = r + 16 < k;
+  const double e0 = has0 ? exp((double)from_orderable(p0hi) - m) : 0.0;
+  const double e1 = has1 ? exp((double)from_orderable(p1hi) - m) : 0.0;
+  const double sum = row16_sum_f64(e0 + e1);
+  const int64_t s0 = t * k;
+  if (has0) {
+    int id = (int)(0xFFFFFFFFu - p0lo);
+    const float w = (float)(e0 / sum);
+    if (write_global) {
+      a.ids[s0 + r] = id;
+      a.w[s0 + r] = w;
+    }
+    if (w_out) w_out[s0 + r - slot_base] = w;
+    int le = id - a.first_local;
+    lexp_out[s0 + r - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
+  }
+  if (has1) {
+    int id = (int)(0xFFFFFFFFu - p1lo);
+    const float w = (float)(e1 / sum);
+    if (write_global) {
+      a.ids[s0 + r + 16] = id;
+      a.w[s0 + r + 16] = w;
+    }
+    if (w_out) w_out[s0 + r + 16 - slot_base] = w;
+    int le = id - a.first_local;
+    lexp_out[s0 + r + 16 - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
+  }
+}
+
+// MAXVPL: largest logits-per-lane variant compiled in (E_global <= 16 MAXVPL)
+template <int MAXVPL = 32>
+__device__ void topk_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
+                         bool write_global = true) {
+  const int vpl = (a.E_global + 15) / 16;
+  if (vpl <= 1) topk_row<1>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (vpl <= 2) topk_row<2>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (MAXVPL <= 4 || vpl <= 4) topk_row<4>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (MAXVPL <= 8 || vpl <= 8) topk_row<8>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (MAXVPL <= 16 || vpl <= 16) topk_row<16>(a, t, lexp_out, w_out, slot_base, write_global);
+  else topk_row<32>(a, t, lexp_out, w_out, slot_base, write_global);
+}
+
+// Rank of each slot of chunk c among the chunk's slots with the same local
+// expert, and the chunk's per-expert counts cnt[e * stride] (zeroed
+// beforehand; only experts present in the chunk are written).  One wave.
+// The lanes holding the same expert are found bit by bit: one ballot per bit
+// of the expert id (nbits = bits of E_local - 1), each lane keeping the lanes
+// that agree with its own bit -- a fixed number of ballots, however many
+// distinct experts the chunk holds.
+__device__ void chunk_ranks(int64_t S, int64_t c, const int32_t* lexp, int32_t* cnt, int64_t stride,
+                            int32_t* rank, int nbits) {
+  const int lane = lane_id();
+  const int64_t s = c * 64 + lane;
+  const int e = s < S ? lexp[s] : -1;
+  uint64_t same = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  if (e >= 0) {
+    const uint64_t below = same & ((1ull << lane) - 1ull);
+    if (below == 0) cnt[e * stride] = __popcll(same);
+    if (s < S) rank[s] = __popcll(below);
+  } else if (s < S) {
+    rank[s] = 0;
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each 16-lane
+// row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read 0), then
+// lane 15 of rows 0 and 2 added into rows 1 and 3 (row_bcast:15) and lane 31
+// into rows 2 and 3 (row_bcast:31); rows masked off keep adding 0.
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
+// Exclusive scan of the per-expert counts v[0..n) by one wave: expert offsets
+// and, for the two token-tile heights mt1/mt2, tile offsets (prefix of
+// ceil(v/mt)) into offs_lds[0..n] and t1_lds[0..n] (entry n = total).  With
+// write_global it also writes a.offsets, a.tile_off1/2 and the flat tile
+// tables tiles1/tiles2: tile i -> {expert, rows, first sorted position, 0}.
+// tiles_lds (may be null) receives the mt1 tile table.
+__device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, bool write_global,
+                                  int32_t* offs_lds, int32_t* t1_lds, int4* tiles_lds = nullptr) {
+  const int lane = lane_id();
+  const int mt1 = a.mt1, mt2 = a.mt2;
+  const int per = (n + 63) / 64;
+  const int b = lane * per;
+  int32_t s0 = 0, s1 = 0, s2 = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      int32_t c = v[b + i];
+      s0 += c;
+      s1 += (c + mt1 - 1) / mt1;
+      s2 += (c + mt2 - 1) / mt2;
+    }
+  // inclusive wave prefix of the lane totals
+  const int32_t i0 = wave_incl_sum(s0), i1 = wave_incl_sum(s1), i2 = wave_incl_sum(s2);
+  int32_t r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      const int e = b + i;
+      const int32_t c = v[e];
+      offs_lds[e] = r0;
+      t1_lds[e] = r1;
+      if (tiles_lds)
+        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt1, ++j)
+          tiles_lds[r1 + j] = make_int4(e, c - m0 < mt1 ? c - m0 : mt1, r0 + m0, 0);
+      if (write_global) {
+        a.offsets[e] = r0;
+        a.tile_off1[e] = r1;
+        a.tile_off2[e] = r2;
+        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt1, ++j)
+          a.tiles1[r1 + j] = make_int4(e, c - m0 < mt1 ? c - m0 : mt1, r0 + m0, 0);
+        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt2, ++j)
+          a.tiles2[r2 + j] = make_int4(e, c - m0 < mt2 ? c - m0 : mt2, r0 + m0, 0);
+      }
+      r0 += c;
+      r1 += (c + mt1 - 1) / mt1;
+      r2 += (c + mt2 - 1) / mt2;
+    }
+  if (lane == 63) {
+    offs_lds[n] = i0;
+    t1_lds[n] = i1;
+    if (write_global) {
+      a.offsets[n] = i0;
+      a.tile_off1[n] = i1;
+      a.tile_off2[n] = i2;
+    }
+  }
+}
+
+// Sorted position pos of slot s: the permutation both ways, the side tables
+// (token and router weight w of pos) and -- for 16-row tiles -- the token of
+// that tile row.  off_e, tile_e: offset and first 16-row tile of the slot's
+// expert.
+__device__ __forceinline__ void place_slot(const RouteArgs& a, int64_t s, int32_t pos, float w, int32_t off_e,
+                                           int32_t tile_e) {
+  const int32_t t = (int32_t)(s / a.top_k);
+  a.sorted[pos] = (int32_t)s;
+  a.inv[s] = pos;
+  a.pos_tok[pos] = t;
+  a.pos_w[pos] = w;
+  if (a.tile_tok) {
+    const int32_t rel = pos - off_e;
+    a.tile_tok[(int64_t)(tile_e + rel / 16) * 16 + rel % 16] = t;
+  }
+}
+
+// LDS of route_block in 32-bit words: the mt1 tile table (int4 entries, first,
+// so it stays 16-byte aligned), then per slot expert / rank / weight, the
+// per-position token, chunk counts, counts and the two offset arrays.
+__host__ __device__ constexpr int64_t route_block_words(int64_t S, int64_t E, int64_t tile_bound) {
+  return 4 * tile_bound + 4 * S + ((S + 63) / 64) * E + 3 * E + 2;
+}
+
+struct RouteLds {
+  int4* tiles;     // [tile bound]  mt1 tiles {expert, rows, first sorted position, 0}
+  int32_t* lexp;   // [S]
+  int32_t* rank;   // [S]
+  float* wl;       // [S]
+  int32_t* ptok;   // [S]  token of each sorted position
+  int32_t* cnt;    // [nchunk][E]
+  int32_t* counts; // [E]
+  int32_t* offs;   // [E + 1]
+  int32_t* t1;     // [E + 1]  mt1 tile offsets; t1[E] = number of tiles
+};
+
+// tile_bound 0: no LDS tile table (tiles is null and nothing is written there)
+__device__ __forceinline__ RouteLds route_lds(int32_t* base, int64_t S, int64_t E, int64_t tile_bound) {
+  RouteLds L;
+  L.tiles = tile_bound > 0 ? reinterpret_cast<int4*>(base) : nullptr;
+  L.lexp = base + 4 * tile_bound;
+  L.rank = L.lexp + S;
+  L.wl = reinterpret_cast<float*>(L.rank + S);
+  L.ptok = reinterpret_cast<int32_t*>(L.wl + S);
+  L.cnt = L.ptok + S;
+  L.counts = L.cnt + ((S + 63) / 64) * E;
+  L.offs = L.counts + E;
+  L.t1 = L.offs + E + 1;
+  return L;
+}
+
+// The whole routing of a.T tokens by one workgroup (any number of waves),
+// everything after the logits kept in LDS: slot experts, weights and ranks,
+// chunk counts, counts, expert and tile offsets, the mt1 tile table and the
+// token of every sorted position.  With write_global the workgroup also writes
+// every global routing table (ids, w, counts, offsets, tile tables, sorted,
+// inv, pos_tok, pos_w, tile_tok).  Ends with the LDS results visible to the
+// whole workgroup.  MAXVPL: as in topk_any.
+template <int MAXVPL = 32>
+__device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_global) {
+  const int nwaves = blockDim.x / 64;
+  const int wave = threadIdx.x / 64, lane = lane_id();
+  const int64_t S = a.T * (int64_t)a.top_k;
+  const int64_t nchunk = (S + 63) / 64;
+  const int E = a.E_local;
+  for (int64_t i = threadIdx.x; i < nchunk * E; i += blockDim.x) L.cnt[i] = 0;
+  for (int64_t t = wave * 4 + (lane >> 4); t < a.T; t += nwaves * 4)
+    topk_any<MAXVPL>(a, t, L.lexp, L.wl, 0, write_global);
+  __syncthreads();
+  const int nbits = 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1));
+  for (int64_t c = wave; c < nchunk; c += nwaves) chunk_ranks(S, c, L.lexp, L.cnt + c * E, 1, L.rank, nbits);
+  __syncthreads();
+  // per expert: running sum over chunks -> chunk bases; totals -> counts
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t run = 0;
+    for (int64_t c = 0; c < nchunk; ++c) {
+      int32_t v = L.cnt[c * E + e];
+      L.cnt[c * E + e] = run;
+      run += v;
+    }
+    L.counts[e] = run;
+    if (write_global) a.counts[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) wave_scan_experts(L.counts, E, a, write_global, L.offs, L.t1, L.tiles);
+  __syncthreads();
+  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = L.lexp[s];
+    if (e >= 0) {
+      const int32_t pos = L.offs[e] + L.cnt[(s / 64) * E + e] + L.rank[s];
+      L.ptok[pos] = (int32_t)(s / a.top_k);
+      if (write_global) place_slot(a, s, pos, L.wl[s], L.offs[e], L.t1[e]);
+    } else if (write_global) {
+      a.inv[s] = -1;
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace
+
+
+}  // namespace mxmoe
