@@ -94,20 +94,31 @@ bool separate_route_kernel() {
   return env && !strcmp(env, "1");
 }
 
+// Token-tile height by the expected rows per expert, r = T*k / E_global
+// (measured on MI355X with the decode and prefill layers' dims, T from 6 to
+// 8192): 16-row tiles, which stream an expert's weights once per 16 rows, win
+// up to r = 24 and lose from r = 36; 64-row tiles win at r = 36 and lose to
+// the 128 x 512 tiles from r = 64.
+constexpr int64_t kRowsPerExpert16 = 28;
+constexpr int64_t kRowsPerExpert64 = 48;
+
 GemmPlan choose_plan(const Shape& s) {
-  // expected rows per local expert ~ T*k / E_global
   GemmPlan p;
   // the K-split kernels address activations through 32-bit buffer offsets and
   // use one wave per 512 elements of K (at most 16 waves)
   const bool ksplit_ok = s.T * s.H * 2 < (int64_t(1) << 30) && s.S * s.I * 2 < (int64_t(1) << 30) &&
                          s.H <= 8192 && s.I <= 8192 && (s.I / 16) % 4 == 0 && (s.H / 32) % 4 == 0;
-  if (s.S <= 16 * s.Eg && ksplit_ok) {
+  // MXFP4_MOE_PLAN=16|64|128 (benchmarks only) forces the token-tile height
+  int forced = 0;
+  if (const char* env = getenv("MXFP4_MOE_PLAN")) forced = atoi(env);
+  const bool lds64 = forced == 64 || (forced == 0 && s.S <= kRowsPerExpert64 * s.Eg);
+  if (ksplit_ok && (forced == 16 || (forced == 0 && s.S <= kRowsPerExpert16 * s.Eg))) {
     p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
-  } else if (const char* env = getenv("MXFP4_MOE_PREFILL_KERNEL"); env && !strcmp(env, "lds")) {
-    // 64-token tiles with register-fed weights (kept for comparison)
+  } else if (lds64) {
+    // 64-token tiles with register-fed weights
     p.ms = 4; p.fg = 2; p.nw = 4; p.direct_a = 0;
   } else {
-    // 128-token x 256-weight-row tiles staged through LDS
+    // 128-token x 512-weight-row tiles staged through LDS
     p.ms = 8; p.fg = 0; p.nw = 4; p.direct_a = 0;
   }
   return p;

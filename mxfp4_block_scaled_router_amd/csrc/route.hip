@@ -17,6 +17,8 @@
 // scan over chunks gives each (chunk, expert) its base, an exclusive scan over
 // experts the offsets, and the scatter puts slot s at
 // offsets[e] + base[chunk][e] + rank[s] -- the stable counting sort.
+#include <stdlib.h>
+
 #include "route_dev.h"
 
 namespace mxmoe {
@@ -129,7 +131,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (S == 0) return hipSuccess;
   const int64_t work = a.T * ((a.E_global + 15) / 16) * a.top_k;  // per-lane compare rounds
   const size_t lds = small_lds_bytes(S, a.E_local);
-  if (lds <= kRouteFusedMaxLds && work <= 8192) {
+  // one workgroup wins up to ~48 tokens of 64 experts, top-8 (measured)
+  int64_t small_work = 2048;
+  if (const char* env = getenv("MXFP4_MOE_ROUTE_SMALL_WORK")) small_work = atoll(env);  // benchmarks only
+  if (lds <= kRouteFusedMaxLds && work <= small_work) {
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), lds, stream, a);
     return hipGetLastError();
   }

@@ -23,6 +23,8 @@ Workloads (shapes and value distributions of the layer's five configurations):
   a4       T=4096 H=4096 I=1536 E=128/128 k=8  x~N(0,1); weights are Student-t(3)
            values times (3K)^-1/2 in fp32 (K = H for w13, K = I for w2), handed over
            unquantised: each side applies its own MXFP4 quantiser
+  verify_bB  T=6B (B = 1, 8, 16, 32, 48) with decode's dims and distributions:
+           speculative verification of 5 draft tokens + 1 per sequence
 
 Every array comes from its own child stream of numpy's SeedSequence(seed), so an
 array does not depend on which other arrays were drawn.  The Student-t weights are
@@ -79,6 +81,11 @@ WORKLOADS = {
     "a4": Workload("a4", 4096, 4096, 1536, 128, 128, 0, 8, weight_kind="student_t", a4=True,
                    seed=1004),
 }
+# Speculative-verify shapes: the decode layer's dims with T = 6 tokens per
+# sequence (5 draft tokens + 1) for batches 1..48.
+for _b, _seed in ((1, 1005), (8, 1006), (16, 1007), (32, 1008), (48, 1009)):
+    WORKLOADS["verify_b%d" % _b] = Workload("verify_b%d" % _b, 6 * _b, 2048, 1536, 64, 64, 0, 8,
+                                            scale_lo=118, scale_hi=124, seed=_seed)
 
 _STREAMS = ("x", "logits", "bias", "w13", "w13s", "w2", "w2s", "outlier_channels", "student_t")
 

@@ -109,6 +109,15 @@ def test_plan_query(lib):
     # many rows per expert: large tiles, always the slot-ordered gather
     big = mx.mxfp4_moe_plan(dims(T=4096, E_global=8, E_local=8), 2)
     assert big == {"tile_rows": 128, "ordered_combine": True}
+    # speculative-verify shapes of the decode layer (T = 6 per sequence): the
+    # tile height follows the expected rows per expert T*k/E_global
+    from mxfp4_block_scaled_router_amd import workloads as W
+    want = {"verify_b1": 16, "verify_b8": 16, "verify_b16": 16, "verify_b32": 16, "verify_b48": 64,
+            "decode": 16, "ep_share": 16, "prefill": 128, "a4": 128}
+    for name, rows in want.items():
+        wl = W.WORKLOADS[name]
+        d = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4)
+        assert mx.mxfp4_moe_plan(d, wl.top_k)["tile_rows"] == rows, name
     out = ctypes.c_int32()
     assert lib.mxfp4_moe_plan(ctypes.byref(dims()), 2, None, ctypes.byref(out)) == NULL_POINTER
     assert lib.mxfp4_moe_plan(ctypes.byref(dims(H=0)), 2, ctypes.byref(out), ctypes.byref(out)) == EMPTY_SHAPE

@@ -51,6 +51,8 @@ SMALL_CASES = {
 A4_CASES = {
     "a4_tiny": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
     "a4_mid": W.WORKLOADS["a4"].replace(T=512, H=1024, I=512, E_global=16, E_local=16, top_k=4),
+    # 32 rows per expert: the 64-row tiles
+    "a4_rows32": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=4),
 }
 
 
@@ -113,6 +115,15 @@ def _sample_mask(T, n, seed):
     m[rng.choice(T, size=min(n, T), replace=False)] = True
     m[0] = m[T - 1] = True
     return m
+
+
+@pytest.mark.parametrize("name", ["verify_b1", "verify_b8", "verify_b32", "verify_b48"])
+def test_forward_verify_shapes(name):
+    """Speculative-verify batches at full size, through the tile height each
+    one is dispatched to (16-row tiles up to batch 32, 64-row at batch 48)."""
+    case = Case(W.WORKLOADS[name])
+    T = case.wl.T
+    _check_case(case, token_mask=None if T <= 16 else _sample_mask(T, 24, 2))
 
 
 def test_forward_ep_share_full_sampled():
