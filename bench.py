@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--deterministic", action="store_true", help="ordered combine")
+    ap.add_argument("--shared", action="store_true",
+                    help="with the shared expert (one more expert every token reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -75,21 +77,26 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 10}), flush=True)
 
 
-def build_inputs(wl, copies):
+def build_inputs(wl, copies, shared=False):
     import numpy as np
     import torch
     import mxfp4_block_scaled_router_amd as mx
     from mxfp4_block_scaled_router_amd import workloads as W
     inp = W.make_inputs(wl)
-    dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4)
+    dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4,
+                        shared=shared)
+    nw = wl.E_local + (1 if shared else 0)  # experts in the weight buffers
     x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).cuda()
     logits = torch.from_numpy(inp["logits"]).cuda()
     if wl.weight_kind == "uniform":
+        if shared:
+            inp.update(zip(("w13", "w13s", "w2", "w2s"),
+                           W.make_uniform_weights(wl.replace(E_local=nw))))
         canon = [torch.from_numpy(inp[k]).cuda() for k in ("w13", "w13s", "w2", "w2s")]
     else:
         # Student-t weights drawn on the GPU and quantised by the library's OCP
         # quantiser (the load-time step), expert by expert
-        E, H, I = wl.E_local, wl.H, wl.I
+        E, H, I = nw, wl.H, wl.I
         canon = [torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
                  torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device="cuda"),
                  torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda"),
@@ -111,7 +118,7 @@ def build_inputs(wl, copies):
     return inp, dims, x, logits, banks, bank
 
 
-def cpu_baseline(wl, inp, target_s):
+def cpu_baseline(wl, inp, target_s, shared=False):
     """Oracle on a bounded sample: whole steps when one step is small enough,
     else a subset of tokens (token_mask); returns tokens/s on this host."""
     import numpy as np
@@ -122,7 +129,7 @@ def cpu_baseline(wl, inp, target_s):
         t0 = time.perf_counter()
         oracle.moe_forward(inp["x"], inp["logits"], inp["w13"], inp["w13s"], inp["w2"], inp["w2s"],
                            top_k=wl.top_k, clamp_limit=wl.clamp_limit, E_global=wl.E_global,
-                           first_local=wl.first_local, a4=wl.a4, token_mask=mask,
+                           first_local=wl.first_local, a4=wl.a4, shared=shared, token_mask=mask,
                            want_act=False, nthreads=threads)
         return time.perf_counter() - t0
 
@@ -165,7 +172,7 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     mx.load_library()
-    inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies)
+    inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies, args.shared)
     if args.deterministic:
         dims.flags |= mx.MXFP4_MOE_DETERMINISTIC
     k = wl.top_k
@@ -261,7 +268,8 @@ def main():
                                             "Student-t(3) weights quantised on the GPU"),
         "config": {"workload": "%s T=%d H=%d I=%d E=%d/%d top-%d clamp=%g%s" % (
             wl.name, T, H, I, wl.E_local, wl.E_global, k, wl.clamp_limit,
-            " A4" if wl.a4 else ""), "T": T, "H": H, "I": I, "E_local": wl.E_local,
+            (" A4" if wl.a4 else "") + (" +shared expert" if args.shared else "")),
+            "T": T, "H": H, "I": I, "E_local": wl.E_local, "shared_expert": bool(args.shared),
             "E_global": wl.E_global, "top_k": k, "touched_experts": touched,
             "local_assignments": n_assign, "weight_copies_rotated": len(banks),
             "bank_bytes": bank_bytes, "combine": "ordered" if plan["ordered_combine"] else "atomic",
@@ -280,7 +288,7 @@ def main():
         if "w13" not in inp:
             rec["cpu_baseline"] = None   # Student-t weights live on the GPU only
         else:
-            rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+            rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.shared)
     print(json.dumps(rec), flush=True)
 
 

@@ -79,6 +79,19 @@ extern "C" {
                                         contractions on scaled FP4 MFMA */
 #define MXFP4_MOE_DETERMINISTIC 0x2u /* combine by an ordered gather instead of fp32
                                         atomics: bit-identical results run to run */
+#define MXFP4_MOE_SHARED_EXPERT 0x4u /* the weight buffers hold E_local + 1 experts: the
+                                        last is a shared MXFP4 expert of the same shape
+                                        that every token reads with weight 1 (the
+                                        always-active MoE MLP whose projections the
+                                        campaign page "glm53-mxfp4-mi355x", section "The
+                                        model card and the metadata disagree", finds
+                                        stored as packed FP4 with a scale tensor).  It
+                                        takes one more slot per token, after the top_k
+                                        routed ones: routing tables and intermediates
+                                        below then have top_k + 1 slots per token and
+                                        E_local + 1 experts (slot top_k: id E_global,
+                                        weight 1, table expert E_local).  In an
+                                        expert-parallel split exactly one share sets it. */
 
 typedef struct mxfp4_moe_dims {
   int64_t T;           /* tokens */
@@ -87,7 +100,7 @@ typedef struct mxfp4_moe_dims {
   int64_t E_global;    /* experts the router chooses among (logit columns) */
   int64_t E_local;     /* experts held by this GPU */
   int64_t first_local; /* global id of local expert 0 */
-  uint32_t flags;      /* MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC */
+  uint32_t flags;      /* MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT */
   uint32_t reserved;   /* must be 0 */
 } mxfp4_moe_dims;
 
@@ -101,7 +114,8 @@ const char* mxfp4_moe_status_string(int status);
 int mxfp4_moe_last_hip_error(void);
 
 /*
- * Sizes of the preshuffled (gfx950) weight tensors for all E_local experts.
+ * Sizes of the preshuffled (gfx950) weight tensors for all E_local experts (and
+ * the shared one with MXFP4_MOE_SHARED_EXPERT).
  * Outputs: bytes of w13 codes, w13 scales, w2 codes, w2 scales.  Codes keep the
  * canonical byte count; scales are padded to whole 512-element K groups.
  */
@@ -110,7 +124,8 @@ int mxfp4_moe_preshuffled_bytes(const mxfp4_moe_dims* d, size_t* w13_bytes,
 
 /*
  * One-time weight layout change, canonical -> gfx950 preshuffled.
- * Canonical inputs (device):
+ * Canonical inputs (device; E_local + 1 experts with MXFP4_MOE_SHARED_EXPERT,
+ * the shared one last):
  *   canon_w13  uint8 [E_local][2I][H/2]   rows 0..I-1 gate, I..2I-1 up; element k of
  *                                          a row in byte k/2, low nibble for even k
  *   canon_w13s uint8 [E_local][2I][H/32]  UE8M0 scale of elements 32b..32b+31

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmxfp4_moe.so")
 
 MXFP4_MOE_A4 = 0x1
 MXFP4_MOE_DETERMINISTIC = 0x2
+MXFP4_MOE_SHARED_EXPERT = 0x4
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
@@ -45,10 +46,16 @@ class Dims(ctypes.Structure):
 
     @classmethod
     def make(cls, T, H, I, E_global, E_local=None, first_local=0, a4=False,
-             deterministic=False) -> "Dims":
-        flags = (MXFP4_MOE_A4 if a4 else 0) | (MXFP4_MOE_DETERMINISTIC if deterministic else 0)
+             deterministic=False, shared=False) -> "Dims":
+        flags = ((MXFP4_MOE_A4 if a4 else 0) | (MXFP4_MOE_DETERMINISTIC if deterministic else 0)
+                 | (MXFP4_MOE_SHARED_EXPERT if shared else 0))
         return cls(T, H, I, E_global, E_global if E_local is None else E_local, first_local,
                    flags, 0)
+
+    @property
+    def shared(self) -> int:
+        """1 when the weights carry the shared expert (one more slot per token)."""
+        return 1 if self.flags & MXFP4_MOE_SHARED_EXPERT else 0
 
 
 EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
@@ -245,13 +252,14 @@ def mxfp4_moe_forward_debug(dims: Dims, x, router_logits, w13, w13s, w2, w2s, to
     _dev_tensor(x, torch.bfloat16, "x")
     _dev_tensor(router_logits, torch.float32, "router_logits")
     T, H, I, k = dims.T, dims.H, dims.I, int(top_k)
+    ks = k + dims.shared  # slots per token
     dev = x.device
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    act = torch.zeros((T * k, I), dtype=torch.bfloat16, device=dev)
+    act = torch.zeros((T * ks, I), dtype=torch.bfloat16, device=dev)
     a4 = bool(dims.flags & MXFP4_MOE_A4)
-    actq = torch.zeros((T * k, I // 2), dtype=torch.uint8, device=dev) if a4 else None
-    acts = torch.zeros((T * k, I // 32), dtype=torch.uint8, device=dev) if a4 else None
+    actq = torch.zeros((T * ks, I // 2), dtype=torch.uint8, device=dev) if a4 else None
+    acts = torch.zeros((T * ks, I // 32), dtype=torch.uint8, device=dev) if a4 else None
     xq = torch.zeros((T, H // 2), dtype=torch.uint8, device=dev) if a4 else None
     xs = torch.zeros((T, H // 32), dtype=torch.uint8, device=dev) if a4 else None
     out32 = torch.zeros((T, H), dtype=torch.float32, device=dev)
@@ -270,13 +278,14 @@ def mxfp4_moe_route(dims: Dims, router_logits, top_k: int, workspace=None):
     tensors; the first offsets[-1] entries of sorted are valid)."""
     _dev_tensor(router_logits, torch.float32, "router_logits")
     T, k, El = dims.T, int(top_k), dims.E_local
+    ks, Et = k + dims.shared, El + dims.shared  # slots per token, table experts
     dev = router_logits.device
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(El, dtype=torch.int32, device=dev)
-    offsets = torch.empty(El + 1, dtype=torch.int32, device=dev)
-    sorted_ = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
-    inv = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    ids = torch.empty((T, ks), dtype=torch.int32, device=dev)
+    w = torch.empty((T, ks), dtype=torch.float32, device=dev)
+    counts = torch.empty(Et, dtype=torch.int32, device=dev)
+    offsets = torch.empty(Et + 1, dtype=torch.int32, device=dev)
+    sorted_ = torch.empty(max(T * ks, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(T * ks, 1), dtype=torch.int32, device=dev)
     workspace, nbytes = _workspace(dims, top_k, workspace, dev)
     _check("mxfp4_moe_route",
            _L().mxfp4_moe_route(ctypes.byref(dims), _p(router_logits), k, _p(ids), _p(w),

@@ -31,9 +31,15 @@ bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // ---------------------------------------------------------------- shapes
+// With the shared expert (MXFP4_MOE_SHARED_EXPERT) every token has one more
+// slot, after its kp routed picks, on one more expert, after the Er routed
+// local ones: El and k count the tables' experts and slots, shared one
+// included, so everything after the top-k selection runs unchanged.
 struct Shape {
   int64_t T, H, I, Eg, El, f, k;
-  int64_t S;  // T * k
+  int64_t S;       // T * k: slots
+  int64_t Er, kp;  // routed local experts, routed picks per token
+  int64_t sh;      // 1 with the shared expert
   bool a4, ordered;
 };
 
@@ -42,7 +48,8 @@ GemmPlan choose_plan(const Shape& s);
 int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!d) return MXFP4_MOE_ERR_NULL_POINTER;
   if (d->reserved != 0) return MXFP4_MOE_ERR_BAD_ARGUMENT;
-  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC)) return MXFP4_MOE_ERR_BAD_FLAGS;
+  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT))
+    return MXFP4_MOE_ERR_BAD_FLAGS;
   if (d->T < 0 || d->H < 0 || d->I < 0 || d->E_global < 0 || d->E_local < 0 || d->first_local < 0)
     return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->H == 0 || d->I == 0 || d->E_global == 0 || d->E_local == 0)
@@ -60,9 +67,12 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   s->H = d->H;
   s->I = d->I;
   s->Eg = d->E_global;
-  s->El = d->E_local;
+  s->sh = (d->flags & MXFP4_MOE_SHARED_EXPERT) ? 1 : 0;
+  s->Er = d->E_local;
+  s->El = d->E_local + s->sh;
   s->f = d->first_local;
-  s->k = need_k ? top_k : 1;
+  s->kp = need_k ? top_k : 1;
+  s->k = s->kp + s->sh;
   s->a4 = (d->flags & MXFP4_MOE_A4) != 0;
   s->ordered = (d->flags & MXFP4_MOE_DETERMINISTIC) != 0;
   // element counts that the kernels index with int64 and int32
@@ -220,6 +230,8 @@ RouteArgs route_args(const Shape& s, const float* logits, void* ws, const Layout
   r.T = s.T;
   r.E_global = (int32_t)s.Eg;
   r.E_local = (int32_t)s.El;
+  r.E_route = (int32_t)s.Er;
+  r.picks = (int32_t)s.kp;
   r.first_local = (int32_t)s.f;
   r.top_k = (int32_t)s.k;
   r.mt1 = mt1;

@@ -583,6 +583,10 @@ hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t s) {
   dim3 grid((unsigned)((n4 + 255) / 256));
   if (ordered && a.top_k <= 8 && a.T <= INT32_MAX)
     hipLaunchKernelGGL(combine_gather_kernel<8>, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  else if (ordered && a.top_k == 9 && a.T <= INT32_MAX)  // top-8 + the shared expert
+    hipLaunchKernelGGL(combine_gather_kernel<9>, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  else if (ordered && a.top_k <= 16 && a.T <= INT32_MAX)
+    hipLaunchKernelGGL(combine_gather_kernel<16>, dim3((unsigned)a.T), dim3(256), 0, s, a);
   else if (ordered)
     hipLaunchKernelGGL(combine_ordered_kernel, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(cast_out_kernel, grid, dim3(256), 0, s, a);

@@ -14,7 +14,12 @@ constexpr int kFusedRouteMaxVpl = 8;
 struct RouteArgs {
   const float* logits;  // [T][E_global]
   int64_t T;
+  // E_local: experts in the tables; top_k: slots per token.  With the shared
+  // expert they exceed the routed local experts E_route and the router's picks
+  // by one: slot t*top_k + picks of every token is on table expert E_route,
+  // weight 1, id E_global.
   int32_t E_global, E_local, first_local, top_k;
+  int32_t E_route, picks;
   int32_t mt1, mt2;     // token-tile heights of the gate_up and down kernels
   int32_t* ids;         // [S]
   float* w;             // [S]

@@ -129,7 +129,7 @@ bool route_fusable(const RouteArgs& a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int64_t S = a.T * (int64_t)a.top_k;
   if (S == 0) return hipSuccess;
-  const int64_t work = a.T * ((a.E_global + 15) / 16) * a.top_k;  // per-lane compare rounds
+  const int64_t work = a.T * ((a.E_global + 15) / 16) * a.picks;  // per-lane compare rounds
   const size_t lds = small_lds_bytes(S, a.E_local);
   // one workgroup wins up to ~48 tokens of 64 experts, top-8 (measured)
   int64_t small_work = 2048;

@@ -91,7 +91,7 @@ template <int VPL>
 __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
                          bool write_global) {
   const int r = lane_id() & 15;
-  const int E = a.E_global, k = a.top_k;
+  const int E = a.E_global, k = a.picks;
   const float* row = a.logits + t * (int64_t)E;
   uint64_t key[VPL];
 #pragma unroll
@@ -121,7 +121,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
   const double e0 = has0 ? exp((double)from_orderable(p0hi) - m) : 0.0;
   const double e1 = has1 ? exp((double)from_orderable(p1hi) - m) : 0.0;
   const double sum = row16_sum_f64(e0 + e1);
-  const int64_t s0 = t * k;
+  const int64_t s0 = t * a.top_k;  // slots per token (picks + shared)
   if (has0) {
     int id = (int)(0xFFFFFFFFu - p0lo);
     const float w = (float)(e0 / sum);
@@ -131,7 +131,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
     }
     if (w_out) w_out[s0 + r - slot_base] = w;
     int le = id - a.first_local;
-    lexp_out[s0 + r - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
+    lexp_out[s0 + r - slot_base] = (le >= 0 && le < a.E_route) ? le : -1;
   }
   if (has1) {
     int id = (int)(0xFFFFFFFFu - p1lo);
@@ -142,7 +142,16 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
     }
     if (w_out) w_out[s0 + r + 16 - slot_base] = w;
     int le = id - a.first_local;
-    lexp_out[s0 + r + 16 - slot_base] = (le >= 0 && le < a.E_local) ? le : -1;
+    lexp_out[s0 + r + 16 - slot_base] = (le >= 0 && le < a.E_route) ? le : -1;
+  }
+  // shared expert: the slot after the picks, table expert E_route, weight 1
+  if (a.top_k > k && r == 0) {
+    if (write_global) {
+      a.ids[s0 + k] = E;
+      a.w[s0 + k] = 1.0f;
+    }
+    if (w_out) w_out[s0 + k - slot_base] = 1.0f;
+    lexp_out[s0 + k - slot_base] = a.E_route;
   }
 }
 

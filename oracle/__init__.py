@@ -61,7 +61,7 @@ def _load():
     lib.orc_route.restype = ctypes.c_int
     lib.orc_route.argtypes = [P, i64, i64, i32, P, P]
     lib.orc_permute.restype = i64
-    lib.orc_permute.argtypes = [P, i64, i32, i64, i64, P, P, P, P]
+    lib.orc_permute.argtypes = [P, i64, i32, i64, i64, i64, P, P, P, P]
     lib.orc_swiglu.restype = ctypes.c_float
     lib.orc_swiglu.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
     lib.orc_moe_forward.restype = i64
@@ -75,7 +75,8 @@ class _Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("E_global", ctypes.c_int64), ("E_local", ctypes.c_int64),
                 ("first_local", ctypes.c_int64), ("top_k", ctypes.c_int32),
-                ("clamp_limit", ctypes.c_float), ("a4", ctypes.c_int32)]
+                ("clamp_limit", ctypes.c_float), ("a4", ctypes.c_int32),
+                ("shared", ctypes.c_int32), ("given_actq", ctypes.c_int32)]
 
 
 def _ptr(a):
@@ -147,14 +148,17 @@ def route(logits: np.ndarray, top_k: int):
     return ids, w
 
 
-def permute(ids: np.ndarray, first_local: int, E_local: int):
+def permute(ids: np.ndarray, first_local: int, E_local: int, shared_id: int = -1):
+    """Counting sort of the slots by local expert; with shared_id >= 0 the slots
+    holding that id form one more expert, table entry E_local."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     T, k = ids.shape
-    counts = np.empty(E_local, dtype=np.int32)
-    offsets = np.empty(E_local + 1, dtype=np.int32)
+    n_exp = E_local + (1 if shared_id >= 0 else 0)
+    counts = np.empty(n_exp, dtype=np.int32)
+    offsets = np.empty(n_exp + 1, dtype=np.int32)
     sorted_ = np.empty(T * k, dtype=np.int32)
     inv = np.empty(T * k, dtype=np.int32)
-    n = _load().orc_permute(_ptr(ids), T, k, first_local, E_local, _ptr(counts),
+    n = _load().orc_permute(_ptr(ids), T, k, first_local, E_local, shared_id, _ptr(counts),
                             _ptr(offsets), _ptr(sorted_), _ptr(inv))
     return counts, offsets, sorted_[:n].copy(), inv
 
@@ -180,14 +184,22 @@ class OracleResult:
 
 
 def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_global=None,
-                first_local=0, a4=False, token_mask=None, want_act=True, nthreads=0):
+                first_local=0, a4=False, shared=False, token_mask=None, want_act=True, nthreads=0,
+                actq_in=None, acts_in=None):
     """The whole layer on canonical-layout inputs (see ``moe_oracle.h``).
 
     ``x_bits``: uint16 bf16 bits [T, H]; ``logits``: float32 [T, E_global];
-    ``w13``: uint8 [E_local, 2I, H/2]; ``w13s``: uint8 [E_local, 2I, H/32];
-    ``w2``: uint8 [E_local, H, I/2]; ``w2s``: uint8 [E_local, H, I/32].
+    ``w13``: uint8 [E, 2I, H/2]; ``w13s``: uint8 [E, 2I, H/32];
+    ``w2``: uint8 [E, H, I/2]; ``w2s``: uint8 [E, H, I/32], where E = E_local
+    routed experts, plus one shared expert (the last) when ``shared``.  The
+    tables then have top_k + 1 slots per token (slot top_k: id E_global, weight
+    1) and E_local + 1 experts.
     ``token_mask`` (bool [T]) restricts expert work and the combine to the
     marked tokens; rows of ``out``/``out32`` for other tokens are left zero.
+    ``actq_in``/``acts_in`` (A4 only; [N_assign, I/2], [N_assign, I/32] in sorted
+    order): down reads these quantised SwiGLU outputs instead of quantising its
+    own, so a comparison downstream of that quantisation starts from the same
+    codes on both sides.
     """
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -196,18 +208,24 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     w2 = np.ascontiguousarray(w2, dtype=np.uint8)
     w2s = np.ascontiguousarray(w2s, dtype=np.uint8)
     T, H = x_bits.shape
-    E_local, two_i, _ = w13.shape
+    Ew, two_i, _ = w13.shape
     I = two_i // 2
+    sh = 1 if shared else 0
+    E_local = Ew - sh
     Eg = logits.shape[1] if E_global is None else E_global
-    assert logits.shape == (T, Eg)
-    assert w13.shape == (E_local, 2 * I, H // 2) and w13s.shape == (E_local, 2 * I, H // 32)
-    assert w2.shape == (E_local, H, I // 2) and w2s.shape == (E_local, H, I // 32)
-    d = _Dims(T, H, I, Eg, E_local, first_local, top_k, clamp_limit, 1 if a4 else 0)
-    S = T * top_k
-    ids = np.empty((T, top_k), np.int32)
-    w = np.empty((T, top_k), np.float32)
-    counts = np.empty(E_local, np.int32)
-    offsets = np.empty(E_local + 1, np.int32)
+    assert logits.shape == (T, Eg) and E_local >= 1
+    assert w13.shape == (Ew, 2 * I, H // 2) and w13s.shape == (Ew, 2 * I, H // 32)
+    assert w2.shape == (Ew, H, I // 2) and w2s.shape == (Ew, H, I // 32)
+    given = actq_in is not None
+    assert given == (acts_in is not None) and (a4 or not given)
+    d = _Dims(T, H, I, Eg, E_local, first_local, top_k, clamp_limit, 1 if a4 else 0, sh,
+              1 if given else 0)
+    k = top_k + sh
+    S = T * k
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    counts = np.empty(Ew, np.int32)
+    offsets = np.empty(Ew + 1, np.int32)
     sorted_ = np.zeros(max(S, 1), np.int32)
     inv = np.empty(max(S, 1), np.int32)
     act = np.zeros((max(S, 1), I), np.uint16) if want_act else None
@@ -217,6 +235,10 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     xs = np.zeros((T, H // 32), np.uint8) if a4 else None
     actq = np.zeros((max(S, 1), I // 2), np.uint8) if a4 else None
     acts = np.zeros((max(S, 1), I // 32), np.uint8) if a4 else None
+    if given:
+        n_in = np.asarray(actq_in).shape[0]
+        actq[:n_in] = actq_in
+        acts[:n_in] = acts_in
     mask = None
     if token_mask is not None:
         mask = np.ascontiguousarray(np.asarray(token_mask, dtype=bool).astype(np.uint8))

@@ -20,6 +20,12 @@
  *   - Routing: top-k of the router's softmax with renormalised weights; only the
  *     experts the router picked are read (campaign page, section "A file is a
  *     census; a decode step is a sample").
+ *   - Shared expert (optional): an MXFP4 MLP of the same shape that every token
+ *     reads, packed codes with a scale tensor beside them (campaign page,
+ *     section "The model card and the metadata disagree"), in the always-active
+ *     set of the census formula (section "A file is a census; a decode step is
+ *     a sample").  It enters the combine with weight 1 as one more slot per
+ *     token, after the k routed ones.
  *
  * Precision: x is bf16, every contraction accumulates in fp32 in increasing K
  * order from +0.0f, the SwiGLU output is rounded to bf16, the combine adds
@@ -260,22 +266,32 @@ int orc_route(const float* logits, int64_t T, int64_t E, int32_t k, int32_t* ids
 /* ---------------------------------------------------------------- permutation */
 
 /* Assignment slot s = t*k + j.  A slot is local when first_local <= id <
- * first_local + E_local; local expert e = id - first_local.  Counting sort that
- * keeps slot order within each expert. */
+ * first_local + E_local; local expert e = id - first_local.  With shared_id >= 0
+ * a slot whose id equals shared_id belongs to the shared expert, table entry
+ * E_local (the tables then have E_local + 1 experts).  Counting sort that keeps
+ * slot order within each expert. */
+static int64_t local_expert(int32_t id, int64_t first_local, int64_t E_local, int64_t shared_id) {
+  if (shared_id >= 0 && id == shared_id) return E_local;
+  int64_t e = (int64_t)id - first_local;
+  return (e >= 0 && e < E_local) ? e : -1;
+}
+
 int64_t orc_permute(const int32_t* ids, int64_t T, int32_t k, int64_t first_local, int64_t E_local,
-                    int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv) {
-  int64_t n_slots = T * k;
-  for (int64_t e = 0; e < E_local; ++e) counts[e] = 0;
+                    int64_t shared_id, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                    int32_t* inv) {
+  const int64_t n_slots = T * k;
+  const int64_t n_exp = E_local + (shared_id >= 0 ? 1 : 0);
+  for (int64_t e = 0; e < n_exp; ++e) counts[e] = 0;
   for (int64_t s = 0; s < n_slots; ++s) {
-    int64_t e = (int64_t)ids[s] - first_local;
-    if (e >= 0 && e < E_local) counts[e] += 1;
+    int64_t e = local_expert(ids[s], first_local, E_local, shared_id);
+    if (e >= 0) counts[e] += 1;
   }
   offsets[0] = 0;
-  for (int64_t e = 0; e < E_local; ++e) offsets[e + 1] = offsets[e] + counts[e];
-  int32_t* cursor = (int32_t*)calloc((size_t)(E_local > 0 ? E_local : 1), sizeof(int32_t));
+  for (int64_t e = 0; e < n_exp; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* cursor = (int32_t*)calloc((size_t)(n_exp > 0 ? n_exp : 1), sizeof(int32_t));
   for (int64_t s = 0; s < n_slots; ++s) {
-    int64_t e = (int64_t)ids[s] - first_local;
-    if (e >= 0 && e < E_local) {
+    int64_t e = local_expert(ids[s], first_local, E_local, shared_id);
+    if (e >= 0) {
       int32_t pos = offsets[e] + cursor[e];
       cursor[e] += 1;
       sorted[pos] = (int32_t)s;
@@ -285,7 +301,7 @@ int64_t orc_permute(const int32_t* ids, int64_t T, int32_t k, int64_t first_loca
     }
   }
   free(cursor);
-  return offsets[E_local];
+  return offsets[n_exp];
 }
 
 /* ---------------------------------------------------------------- SwiGLU */
@@ -309,9 +325,12 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
                         float* out32, uint16_t* out, int32_t nthreads) {
   const int64_t T = d->T, H = d->H, I = d->I, Eg = d->E_global, El = d->E_local;
   const int64_t f = d->first_local;
-  const int32_t k = d->top_k;
+  const int32_t kr = d->top_k;               /* routed picks per token */
+  const int32_t sh = d->shared ? 1 : 0;      /* shared expert present */
+  const int32_t k = kr + sh;                 /* slots per token */
+  const int64_t Ew = El + sh;                /* experts in the weight buffers and tables */
   if (T < 0 || H <= 0 || I <= 0 || H % 32 || I % 32 || El <= 0 || Eg <= 0 || f < 0 ||
-      f + El > Eg || k < 1 || k > Eg)
+      f + El > Eg || kr < 1 || kr > Eg || (d->given_actq && (!d->a4 || !actq || !acts)))
     return -2;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -321,14 +340,31 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
   const int64_t S = T * k;
   int32_t* ids_ = ids ? ids : (int32_t*)malloc(sizeof(int32_t) * (size_t)(S ? S : 1));
   float* w_ = w ? w : (float*)malloc(sizeof(float) * (size_t)(S ? S : 1));
-  int32_t* cnt_ = counts ? counts : (int32_t*)malloc(sizeof(int32_t) * (size_t)El);
-  int32_t* off_ = offsets ? offsets : (int32_t*)malloc(sizeof(int32_t) * (size_t)(El + 1));
+  int32_t* cnt_ = counts ? counts : (int32_t*)malloc(sizeof(int32_t) * (size_t)Ew);
+  int32_t* off_ = offsets ? offsets : (int32_t*)malloc(sizeof(int32_t) * (size_t)(Ew + 1));
   int32_t* sor_ = sorted ? sorted : (int32_t*)malloc(sizeof(int32_t) * (size_t)(S ? S : 1));
   int32_t* inv_ = inv ? inv : (int32_t*)malloc(sizeof(int32_t) * (size_t)(S ? S : 1));
 
-  int64_t status = orc_route(logits, T, Eg, k, ids_, w_);
+  /* the k routed picks of token t go to slots t*k + j, j < kr; the shared
+   * expert (id E_global, outside the router's range) takes slot t*k + kr with
+   * weight 1 */
+  int32_t* rids = (int32_t*)malloc(sizeof(int32_t) * nz(T * kr));
+  float* rw = (float*)malloc(sizeof(float) * nz(T * kr));
+  int64_t status = orc_route(logits, T, Eg, kr, rids, rw);
+  for (int64_t t = 0; t < T && status == 0; ++t) {
+    for (int32_t j = 0; j < kr; ++j) {
+      ids_[t * k + j] = rids[t * kr + j];
+      w_[t * k + j] = rw[t * kr + j];
+    }
+    if (sh) {
+      ids_[t * k + kr] = (int32_t)Eg;
+      w_[t * k + kr] = 1.0f;
+    }
+  }
+  free(rids);
+  free(rw);
   int64_t N = 0;
-  if (status == 0) N = orc_permute(ids_, T, k, f, El, cnt_, off_, sor_, inv_);
+  if (status == 0) N = orc_permute(ids_, T, k, f, El, sh ? Eg : -1, cnt_, off_, sor_, inv_);
 
   /* activations as fp32 values: x itself, or (A4) x quantised along H and
    * decoded again */
@@ -361,7 +397,7 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
   float* w2t = (float*)malloc(sizeof(float) * (size_t)(I * H));
   float* rowbuf = (float*)malloc(sizeof(float) * (size_t)(H > 2 * I ? H : 2 * I));
 
-  for (int64_t e = 0; e < El && status == 0; ++e) {
+  for (int64_t e = 0; e < Ew && status == 0; ++e) {
     int any = 0;
     for (int64_t p = off_[e]; p < off_[e + 1]; ++p) any |= (yrow[p] >= 0);
     if (!any) continue;
@@ -403,7 +439,9 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       for (int64_t i = 0; i < I; ++i) ab[i] = orc_bf16_from_f32(orc_swiglu(h[i], h[I + i], d->clamp_limit));
       if (act)
         for (int64_t i = 0; i < I; ++i) act[p * I + i] = ab[i];
-      if (d->a4) {
+      if (d->a4 && d->given_actq) {
+        orc_dequant(actq + p * (I / 2), acts + p * (I / 32), 1, I, a);
+      } else if (d->a4) {
         uint8_t* q = (uint8_t*)malloc((size_t)(I / 2));
         uint8_t* s = (uint8_t*)malloc((size_t)(I / 32));
         orc_quantize_bf16(ab, 1, I, q, s);

@@ -32,6 +32,11 @@ typedef struct {
   int32_t top_k;
   float clamp_limit;
   int32_t a4; /* 1: x and the SwiGLU output are MXFP4-quantised before each contraction */
+  int32_t shared; /* 1: the weight buffers hold E_local + 1 experts; the last is a shared
+                     expert every token reads with weight 1 (slot k of each token) */
+  int32_t given_actq; /* A4 only, 1: down reads actq/acts as inputs (the quantised SwiGLU
+                         output of another implementation, rows in sorted order)
+                         instead of quantising its own; everything else unchanged */
 } orc_dims;
 
 /* element and scale decoding */
@@ -54,9 +59,12 @@ float orc_f32_from_bf16(uint16_t b);
 /* router: softmax over all global experts, top-k, renormalise over the k picks */
 int orc_route(const float* logits, int64_t T, int64_t E_global, int32_t k, int32_t* ids, float* w);
 
-/* local filter + histogram + exclusive scan + stable scatter; returns N_assign */
+/* local filter + histogram + exclusive scan + stable scatter; returns N_assign.
+ * shared_id >= 0: slots with that id go to table entry E_local (the shared
+ * expert; counts/offsets then have E_local + 1 / E_local + 2 entries). */
 int64_t orc_permute(const int32_t* ids, int64_t T, int32_t k, int64_t first_local, int64_t E_local,
-                    int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv);
+                    int64_t shared_id, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                    int32_t* inv);
 
 /* clamped SwiGLU of one (gate, up) pair in fp32 */
 float orc_swiglu(float g, float u, float limit);
@@ -65,6 +73,8 @@ float orc_swiglu(float g, float u, float limit);
  * Full layer.  token_mask (nullable, uint8 [T]) restricts the expert work and
  * the combine to the tokens whose mask byte is non-zero; the routing tables are
  * always produced for every token.  Outputs that are NULL are not written.
+ *   (with the shared expert read k as top_k + 1 and E_local as E_local + 1 below;
+ *    ids[t][top_k] = E_global and w[t][top_k] = 1 mark the shared slot)
  *   ids/w      [T][k]             counts [E_local], offsets [E_local+1]
  *   sorted/inv [T*k]              act bf16 bits [T*k][I] (row p = sorted position p)
  *   xq/xs      [T][H/2], [T][H/32]          (A4 only)

@@ -43,15 +43,24 @@ class Case:
     """Inputs of one parity case, on host (canonical numpy) and device."""
 
     def __init__(self, wl: W.Workload, inp: dict | None = None, a4: bool | None = None,
-                 deterministic: bool = False):
+                 deterministic: bool = False, shared: bool = False):
         self.wl = wl
         self.a4 = wl.a4 if a4 is None else a4
         self.deterministic = deterministic
-        self.inp = W.make_inputs(wl) if inp is None else inp
+        self.shared = shared
+        if inp is not None:
+            self.inp = inp
+        elif shared and wl.weight_kind == "uniform":
+            # one more expert's weights, drawn as the routed ones: the shared expert
+            self.inp = W.make_inputs(wl, weights=False)
+            wlw = wl.replace(E_local=wl.E_local + 1)
+            self.inp.update(zip(("w13", "w13s", "w2", "w2s"), W.make_uniform_weights(wlw)))
+        else:
+            self.inp = W.make_inputs(wl)
         if "w13" not in self.inp:
             self._quantise_student_t()
         self.dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local,
-                                 a4=self.a4, deterministic=deterministic)
+                                 a4=self.a4, deterministic=deterministic, shared=shared)
         self.x = bf16_dev(self.inp["x"])
         self.logits = to_dev(self.inp["logits"])
         canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
@@ -62,7 +71,7 @@ class Case:
         """Student-t weights: drawn on the GPU, quantised there by the library and
         on the host by the oracle; both codes must agree bit for bit."""
         wl = self.wl
-        E, H, I = wl.E_local, wl.H, wl.I
+        E, H, I = wl.E_local + (1 if self.shared else 0), wl.H, wl.I
         w13 = np.empty((E, 2 * I, H // 2), np.uint8)
         w13s = np.empty((E, 2 * I, H // 32), np.uint8)
         w2 = np.empty((E, H, I // 2), np.uint8)
@@ -95,13 +104,14 @@ class Case:
         torch.cuda.synchronize()
         return {k: v.cpu().numpy() for k, v in r.items()}
 
-    def run_oracle(self, token_mask=None):
+    def run_oracle(self, token_mask=None, actq_in=None, acts_in=None):
         wl = self.wl
         return oracle.moe_forward(self.inp["x"], self.inp["logits"], self.inp["w13"],
                                   self.inp["w13s"], self.inp["w2"], self.inp["w2s"],
                                   top_k=wl.top_k, clamp_limit=wl.clamp_limit,
                                   E_global=wl.E_global, first_local=wl.first_local, a4=self.a4,
-                                  token_mask=token_mask, want_act=token_mask is None)
+                                  shared=self.shared, token_mask=token_mask,
+                                  want_act=token_mask is None, actq_in=actq_in, acts_in=acts_in)
 
 
 def compare_route(g: dict, o) -> None:

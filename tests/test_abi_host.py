@@ -75,7 +75,7 @@ def ws_status(d, k=2):
     ({}, -1, BAD_TOP_K), ({}, 9, BAD_TOP_K), ({"E_global": 64, "E_local": 64}, 33, BAD_TOP_K),
     ({"T": 1 << 40}, 8, SHAPE_OVERFLOW), ({"T": 1 << 60, "H": 1 << 10}, 2, SHAPE_OVERFLOW),
     ({"first_local": (1 << 63) - 4}, 2, SHAPE_OVERFLOW),
-    ({"flags": 0x4}, 2, BAD_FLAGS),
+    ({"flags": 0x8}, 2, BAD_FLAGS),
 ])
 def test_dims_refusals(lib, kw, k, expect):
     st, _ = ws_status(dims(**kw), k)
@@ -93,6 +93,21 @@ def test_workspace_grows_with_flags(lib):
     _, det = ws_status(dims(flags=mx.MXFP4_MOE_DETERMINISTIC))
     _, a4 = ws_status(dims(flags=mx.MXFP4_MOE_A4))
     assert base > 0 and det > 0 and a4 > base
+
+
+def test_shared_expert_sizes(lib):
+    """The shared expert is one more expert in the weight buffers and one more
+    slot per token in the workspace."""
+    plain = mx.mxfp4_moe_preshuffled_bytes(dims(H=512, I=256, E_local=8))
+    shared = mx.mxfp4_moe_preshuffled_bytes(dims(H=512, I=256, E_local=8,
+                                                 flags=mx.MXFP4_MOE_SHARED_EXPERT))
+    for a, b in zip(plain, shared):
+        assert b == a // 8 * 9
+    _, base = ws_status(dims())
+    st, sh = ws_status(dims(flags=mx.MXFP4_MOE_SHARED_EXPERT))
+    assert st == 0 and sh > base
+    d = dims(flags=mx.MXFP4_MOE_SHARED_EXPERT)
+    assert mx.mxfp4_moe_plan(d, 2)["tile_rows"] in (16, 64, 128)
 
 
 def test_null_dims(lib):

@@ -234,6 +234,25 @@ def test_a4_mode_quantises_x_and_act():
     np.testing.assert_array_equal(r16.act, r.act)
 
 
+def test_a4_down_from_given_codes():
+    """Down from caller-supplied activation codes: the oracle's own codes give
+    its end-to-end result bit for bit; one changed block changes exactly the
+    output row of the token that owns it."""
+    wl, inp = _small(T=16, H=256, I=128, E=4, k=2, seed=62)
+    args = (inp["x"], inp["logits"], inp["w13"], inp["w13s"], inp["w2"], inp["w2s"])
+    r = oracle.moe_forward(*args, top_k=2, clamp_limit=7.0, a4=True)
+    again = oracle.moe_forward(*args, top_k=2, clamp_limit=7.0, a4=True, actq_in=r.actq,
+                               acts_in=r.acts)
+    np.testing.assert_array_equal(again.out32, r.out32)
+    q = r.actq.copy()
+    q[5, :16] ^= 0x11                                   # another code in 32 elements of row 5
+    moved = oracle.moe_forward(*args, top_k=2, clamp_limit=7.0, a4=True, actq_in=q,
+                               acts_in=r.acts)
+    t5 = int(r.sorted[5]) // 2
+    diff_rows = np.nonzero((moved.out32 != r.out32).any(axis=1))[0]
+    assert list(diff_rows) == [t5]
+
+
 def test_tamper_control_is_caught():
     """A flipped weight byte of a routed expert must change the output."""
     wl, inp = _small(T=16, H=256, I=128, E=4, k=2, seed=71)
