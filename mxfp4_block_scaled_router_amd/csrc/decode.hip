@@ -245,9 +245,30 @@ __device__ __forceinline__ bool reduce_to_wave0(f32x4_t (&acc)[NG], float* red, 
 // through an empty descriptor (no traffic).  Nothing loaded is
 // carried from one segment to the next, so no loaded register has to be
 // copied at a join (such a copy waits for every load in flight).
-__device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue) {
-  *ub = U * blockIdx.x / gridDim.x;
-  *ue = U * (blockIdx.x + 1) / gridDim.x;
+// Shares weighted by dispatch slot: of the workgroups resident on one CU the
+// ones dispatched later stream more slowly, so workgroup b, the (b / cus)-th
+// on its CU, gets a share in proportion to 1 / (1 + c * (b / cus)).  W(b) is
+// the weight of the workgroups before b; every workgroup evaluates it the same
+// way, so the shares tile [0, U) exactly.  cus == 0 or c == 0: equal shares.
+__device__ __forceinline__ double slot_weight_before(unsigned b, unsigned G, unsigned cus, float c) {
+  double w = 0.0;
+  for (unsigned s = 0, b0 = 0; b0 < b; ++s, b0 += cus) {
+    const unsigned n = (b - b0 < cus ? b - b0 : cus);
+    w += (double)n / (1.0 + (double)c * s);
+  }
+  (void)G;
+  return w;
+}
+__device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, int cus = 0, float c = 0.f) {
+  if (cus <= 0 || c == 0.f) {
+    *ub = U * blockIdx.x / gridDim.x;
+    *ue = U * (blockIdx.x + 1) / gridDim.x;
+    return;
+  }
+  const unsigned G = gridDim.x, b = blockIdx.x;
+  const double tot = slot_weight_before(G, G, cus, c);
+  *ub = b == 0 ? 0 : (int64_t)((double)U * (slot_weight_before(b, G, cus, c) / tot));
+  *ue = b + 1 == G ? U : (int64_t)((double)U * (slot_weight_before(b + 1, G, cus, c) / tot));
 }
 
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
@@ -284,7 +305,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     ntiles = tile_count(a);
   }
   int64_t ub, ue;
-  share_of((int64_t)ntiles * FB, &ub, &ue);
+  share_of((int64_t)ntiles * FB, &ub, &ue, a.slot_cus, a.slot_c);
   const uint32_t gbytes = (uint32_t)(16 * (H / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(H) * 256);
   const int64_t cpe = codes_per_expert(a.N, H), spe = scales_per_expert(a.N, H);
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   const int kt0 = wave * KPW;
   const int FB = (int)(H / (16 * NG));
   int64_t ub, ue;
-  share_of((int64_t)tile_count(a) * FB, &ub, &ue);
+  share_of((int64_t)tile_count(a) * FB, &ub, &ue, a.slot_cus, a.slot_c);
   const uint32_t gbytes = (uint32_t)(16 * (I / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(I) * 256);
   const int64_t cpe = codes_per_expert(H, I), spe = scales_per_expert(H, I);
@@ -553,6 +574,31 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
   return hipSuccess;
 }
 
+// Slot weights c of the shares (measured on MI355X: with 3 workgroups per CU
+// the third streams ~1.35x slower than the first; c = 0.15 for gate_up and 0.1
+// for down took the kernels' last workgroups in by ~1 us).
+// MXFP4_MOE_SLOT_C_GU / MXFP4_MOE_SLOT_C_DN (benchmarks only) override them.
+float slot_c(const char* name, float dflt) {
+  const char* v = getenv(name);
+  return v ? (float)atof(v) : dflt;
+}
+std::mutex g_cus_mu;
+int g_cus[64];
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(g_cus_mu);
+    if (g_cus[dev] > 0) return g_cus[dev];
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(g_cus_mu);
+    g_cus[dev] = cus;
+  }
+  return cus;
+}
+
 template <typename Kernel, typename... Args>
 hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, hipStream_t s,
                              const Args&... args) {
@@ -565,7 +611,11 @@ hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_unit
 }
 
 template <int KPW, int D, bool A4>
-hipError_t gate_up_v(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, hipStream_t s) {
+hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, hipStream_t s) {
+  GemmArgs a = a0;
+  static const float c_gu = slot_c("MXFP4_MOE_SLOT_C_GU", 0.15f);
+  a.slot_c = c_gu;
+  a.slot_cus = a.slot_c != 0.f ? device_cus() : 0;
   const int KT = (int)(a.K / kTileK);
   const int nw = (KT + KPW - 1) / KPW;
   if (nw > 8) return hipErrorInvalidValue;
@@ -585,7 +635,11 @@ hipError_t gate_up_v(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, h
 }
 
 template <int KPW, int D, bool A4, bool ORDERED>
-hipError_t down_v(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
+  GemmArgs a = a0;
+  static const float c_dn = slot_c("MXFP4_MOE_SLOT_C_DN", 0.10f);
+  a.slot_c = c_dn;
+  a.slot_cus = a.slot_c != 0.f ? device_cus() : 0;
   constexpr int NG = 2;
   const int KT = (int)(a.K / kTileK);
   const int nw = (KT + KPW - 1) / KPW;

@@ -70,6 +70,9 @@ struct GemmArgs {
   // side duty: zero this fp32 buffer (grid-stride), may be null
   float* zero_buf;
   int64_t zero_n;
+  // 16-row kernels: shares weighted by dispatch slot (set by the launcher)
+  int32_t slot_cus;
+  float slot_c;
 };
 
 struct CombineArgs {
