@@ -53,6 +53,11 @@ def _load():
     lib.orc_ue8m0_value.restype = ctypes.c_double
     lib.orc_ue8m0_value.argtypes = [i32]
     lib.orc_dequant.argtypes = [P, P, i64, i64, P]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_value.argtypes = [i32]
+    lib.orc_dequant8.argtypes = [P, P, i64, i64, P]
+    for name in ("orc_quantize8_f64", "orc_quantize8_bf16"):
+        getattr(lib, name).argtypes = [P, i64, i64, P, P]
     for name in ("orc_quantize_f64", "orc_quantize_f32", "orc_quantize_bf16"):
         getattr(lib, name).argtypes = [P, i64, i64, P, P]
     lib.orc_bf16_from_f32.restype = ctypes.c_uint16
@@ -76,7 +81,8 @@ class _Dims(ctypes.Structure):
                 ("E_global", ctypes.c_int64), ("E_local", ctypes.c_int64),
                 ("first_local", ctypes.c_int64), ("top_k", ctypes.c_int32),
                 ("clamp_limit", ctypes.c_float), ("a4", ctypes.c_int32),
-                ("shared", ctypes.c_int32), ("given_actq", ctypes.c_int32)]
+                ("shared", ctypes.c_int32), ("given_actq", ctypes.c_int32),
+                ("a8", ctypes.c_int32)]
 
 
 def _ptr(a):
@@ -119,6 +125,37 @@ def quantize(v: np.ndarray):
     lib = _load()
     fn = {np.dtype(np.float64): lib.orc_quantize_f64, np.dtype(np.float32): lib.orc_quantize_f32,
           np.dtype(np.uint16): lib.orc_quantize_bf16}[v.dtype]
+    fn(_ptr(v), rows, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3_value(int(code))
+
+
+def dequant8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 codes [..., K] (one E4M3 byte each) + scales [..., K/32] -> float32."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    K = codes.shape[-1]
+    rows = codes.size // K
+    assert scales.size == rows * (K // 32)
+    out = np.empty(codes.shape, dtype=np.float32)
+    _load().orc_dequant8(_ptr(codes), _ptr(scales), rows, K, _ptr(out))
+    return out
+
+
+def quantize8(v: np.ndarray):
+    """OCP MX quantiser with E4M3 elements along the last axis.  ``v``: float64
+    or uint16 bf16 bits.  Returns (codes [..., K], scales [..., K/32])."""
+    v = np.ascontiguousarray(v)
+    K = v.shape[-1]
+    assert K % 32 == 0
+    rows = v.size // K
+    codes = np.empty(v.shape, dtype=np.uint8)
+    scales = np.empty(v.shape[:-1] + (K // 32,), dtype=np.uint8)
+    lib = _load()
+    fn = {np.dtype(np.float64): lib.orc_quantize8_f64, np.dtype(np.uint16): lib.orc_quantize8_bf16}[v.dtype]
     fn(_ptr(v), rows, K, _ptr(codes), _ptr(scales))
     return codes, scales
 
@@ -185,7 +222,7 @@ class OracleResult:
 
 def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_global=None,
                 first_local=0, a4=False, shared=False, token_mask=None, want_act=True, nthreads=0,
-                actq_in=None, acts_in=None):
+                actq_in=None, acts_in=None, a8=False):
     """The whole layer on canonical-layout inputs (see ``moe_oracle.h``).
 
     ``x_bits``: uint16 bf16 bits [T, H]; ``logits``: float32 [T, E_global];
@@ -196,10 +233,11 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     1) and E_local + 1 experts.
     ``token_mask`` (bool [T]) restricts expert work and the combine to the
     marked tokens; rows of ``out``/``out32`` for other tokens are left zero.
-    ``actq_in``/``acts_in`` (A4 only; [N_assign, I/2], [N_assign, I/32] in sorted
-    order): down reads these quantised SwiGLU outputs instead of quantising its
-    own, so a comparison downstream of that quantisation starts from the same
-    codes on both sides.
+    ``actq_in``/``acts_in`` (A4/A8 only; [N_assign, I/2] or [N_assign, I],
+    and [N_assign, I/32], in sorted order): down reads these quantised SwiGLU
+    outputs instead of quantising its own, so a comparison downstream of that
+    quantisation starts from the same codes on both sides.
+    ``a8``: as ``a4`` with MXFP8 (E4M3) codes, one byte per element.
     """
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -217,9 +255,9 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     assert w13.shape == (Ew, 2 * I, H // 2) and w13s.shape == (Ew, 2 * I, H // 32)
     assert w2.shape == (Ew, H, I // 2) and w2s.shape == (Ew, H, I // 32)
     given = actq_in is not None
-    assert given == (acts_in is not None) and (a4 or not given)
+    assert given == (acts_in is not None) and (a4 or a8 or not given) and not (a4 and a8)
     d = _Dims(T, H, I, Eg, E_local, first_local, top_k, clamp_limit, 1 if a4 else 0, sh,
-              1 if given else 0)
+              1 if given else 0, 1 if a8 else 0)
     k = top_k + sh
     S = T * k
     ids = np.empty((T, k), np.int32)
@@ -231,10 +269,12 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     act = np.zeros((max(S, 1), I), np.uint16) if want_act else None
     out32 = np.zeros((T, H), np.float32)
     out = np.zeros((T, H), np.uint16)
-    xq = np.zeros((T, H // 2), np.uint8) if a4 else None
-    xs = np.zeros((T, H // 32), np.uint8) if a4 else None
-    actq = np.zeros((max(S, 1), I // 2), np.uint8) if a4 else None
-    acts = np.zeros((max(S, 1), I // 32), np.uint8) if a4 else None
+    aq = a4 or a8
+    cpe = 1 if a8 else 2   # codes per byte
+    xq = np.zeros((T, H // cpe), np.uint8) if aq else None
+    xs = np.zeros((T, H // 32), np.uint8) if aq else None
+    actq = np.zeros((max(S, 1), I // cpe), np.uint8) if aq else None
+    acts = np.zeros((max(S, 1), I // 32), np.uint8) if aq else None
     if given:
         n_in = np.asarray(actq_in).shape[0]
         actq[:n_in] = actq_in

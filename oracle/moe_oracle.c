@@ -27,6 +27,10 @@
  *     a sample").  It enters the combine with weight 1 as one more slot per
  *     token, after the k routed ones.
  *
+ * Activation formats: bf16 (W4A16), or x and the SwiGLU output quantised per 32
+ * along K to MXFP4 (A4) or MXFP8 with E4M3 elements (A8) before the contraction
+ * that reads them.
+ *
  * Precision: x is bf16, every contraction accumulates in fp32 in increasing K
  * order from +0.0f, the SwiGLU output is rounded to bf16, the combine adds
  * w*y in fp32 in increasing slot order, and the output is rounded to bf16.
@@ -315,6 +319,106 @@ float orc_swiglu(float g, float u, float limit) {
   return (gc * sig) * uc;
 }
 
+/* ---------------------------------------------------------------- MXFP8 */
+
+/* E4M3 value of an 8-bit code: bit 7 sign, bits 6..3 exponent (bias 7), bits
+ * 2..0 mantissa.  e = 0 holds the subnormals m/8 * 2^-6; exponent 15 with
+ * mantissa 7 is NaN and there is no infinity, so the largest magnitude is
+ * 1.75 * 2^8 = 448 (the OCP 8-bit floating-point format that the MX
+ * specification pairs with the same UE8M0 block scale). */
+double orc_e4m3_value(int32_t code) {
+  int s = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp(m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Round a magnitude a >= 0 to the E4M3 grid: the step is 2^-9 below 2^-6 (the
+ * subnormals) and 2^(floor(log2 a) - 3) above (three mantissa bits); nearest
+ * multiple of the step, ties to the even multiple (the even code), saturating
+ * at 448.  Returns the 7-bit magnitude code, read off the rounded value. */
+static int e4m3_round_magnitude(double a) {
+  double step;
+  if (a < ldexp(1.0, -6)) {
+    step = ldexp(1.0, -9);
+  } else {
+    int E;
+    frexp(a, &E);
+    step = ldexp(1.0, (E - 1) - 3);
+  }
+  double q = rint(a / step) * step;
+  if (q > 448.0) q = 448.0;
+  if (q < ldexp(1.0, -6)) return (int)(q / ldexp(1.0, -9)); /* 0..7: the mantissa */
+  int E;
+  double f = frexp(q, &E); /* q = f * 2^E, f in [0.5, 1): exponent E - 1 */
+  int m = (int)((2.0 * f - 1.0) * 8.0);
+  return ((E - 1 + 7) << 3) | m;
+}
+
+/* One 32-element block, OCP rule for FP8 elements: shared exponent
+ * floor(log2 amax) - 8 (8 is the largest E4M3 exponent), biased by 127 and
+ * clamped to [0, 254]; each element is divided by the shared power of two and
+ * rounded to E4M3.  NaN/infinity and all-zero blocks as for MXFP4. */
+static void quantize8_block(const double* v, uint8_t* codes, uint8_t* scale) {
+  int nonfinite = 0;
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i) {
+    if (!isfinite(v[i]))
+      nonfinite = 1;
+    else if (fabs(v[i]) > amax)
+      amax = fabs(v[i]);
+  }
+  if (nonfinite) {
+    *scale = 255;
+    for (int i = 0; i < 32; ++i) codes[i] = 0;
+    return;
+  }
+  if (amax == 0.0) {
+    *scale = 0;
+    for (int i = 0; i < 32; ++i) codes[i] = signbit(v[i]) ? 0x80 : 0;
+    return;
+  }
+  int E;
+  frexp(amax, &E);
+  int s = (E - 1) - 8 + 127;
+  if (s < 0) s = 0;
+  if (s > 254) s = 254;
+  *scale = (uint8_t)s;
+  for (int i = 0; i < 32; ++i) {
+    double r = ldexp(v[i], 127 - s); /* exact in fp64 */
+    codes[i] = (uint8_t)((signbit(v[i]) ? 0x80 : 0) | e4m3_round_magnitude(fabs(r)));
+  }
+}
+
+void orc_quantize8_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
+                        uint8_t* scales) {
+  double blk[32];
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      for (int i = 0; i < 32; ++i) blk[i] = (double)orc_f32_from_bf16(v[r * K + b * 32 + i]);
+      quantize8_block(blk, codes + r * K + b * 32, scales + r * (K / 32) + b);
+    }
+}
+
+void orc_quantize8_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 32; ++b)
+      quantize8_block(v + r * K + b * 32, codes + r * K + b * 32, scales + r * (K / 32) + b);
+}
+
+void orc_dequant8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                  float* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k)
+      out[r * K + k] = (float)(orc_e4m3_value(codes[r * K + k]) * orc_ue8m0_value(scales[r * (K / 32) + k / 32]));
+}
+
 /* ---------------------------------------------------------------- layer */
 
 int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logits,
@@ -330,7 +434,8 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
   const int32_t k = kr + sh;                 /* slots per token */
   const int64_t Ew = El + sh;                /* experts in the weight buffers and tables */
   if (T < 0 || H <= 0 || I <= 0 || H % 32 || I % 32 || El <= 0 || Eg <= 0 || f < 0 ||
-      f + El > Eg || kr < 1 || kr > Eg || (d->given_actq && (!d->a4 || !actq || !acts)))
+      f + El > Eg || kr < 1 || kr > Eg || (d->a4 && d->a8) ||
+      (d->given_actq && (!(d->a4 || d->a8) || !actq || !acts)))
     return -2;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -376,6 +481,13 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       uint8_t* s = xs ? xs : (uint8_t*)malloc((size_t)(T * H / 32 ? T * H / 32 : 1));
       orc_quantize_bf16(x, T, H, q, s);
       orc_dequant(q, s, T, H, xf);
+      if (!xq) free(q);
+      if (!xs) free(s);
+    } else if (d->a8) {
+      uint8_t* q = xq ? xq : (uint8_t*)malloc(nz(T * H));
+      uint8_t* s = xs ? xs : (uint8_t*)malloc(nz(T * H / 32));
+      orc_quantize8_bf16(x, T, H, q, s);
+      orc_dequant8(q, s, T, H, xf);
       if (!xq) free(q);
       if (!xs) free(s);
     } else {
@@ -441,6 +553,17 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
         for (int64_t i = 0; i < I; ++i) act[p * I + i] = ab[i];
       if (d->a4 && d->given_actq) {
         orc_dequant(actq + p * (I / 2), acts + p * (I / 32), 1, I, a);
+      } else if (d->a8 && d->given_actq) {
+        orc_dequant8(actq + p * I, acts + p * (I / 32), 1, I, a);
+      } else if (d->a8) {
+        uint8_t* q = (uint8_t*)malloc((size_t)I);
+        uint8_t* s = (uint8_t*)malloc((size_t)(I / 32));
+        orc_quantize8_bf16(ab, 1, I, q, s);
+        orc_dequant8(q, s, 1, I, a);
+        if (actq) memcpy(actq + p * I, q, (size_t)I);
+        if (acts) memcpy(acts + p * (I / 32), s, (size_t)(I / 32));
+        free(q);
+        free(s);
       } else if (d->a4) {
         uint8_t* q = (uint8_t*)malloc((size_t)(I / 2));
         uint8_t* s = (uint8_t*)malloc((size_t)(I / 32));

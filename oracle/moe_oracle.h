@@ -34,9 +34,11 @@ typedef struct {
   int32_t a4; /* 1: x and the SwiGLU output are MXFP4-quantised before each contraction */
   int32_t shared; /* 1: the weight buffers hold E_local + 1 experts; the last is a shared
                      expert every token reads with weight 1 (slot k of each token) */
-  int32_t given_actq; /* A4 only, 1: down reads actq/acts as inputs (the quantised SwiGLU
+  int32_t given_actq; /* A4/A8 only, 1: down reads actq/acts as inputs (the quantised SwiGLU
                          output of another implementation, rows in sorted order)
                          instead of quantising its own; everything else unchanged */
+  int32_t a8; /* 1: as a4 with MXFP8 (E4M3 elements, one byte each): xq [T][H],
+                 actq [N][I]; scales as for a4.  a4 and a8 exclude each other */
 } orc_dims;
 
 /* element and scale decoding */
@@ -50,6 +52,15 @@ void orc_quantize_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, 
 void orc_quantize_f32(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales);
 void orc_quantize_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
                        uint8_t* scales);
+
+/* MXFP8: E4M3 element value (0x7F/0xFF NaN), quantiser (codes one byte per
+ * element, [rows][K]; scales [rows][K/32]) and dequantiser */
+double orc_e4m3_value(int32_t code);
+void orc_quantize8_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
+                        uint8_t* scales);
+void orc_quantize8_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales);
+void orc_dequant8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                  float* out);
 
 /* fp32 -> bf16, round to nearest even */
 uint16_t orc_bf16_from_f32(float f);
