@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP4 routed-expert MoE layer on one MI355X (gfx950).
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|tiny|ep_share|prefill|a4]
+    python bench.py [--steps K] [--warmup W] [--workload decode|tiny|ep_share|prefill|a4|a8|verify_bB]
 
 A step is one whole forward of the layer (route, permutation, gate_up + clamped
 SwiGLU, down + weighted combine, output cast) over one batch of seeded synthetic
@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp4": 10100.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 METRIC = "MXFP4 MoE tokens/s; decode HBM TB/s and prefill MFMA util vs peak"
 
 
@@ -84,7 +84,7 @@ def build_inputs(wl, copies, shared=False):
     from mxfp4_block_scaled_router_amd import workloads as W
     inp = W.make_inputs(wl)
     dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4,
-                        shared=shared)
+                        shared=shared, a8=wl.a8)
     nw = wl.E_local + (1 if shared else 0)  # experts in the weight buffers
     x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).cuda()
     logits = torch.from_numpy(inp["logits"]).cuda()
@@ -129,7 +129,8 @@ def cpu_baseline(wl, inp, target_s, shared=False):
         t0 = time.perf_counter()
         oracle.moe_forward(inp["x"], inp["logits"], inp["w13"], inp["w13s"], inp["w2"], inp["w2s"],
                            top_k=wl.top_k, clamp_limit=wl.clamp_limit, E_global=wl.E_global,
-                           first_local=wl.first_local, a4=wl.a4, shared=shared, token_mask=mask,
+                           first_local=wl.first_local, a4=wl.a4, a8=wl.a8, shared=shared,
+                           token_mask=mask,
                            want_act=False, nthreads=threads)
         return time.perf_counter() - t0
 
@@ -231,8 +232,9 @@ def main():
              "combine": 0}
     step_bytes = touched * (w13_b + w2_b) + T * H * 2 + T * wl.E_global * 4 + T * H * 2
     dominant = max(("gate_up", "down"), key=lambda p: phase_ms[p])
-    mfma_dtype = "fp4" if wl.a4 else "bf16"
-    if wl.name in ("prefill", "a4"):
+    # an FP8 x FP4 product issues at the FP8 rate
+    mfma_dtype = "fp4" if wl.a4 else ("fp8" if wl.a8 else "bf16")
+    if wl.name in ("prefill", "a4", "a8"):
         achieved = flops[dominant] / (phase_ms[dominant] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[mfma_dtype],
                 "unit": "TFLOP/s"}
@@ -268,7 +270,8 @@ def main():
                                             "Student-t(3) weights quantised on the GPU"),
         "config": {"workload": "%s T=%d H=%d I=%d E=%d/%d top-%d clamp=%g%s" % (
             wl.name, T, H, I, wl.E_local, wl.E_global, k, wl.clamp_limit,
-            (" A4" if wl.a4 else "") + (" +shared expert" if args.shared else "")),
+            (" A4" if wl.a4 else "") + (" A8" if wl.a8 else "") +
+            (" +shared expert" if args.shared else "")),
             "T": T, "H": H, "I": I, "E_local": wl.E_local, "shared_expert": bool(args.shared),
             "E_global": wl.E_global, "top_k": k, "touched_experts": touched,
             "local_assignments": n_assign, "weight_copies_rotated": len(banks),

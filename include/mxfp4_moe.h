@@ -92,6 +92,12 @@ extern "C" {
                                         E_local + 1 experts (slot top_k: id E_global,
                                         weight 1, table expert E_local).  In an
                                         expert-parallel split exactly one share sets it. */
+#define MXFP4_MOE_A8 0x8u            /* as MXFP4_MOE_A4 with MXFP8 activations: E4M3
+                                        elements (one byte each) under the same UE8M0
+                                        block scale (mxfp4_moe_quantize8), the FP8
+                                        operand of the same scaled MFMA.  Excludes
+                                        MXFP4_MOE_A4 (both: BAD_FLAGS).  Intermediates
+                                        below then hold one code byte per element. */
 
 typedef struct mxfp4_moe_dims {
   int64_t T;           /* tokens */
@@ -100,7 +106,8 @@ typedef struct mxfp4_moe_dims {
   int64_t E_global;    /* experts the router chooses among (logit columns) */
   int64_t E_local;     /* experts held by this GPU */
   int64_t first_local; /* global id of local expert 0 */
-  uint32_t flags;      /* MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT */
+  uint32_t flags;      /* MXFP4_MOE_A4 or MXFP4_MOE_A8, | MXFP4_MOE_DETERMINISTIC
+                          | MXFP4_MOE_SHARED_EXPERT */
   uint32_t reserved;   /* must be 0 */
 } mxfp4_moe_dims;
 
@@ -218,6 +225,21 @@ int mxfp4_moe_route(const mxfp4_moe_dims* d, const float* router_logits, int32_t
 #define MXFP4_MOE_DTYPE_F32 1
 int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
                        uint8_t* scales, hipStream_t stream);
+
+/*
+ * OCP MX quantiser with FP8 E4M3 elements (MXFP8; the format TensorFold PR
+ * #1050's FP4-Local checkpoint stores projections in, commit notes): rows x K
+ * values (K % 32 == 0) -> codes uint8 [rows][K] (one E4M3 byte per element:
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F/0xFF are NaN, no
+ * infinity), scales uint8 [rows][K/32].  Per 32-block: scale byte =
+ * clamp(floor(log2 amax) - 8 + 127, 0, 254); element = E4M3 nearest to
+ * v / 2^(scale-127), ties to the even code, saturating at +-448; NaN/inf
+ * blocks get scale 0xFF and zero codes.  Arguments and errors as
+ * mxfp4_moe_quantize.  The MXFP4_MOE_A8 path applies it to x and to the SwiGLU
+ * output.
+ */
+int mxfp4_moe_quantize8(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                        uint8_t* scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmxfp4_moe.so")
 MXFP4_MOE_A4 = 0x1
 MXFP4_MOE_DETERMINISTIC = 0x2
 MXFP4_MOE_SHARED_EXPERT = 0x4
+MXFP4_MOE_A8 = 0x8
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
@@ -46,9 +47,9 @@ class Dims(ctypes.Structure):
 
     @classmethod
     def make(cls, T, H, I, E_global, E_local=None, first_local=0, a4=False,
-             deterministic=False, shared=False) -> "Dims":
+             deterministic=False, shared=False, a8=False) -> "Dims":
         flags = ((MXFP4_MOE_A4 if a4 else 0) | (MXFP4_MOE_DETERMINISTIC if deterministic else 0)
-                 | (MXFP4_MOE_SHARED_EXPERT if shared else 0))
+                 | (MXFP4_MOE_SHARED_EXPERT if shared else 0) | (MXFP4_MOE_A8 if a8 else 0))
         return cls(T, H, I, E_global, E_global if E_local is None else E_local, first_local,
                    flags, 0)
 
@@ -61,7 +62,7 @@ class Dims(ctypes.Structure):
 EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
             "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
-            "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_plan")
+            "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_quantize8", "mxfp4_moe_plan")
 
 
 def load_library(path: str = LIB_PATH):
@@ -102,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_route.argtypes = [D, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.mxfp4_moe_quantize.restype = ctypes.c_int
     lib.mxfp4_moe_quantize.argtypes = [P, I32, I64, I64, P, P, P]
+    lib.mxfp4_moe_quantize8.restype = ctypes.c_int
+    lib.mxfp4_moe_quantize8.argtypes = [P, I32, I64, I64, P, P, P]
     _lib = lib
     return lib
 
@@ -197,6 +200,22 @@ def mxfp4_moe_quantize(values, in_dtype: int | None = None):
     return codes, scales
 
 
+def mxfp4_moe_quantize8(values, in_dtype: int | None = None):
+    """OCP MX quantiser with E4M3 elements on the GPU: [..., K] bf16 or float32 ->
+    (codes [..., K] one byte each, scales [..., K/32]) uint8 tensors."""
+    if in_dtype is None:
+        in_dtype = DTYPE_BF16 if values.dtype == torch.bfloat16 else DTYPE_F32
+    want = torch.bfloat16 if in_dtype == DTYPE_BF16 else torch.float32
+    _dev_tensor(values, want, "values")
+    K = values.shape[-1]
+    rows = values.numel() // K if K else 0
+    codes = torch.empty(values.shape, dtype=torch.uint8, device=values.device)
+    scales = torch.empty(values.shape[:-1] + (K // 32,), dtype=torch.uint8, device=values.device)
+    _check("mxfp4_moe_quantize8", _L().mxfp4_moe_quantize8(_p(values), int(in_dtype), rows, K,
+                                                          _p(codes), _p(scales), _stream()))
+    return codes, scales
+
+
 # ---------------------------------------------------------------- layer
 
 def _workspace(dims, top_k, workspace, device):
@@ -257,10 +276,12 @@ def mxfp4_moe_forward_debug(dims: Dims, x, router_logits, w13, w13s, w2, w2s, to
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     act = torch.zeros((T * ks, I), dtype=torch.bfloat16, device=dev)
-    a4 = bool(dims.flags & MXFP4_MOE_A4)
-    actq = torch.zeros((T * ks, I // 2), dtype=torch.uint8, device=dev) if a4 else None
+    a8 = bool(dims.flags & MXFP4_MOE_A8)
+    a4 = bool(dims.flags & MXFP4_MOE_A4) or a8   # quantised activations
+    q = 1 if a8 else 2                            # elements per code byte
+    actq = torch.zeros((T * ks, I // q), dtype=torch.uint8, device=dev) if a4 else None
     acts = torch.zeros((T * ks, I // 32), dtype=torch.uint8, device=dev) if a4 else None
-    xq = torch.zeros((T, H // 2), dtype=torch.uint8, device=dev) if a4 else None
+    xq = torch.zeros((T, H // q), dtype=torch.uint8, device=dev) if a4 else None
     xs = torch.zeros((T, H // 32), dtype=torch.uint8, device=dev) if a4 else None
     out32 = torch.zeros((T, H), dtype=torch.float32, device=dev)
     workspace, nbytes = _workspace(dims, top_k, workspace, dev)

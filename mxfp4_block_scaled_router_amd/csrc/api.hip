@@ -40,7 +40,11 @@ struct Shape {
   int64_t S;       // T * k: slots
   int64_t Er, kp;  // routed local experts, routed picks per token
   int64_t sh;      // 1 with the shared expert
-  bool a4, ordered;
+  bool a4, a8, ordered;
+  // activation format of the GEMMs: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 (A8)
+  int af() const { return a4 ? 1 : a8 ? 2 : 0; }
+  bool mx() const { return a4 || a8; }
+  int64_t qdiv() const { return a8 ? 1 : 2; }  // elements per code byte
 };
 
 GemmPlan choose_plan(const Shape& s);
@@ -48,8 +52,9 @@ GemmPlan choose_plan(const Shape& s);
 int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!d) return MXFP4_MOE_ERR_NULL_POINTER;
   if (d->reserved != 0) return MXFP4_MOE_ERR_BAD_ARGUMENT;
-  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT))
+  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT | MXFP4_MOE_A8))
     return MXFP4_MOE_ERR_BAD_FLAGS;
+  if ((d->flags & MXFP4_MOE_A4) && (d->flags & MXFP4_MOE_A8)) return MXFP4_MOE_ERR_BAD_FLAGS;
   if (d->T < 0 || d->H < 0 || d->I < 0 || d->E_global < 0 || d->E_local < 0 || d->first_local < 0)
     return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->H == 0 || d->I == 0 || d->E_global == 0 || d->E_local == 0)
@@ -74,6 +79,7 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   s->kp = need_k ? top_k : 1;
   s->k = s->kp + s->sh;
   s->a4 = (d->flags & MXFP4_MOE_A4) != 0;
+  s->a8 = (d->flags & MXFP4_MOE_A8) != 0;
   s->ordered = (d->flags & MXFP4_MOE_DETERMINISTIC) != 0;
   // element counts that the kernels index with int64 and int32
   int64_t tmp;
@@ -121,7 +127,8 @@ GemmPlan choose_plan(const Shape& s) {
   // MXFP4_MOE_PLAN=16|64|128 (benchmarks only) forces the token-tile height
   int forced = 0;
   if (const char* env = getenv("MXFP4_MOE_PLAN")) forced = atoi(env);
-  const bool lds64 = forced == 64 || (forced == 0 && s.S <= kRowsPerExpert64 * s.Eg);
+  // (the 64-row kernels have no MXFP8 activations: A8 takes the 128-row tiles)
+  const bool lds64 = !s.a8 && (forced == 64 || (forced == 0 && s.S <= kRowsPerExpert64 * s.Eg));
   if (ksplit_ok && (forced == 16 || (forced == 0 && s.S <= kRowsPerExpert16 * s.Eg))) {
     p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
   } else if (lds64) {
@@ -177,10 +184,10 @@ Layout layout_of(const Shape& s) {
   L.act = take(S * (size_t)s.I * 2);
   L.out32 = s.ordered ? 0 : take((size_t)s.T * (size_t)s.H * 4);
   L.ybuf = s.ordered ? take(S * (size_t)s.H * 4) : 0;
-  if (s.a4) {
-    L.xq = take((size_t)s.T * (size_t)s.H / 2);
+  if (s.mx()) {
+    L.xq = take((size_t)s.T * (size_t)s.H / (size_t)s.qdiv());
     L.xs = take((size_t)s.T * (size_t)s.H / 32);
-    L.actq = take(S * (size_t)s.I / 2);
+    L.actq = take(S * (size_t)s.I / (size_t)s.qdiv());
     L.acts = take(S * (size_t)s.I / 32);
   } else {
     L.xq = L.xs = L.actq = L.acts = 0;
@@ -290,7 +297,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   hipError_t e = fused_route ? hipSuccess : launch_route(r, stream);
   if (e != hipSuccess) return hip_fail(e);
 
-  if (s.a4) {
+  if (s.mx()) {
     QuantArgs q;
     q.in = x;
     q.in_dtype = 0;
@@ -299,6 +306,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     q.in_row_stride = s.H;
     q.codes = at<uint8_t>(ws, L.xq);
     q.scales = at<uint8_t>(ws, L.xs);
+    q.fp8 = s.a8 ? 1 : 0;
     e = launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -319,8 +327,8 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   // gate_up
   g.a_bf16 = reinterpret_cast<const uint16_t*>(x);
   g.a_rows = s.T;
-  g.a_codes = s.a4 ? at<uint8_t>(ws, L.xq) : nullptr;
-  g.a_scales = s.a4 ? at<uint8_t>(ws, L.xs) : nullptr;
+  g.a_codes = s.mx() ? at<uint8_t>(ws, L.xq) : nullptr;
+  g.a_scales = s.mx() ? at<uint8_t>(ws, L.xs) : nullptr;
   g.w_codes = w13;
   g.w_scales = w13s;
   g.tile_off = r.tile_off1;
@@ -330,12 +338,12 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.act = at<uint16_t>(ws, L.act);
   g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.zero_n = s.ordered ? 0 : s.T * s.H;
-  e = plan.ms == 1   ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.a4, stream)
-      : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.a4, stream)
+  e = plan.ms == 1   ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.af(), stream)
+      : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
 
-  if (s.a4) {
+  if (s.mx()) {
     QuantArgs q;
     q.in = at<uint16_t>(ws, L.act);
     q.in_dtype = 0;
@@ -344,6 +352,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     q.in_row_stride = s.I;
     q.codes = at<uint8_t>(ws, L.actq);
     q.scales = at<uint8_t>(ws, L.acts);
+    q.fp8 = s.a8 ? 1 : 0;
     e = launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -352,8 +361,8 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   // down + combine
   g.a_bf16 = at<uint16_t>(ws, L.act);
   g.a_rows = s.S;
-  g.a_codes = s.a4 ? at<uint8_t>(ws, L.actq) : nullptr;
-  g.a_scales = s.a4 ? at<uint8_t>(ws, L.acts) : nullptr;
+  g.a_codes = s.mx() ? at<uint8_t>(ws, L.actq) : nullptr;
+  g.a_scales = s.mx() ? at<uint8_t>(ws, L.acts) : nullptr;
   g.w_codes = w2;
   g.w_scales = w2s;
   g.tile_off = r.tile_off2;
@@ -364,8 +373,8 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.zero_n = 0;
   g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
-  e = plan.ms == 1   ? launch_down_ksplit(g, max_tiles(s, mt), s.a4, s.ordered, stream)
-      : plan.ms == 8 ? launch_down_tile(g, max_tiles(s, mt), s.a4, s.ordered, stream)
+  e = plan.ms == 1   ? launch_down_ksplit(g, max_tiles(s, mt), s.af(), s.ordered, stream)
+      : plan.ms == 8 ? launch_down_tile(g, max_tiles(s, mt), s.af(), s.ordered, stream)
                      : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
   if ((e = mark(3)) != hipSuccess) return hip_fail(e);
@@ -529,17 +538,19 @@ int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float*
                               workspace_bytes, &s, &L);
   if (st) return st;
   if (!act) return MXFP4_MOE_ERR_NULL_POINTER;
-  if (s.a4 && (!actq || !acts || !xq || !xs)) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (s.mx() && (!actq || !acts || !xq || !xs)) return MXFP4_MOE_ERR_NULL_POINTER;
   st = check_device();
   if (st) return st;
   if (!aligned(out32, 16)) return MXFP4_MOE_ERR_MISALIGNED;
   st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream, out32);
   if (st) return st;
   hipError_t e = launch_copy_rows(at<uint8_t>(workspace, L.act), act, s.S * s.I * 2, stream);
-  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.actq), actq, s.S * s.I / 2, stream);
-  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.acts), acts, s.S * s.I / 32, stream);
-  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.xq), xq, s.T * s.H / 2, stream);
-  if (e == hipSuccess && s.a4) e = launch_copy_rows(at<uint8_t>(workspace, L.xs), xs, s.T * s.H / 32, stream);
+  if (e == hipSuccess && s.mx())
+    e = launch_copy_rows(at<uint8_t>(workspace, L.actq), actq, s.S * s.I / s.qdiv(), stream);
+  if (e == hipSuccess && s.mx()) e = launch_copy_rows(at<uint8_t>(workspace, L.acts), acts, s.S * s.I / 32, stream);
+  if (e == hipSuccess && s.mx())
+    e = launch_copy_rows(at<uint8_t>(workspace, L.xq), xq, s.T * s.H / s.qdiv(), stream);
+  if (e == hipSuccess && s.mx()) e = launch_copy_rows(at<uint8_t>(workspace, L.xs), xs, s.T * s.H / 32, stream);
   if (e != hipSuccess) return hip_fail(e);
   return MXFP4_MOE_OK;
 }
@@ -573,8 +584,8 @@ int mxfp4_moe_route(const mxfp4_moe_dims* d, const float* router_logits, int32_t
   return MXFP4_MOE_OK;
 }
 
-int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
-                       uint8_t* scales, hipStream_t stream) {
+static int quantize_rows(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                         uint8_t* scales, int fp8, hipStream_t stream) {
   if (in_dtype != MXFP4_MOE_DTYPE_BF16 && in_dtype != MXFP4_MOE_DTYPE_F32) return MXFP4_MOE_ERR_BAD_ARGUMENT;
   if (rows < 0 || K < 0) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
   if (K == 0) return MXFP4_MOE_ERR_EMPTY_SHAPE;
@@ -594,9 +605,20 @@ int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K
   q.in_row_stride = K;
   q.codes = codes;
   q.scales = scales;
+  q.fp8 = fp8;
   hipError_t e = launch_quantize(q, stream);
   if (e != hipSuccess) return hip_fail(e);
   return MXFP4_MOE_OK;
+}
+
+int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales, hipStream_t stream) {
+  return quantize_rows(in, in_dtype, rows, K, codes, scales, 0, stream);
+}
+
+int mxfp4_moe_quantize8(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
+                        uint8_t* scales, hipStream_t stream) {
+  return quantize_rows(in, in_dtype, rows, K, codes, scales, 1, stream);
 }
 
 }  // extern "C"

@@ -158,6 +158,65 @@ __device__ __forceinline__ void mx_quantize_block32(const float* v, uint32_t* pa
   *scale_out = s;
 }
 
+// ---- MXFP8 (E4M3 elements: bias 7, 3 mantissa bits, largest 448, 0x7F NaN)
+
+// E4M3 magnitude code of a >= 0 (already divided by the block scale): round to
+// nearest, ties to the even code, saturating at 448 (code 0x7E).  Below 2^-6
+// the grid step is 2^-9 (subnormals: code = a * 512 rounded); above, rounding
+// the fp32 significand to 3 bits (nearest, ties to even, a carry moves into
+// the exponent) and rebiasing the exponent from 127 to 7 gives the code.
+__device__ __forceinline__ uint32_t e4m3_magnitude_code(float a) {
+  if (a >= 448.0f) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;  // exponent field << 3 | 3 mantissa bits
+  const uint32_t code = r - (120u << 3);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// MXFP8 scale byte: floor(log2 amax) - 8 + 127 = exponent field - 8, clamped to
+// [0, 254] (8 is the largest E4M3 exponent).
+__device__ __forceinline__ uint32_t mx8_scale_from_amax_bits(uint32_t amax_bits) {
+  int s = (int)(amax_bits >> 23) - 8;
+  s = s < 0 ? 0 : s;
+  s = s > 254 ? 254 : s;
+  return (uint32_t)s;
+}
+
+// Quantise 32 fp32 values (one MX block) to 32 E4M3 code bytes + a scale byte.
+__device__ __forceinline__ void mx8_quantize_block32(const float* v, uint32_t* codes8,
+                                                     uint32_t* scale_out) {
+  uint32_t amax_bits = 0;
+  bool nonfinite = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t b = __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu;
+    nonfinite |= (b >= 0x7F800000u);
+    amax_bits = b > amax_bits ? b : amax_bits;
+  }
+  if (nonfinite) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) codes8[w] = 0;
+    *scale_out = 255;
+    return;
+  }
+  uint32_t s = mx8_scale_from_amax_bits(amax_bits);
+  float inv = mx_inv_scale(s);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = v[w * 4 + i];
+      uint32_t sign = __builtin_bit_cast(uint32_t, x) >> 31;
+      float a = __builtin_fabsf(x) * inv;
+      word |= ((sign << 7) | e4m3_magnitude_code(a)) << (8 * i);
+    }
+    codes8[w] = word;
+  }
+  *scale_out = s;
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Streaming loads of weight data, read once per step: the non-temporal hint

@@ -52,17 +52,26 @@ struct WSlice {
   uint32_t sd[NG][2];
 };
 
+// Activation formats: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 with E4M3 elements (A8).
+constexpr int kActBf16 = 0, kActFp4 = 1, kActFp8 = 2;
+
 // Activation operands of one wave's K range: bf16 (4 MFMA operands per
-// k-tile) or, A4, one packed block and its scale byte per k-tile.
-template <int KPW, bool A4>
+// k-tile), or per lane and k-tile 32 MX elements -- 16 bytes of packed E2M1 or
+// 32 bytes of E4M3 -- and one scale byte.
+template <int KPW, int AF>
 struct ASlice;
 template <int KPW>
-struct ASlice<KPW, false> {
+struct ASlice<KPW, kActBf16> {
   u32x4_t av[KPW][4];
 };
 template <int KPW>
-struct ASlice<KPW, true> {
+struct ASlice<KPW, kActFp4> {
   u32x4_t av[KPW];
+  uint32_t as[KPW];
+};
+template <int KPW>
+struct ASlice<KPW, kActFp8> {
+  u32x4_t av[KPW][2];
   uint32_t as[KPW];
 };
 
@@ -114,7 +123,7 @@ __device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, __amdgpu_buffer_
 // need no select (a select would force a wait right after the load), and only
 // valid rows generate traffic.
 template <int KPW>
-__device__ __forceinline__ void load_aslice(ASlice<KPW, false>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
+__device__ __forceinline__ void load_aslice(ASlice<KPW, kActBf16>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
                                             uint32_t oob, __amdgpu_buffer_rsrc_t, uint32_t, uint32_t, int kt0,
                                             int KT) {
   const int g = lane_id() >> 4;
@@ -127,7 +136,7 @@ __device__ __forceinline__ void load_aslice(ASlice<KPW, false>& t, __amdgpu_buff
     }
 }
 template <int KPW>
-__device__ __forceinline__ void load_aslice(ASlice<KPW, true>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
+__device__ __forceinline__ void load_aslice(ASlice<KPW, kActFp4>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
                                             uint32_t oob, __amdgpu_buffer_rsrc_t rss, uint32_t soff0,
                                             uint32_t soob, int kt0, int KT) {
   const int g = lane_id() >> 4;
@@ -140,6 +149,27 @@ __device__ __forceinline__ void load_aslice(ASlice<KPW, true>& t, __amdgpu_buffe
     t.as[c] = __builtin_amdgcn_raw_buffer_load_b8(rss, soff, 0, 0);
   }
 }
+// MXFP8 row: one byte per element.  With 8-bit A elements the scaled MFMA
+// takes K elements 16 g .. 16 g + 15 of the k-tile from lane group g's first
+// four registers and 64 + 16 g .. 64 + 16 g + 15 from its last four, while the
+// scale byte of 32-element block b is still read from lane group b (layout
+// measured on gfx950 with one-hot operands).  So lane group g loads the two
+// 16-byte pieces at 128 kt + 16 g and 128 kt + 64 + 16 g, and block g's scale.
+template <int KPW>
+__device__ __forceinline__ void load_aslice(ASlice<KPW, kActFp8>& t, __amdgpu_buffer_rsrc_t rs, uint32_t off0,
+                                            uint32_t oob, __amdgpu_buffer_rsrc_t rss, uint32_t soff0,
+                                            uint32_t soob, int kt0, int KT) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int c = 0; c < KPW; ++c) {
+    const bool kin = kt0 + c < KT;
+    const uint32_t off = kin ? off0 + (uint32_t)(kt0 + c) * 128u + (uint32_t)g * 16u : oob;
+    const uint32_t soff = kin ? soff0 + (uint32_t)(4 * (kt0 + c) + g) : soob;
+    t.av[c][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    t.av[c][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64u, 0, 0));
+    t.as[c] = __builtin_amdgcn_raw_buffer_load_b8(rss, soff, 0, 0);
+  }
+}
 
 // acc[g] += A(16 rows x this wave's K range) * W(row group g)^T, k-tile by
 // k-tile, and as each k-tile's registers are consumed, refill(c) loads the
@@ -149,7 +179,7 @@ __device__ __forceinline__ void load_aslice(ASlice<KPW, true>& t, __amdgpu_buffe
 // Slots past K contribute zero through both operands; FULL (every wave's
 // k-tiles inside K) drops the zeroing selects.
 template <bool FULL, int NG, int KPW, typename Refill>
-__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, false>& at, int kt0, int KT,
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, kActBf16>& at, int kt0, int KT,
                                                f32x4_t (&acc)[NG], Refill&& refill) {
   float sc[KPW][NG];
 #pragma unroll
@@ -177,8 +207,10 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-template <bool FULL, int NG, int KPW, typename Refill>
-__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, true>& at, int kt0, int KT,
+// MX activations (AF = A4 or A8): the scaled MFMA takes the raw blocks and
+// both scale bytes; A's format code is FP4 (4) or FP8 E4M3 (0), W's FP4.
+template <bool FULL, int NG, int KPW, int AF, typename Refill>
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, AF>& at, int kt0, int KT,
                                                f32x4_t (&acc)[NG], Refill&& refill) {
   uint32_t sbyte[KPW][NG];
 #pragma unroll
@@ -198,12 +230,17 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
     const bool kin = FULL || kt0 + c < KT;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const i32x8_t A = {(int)at.av[c][0], (int)at.av[c][1], (int)at.av[c][2], (int)at.av[c][3], 0, 0, 0, 0};
+      i32x8_t A;
+      if constexpr (AF == kActFp8)
+        A = (i32x8_t){(int)at.av[c][0][0], (int)at.av[c][0][1], (int)at.av[c][0][2], (int)at.av[c][0][3],
+                      (int)at.av[c][1][0], (int)at.av[c][1][1], (int)at.av[c][1][2], (int)at.av[c][1][3]};
+      else
+        A = (i32x8_t){(int)at.av[c][0], (int)at.av[c][1], (int)at.av[c][2], (int)at.av[c][3], 0, 0, 0, 0};
       u32x4_t wb = wt.w[c][gi];
       if constexpr (!FULL) wb = kin ? wb : (u32x4_t){0u, 0u, 0u, 0u};
       const i32x8_t B = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], 0, 0, 0, 0};
-      acc[gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[gi], 4, 4, 0, (int)at.as[c], 0,
-                                                                 (int)sbyte[c][gi]);
+      acc[gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[gi], AF == kActFp8 ? 0 : 4, 4, 0,
+                                                                 (int)at.as[c], 0, (int)sbyte[c][gi]);
     }
     refill(c);
     __builtin_amdgcn_sched_barrier(0);
@@ -276,7 +313,7 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, in
 // ROUTE: every workgroup first routes the tokens itself (route_block, tables in
 // LDS after the partial buffers; workgroup 0 also writes the global tables that
 // the down and combine kernels read), so no routing kernel runs before this one.
-template <int KPW, int D, bool A4, bool FULL, bool ROUTE>
+template <int KPW, int D, int AF, bool FULL, bool ROUTE>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteArgs ra) {
   extern __shared__ float red[];  // [2][waves][2][64][4], then (ROUTE) the routing tables
   if (a.zero_buf) {
@@ -348,10 +385,11 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     else
       tok_raw = a.tile_tok[(int64_t)t * 16 + r];
     const int64_t tok = valid ? tok_raw : 0;
-    ASlice<KPW, A4> at;
-    if constexpr (A4) {
-      const uint32_t nb = (uint32_t)(a.a_rows * (H / 2)), ns = (uint32_t)(a.a_rows * (H / 32));
-      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * (H / 2)) : nb, nb,
+    ASlice<KPW, AF> at;
+    if constexpr (AF != kActBf16) {
+      const int64_t rb = AF == kActFp8 ? H : H / 2;  // code bytes per row
+      const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (H / 32));
+      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * rb) : nb, nb,
                   make_rsrc(a.a_scales, ns), valid ? (uint32_t)(tok * (H / 32)) : ns, ns, kt0, KT);
     } else {
       const uint32_t nb = (uint32_t)(a.a_rows * H * 2);
@@ -400,7 +438,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
 
 // down + combine: unit = (tile, 16*NG output features).  Atomic combine adds
 // weight * y into out32[token]; ORDERED writes y per sorted position to ybuf.
-template <int KPW, int NG, int D, bool A4, bool ORDERED, bool FULL>
+template <int KPW, int NG, int D, int AF, bool ORDERED, bool FULL>
 __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   extern __shared__ float red[];  // [2][waves][NG][64][4]
   const int lane = lane_id();
@@ -442,10 +480,11 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
     for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
     const bool valid = r < rows;
     const int64_t pr = p0 + r;
-    ASlice<KPW, A4> at;
-    if constexpr (A4) {
-      const uint32_t nb = (uint32_t)(a.a_rows * (I / 2)), ns = (uint32_t)(a.a_rows * (I / 32));
-      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * (I / 2)) : nb, nb,
+    ASlice<KPW, AF> at;
+    if constexpr (AF != kActBf16) {
+      const int64_t rb = AF == kActFp8 ? I : I / 2;  // code bytes per row
+      const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (I / 32));
+      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * rb) : nb, nb,
                   make_rsrc(a.a_scales, ns), valid ? (uint32_t)(pr * (I / 32)) : ns, ns, kt0, KT);
     } else {
       const uint32_t nb = (uint32_t)(a.a_rows * I * 2);
@@ -521,9 +560,10 @@ struct Variant {
   int kpw, d;
 };
 
-Variant pick(int64_t K) {
+Variant pick(int64_t K, bool defaults_only = false) {
   const int64_t KT = K / kTileK;
   Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 1};
+  if (defaults_only) return v;
   if (const char* env = getenv("MXFP4_MOE_DECODE_VARIANT")) {
     int kpw = 0, d = 0;
     if (sscanf(env, "k%dd%d", &kpw, &d) == 2 && (kpw == 2 || kpw == 4) && (d == 1 || d == 2) &&
@@ -610,7 +650,7 @@ hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_unit
   return hipGetLastError();
 }
 
-template <int KPW, int D, bool A4>
+template <int KPW, int D, int AF>
 hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, hipStream_t s) {
   GemmArgs a = a0;
   static const float c_gu = slot_c("MXFP4_MOE_SLOT_C_GU", 0.15f);
@@ -626,15 +666,15 @@ hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, 
     const int64_t bound = (r->E_local < S ? r->E_local : S) + S / 16;
     lds += (size_t)route_block_words(S, r->E_local, bound) * sizeof(int32_t);
     if (lds > kRouteFusedMaxLds) return hipErrorInvalidValue;
-    return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true, true>, nw, lds, mu, s, a, *r)
-                         : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false, true>, nw, lds, mu, s, a, *r);
+    return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, true, true>, nw, lds, mu, s, a, *r)
+                         : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, true>, nw, lds, mu, s, a, *r);
   }
   const RouteArgs none{};
-  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, true, false>, nw, lds, mu, s, a, none)
-                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, A4, false, false>, nw, lds, mu, s, a, none);
+  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, true, false>, nw, lds, mu, s, a, none)
+                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, false>, nw, lds, mu, s, a, none);
 }
 
-template <int KPW, int D, bool A4, bool ORDERED>
+template <int KPW, int D, int AF, bool ORDERED>
 hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
   GemmArgs a = a0;
   static const float c_dn = slot_c("MXFP4_MOE_SLOT_C_DN", 0.10f);
@@ -646,44 +686,56 @@ hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 16 / NG);
   const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
-  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, true>, nw, lds, mu, s, a)
-                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, A4, ORDERED, false>, nw, lds, mu, s, a);
+  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>, nw, lds, mu, s, a)
+                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>, nw, lds, mu, s, a);
 }
 
 template <int KPW, int D>
-hipError_t gate_up_kd(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, bool a4, hipStream_t s) {
-  return a4 ? gate_up_v<KPW, D, true>(a, r, max_tiles, s) : gate_up_v<KPW, D, false>(a, r, max_tiles, s);
+hipError_t gate_up_kd(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, int af, hipStream_t s) {
+  if (af == kActFp8) {
+    if constexpr (KPW >= 4 && D == 1) return gate_up_v<KPW, D, kActFp8>(a, r, max_tiles, s);
+    return hipErrorInvalidValue;
+  }
+  return af == kActFp4 ? gate_up_v<KPW, D, kActFp4>(a, r, max_tiles, s) : gate_up_v<KPW, D, kActBf16>(a, r, max_tiles, s);
 }
 template <int KPW, int D>
-hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
-  if (a4) return ordered ? down_v<KPW, D, true, true>(a, max_tiles, s) : down_v<KPW, D, true, false>(a, max_tiles, s);
-  return ordered ? down_v<KPW, D, false, true>(a, max_tiles, s) : down_v<KPW, D, false, false>(a, max_tiles, s);
+hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
+  if (af == kActFp8) {
+    // A8 comes only in the default variants (KPW 4, 5 or 8 with one unit ahead)
+    if constexpr (KPW >= 4 && D == 1)
+      return ordered ? down_v<KPW, D, kActFp8, true>(a, max_tiles, s)
+                     : down_v<KPW, D, kActFp8, false>(a, max_tiles, s);
+    return hipErrorInvalidValue;
+  }
+  if (af == kActFp4)
+    return ordered ? down_v<KPW, D, kActFp4, true>(a, max_tiles, s) : down_v<KPW, D, kActFp4, false>(a, max_tiles, s);
+  return ordered ? down_v<KPW, D, kActBf16, true>(a, max_tiles, s) : down_v<KPW, D, kActBf16, false>(a, max_tiles, s);
 }
 }  // namespace
 
 #define MXMOE_DECODE_VARIANTS(F) F(2, 1) F(2, 2) F(4, 1) F(4, 2)
 
-hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, bool a4,
+hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, int af,
                                  hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const Variant v = pick(a.K);
+  const Variant v = pick(a.K, af == kActFp8);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return gate_up_kd<KPW, D>(a, route, max_tiles, a4, s);
+  if (v.kpw == KPW && v.d == D) return gate_up_kd<KPW, D>(a, route, max_tiles, af, s);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return gate_up_kd<5, 1>(a, route, max_tiles, a4, s);
-  return gate_up_kd<8, 1>(a, route, max_tiles, a4, s);
+  if (v.kpw == 5) return gate_up_kd<5, 1>(a, route, max_tiles, af, s);
+  return gate_up_kd<8, 1>(a, route, max_tiles, af, s);
 }
 
-hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
+hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const Variant v = pick(a.K);
+  const Variant v = pick(a.K, af == kActFp8);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return down_kd<KPW, D>(a, max_tiles, a4, ordered, s);
+  if (v.kpw == KPW && v.d == D) return down_kd<KPW, D>(a, max_tiles, af, ordered, s);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, a4, ordered, s);
-  return down_kd<8, 1>(a, max_tiles, a4, ordered, s);
+  if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, af, ordered, s);
+  return down_kd<8, 1>(a, max_tiles, af, ordered, s);
 }
 
 }  // namespace mxmoe

@@ -91,8 +91,9 @@ struct QuantArgs {
   int32_t in_dtype;      // 0 bf16, 1 f32
   int64_t rows, K;
   int64_t in_row_stride; // elements
-  uint8_t* codes;        // [rows][K/2]
+  uint8_t* codes;        // [rows][K/2] (MXFP4) or [rows][K] (MXFP8)
   uint8_t* scales;       // [rows][K/32]
+  int32_t fp8;           // 1: E4M3 elements (MXFP8)
 };
 
 struct PreshuffleArgs {
@@ -122,12 +123,13 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, 
                        bool ordered, hipStream_t stream);
 // route non-null: every workgroup routes the tokens itself first (no routing
 // kernel before it); only when route_fusable(*route)
-hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, bool a4,
+// af: activation format, 0 bf16, 1 MXFP4 (A4), 2 MXFP8 (A8)
+hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, int af,
                                  hipStream_t stream);
 // 128-token x 256-weight-row tiles, LDS ring fed by global->LDS copies (tile.hip)
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t stream);
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t stream);
-hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered,
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t stream);
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t stream);
+hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

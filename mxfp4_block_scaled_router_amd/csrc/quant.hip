@@ -10,6 +10,10 @@
 // zero codes.  Codes are packed two per byte, element 2i in the low nibble
 // (campaign page "glm53-mxfp4-mi355x", section "A fused tensor with two dtypes
 // in it": a packed row is half the logical width).
+//
+// With fp8 set the elements are E4M3 instead (MXFP8, one byte each): scale byte
+// = clamp(floor(log2 amax) - 8 + 127, 0, 254), nearest E4M3, ties to the even
+// code, saturating at 448; NaN/inf blocks as above.
 #include "common.h"
 #include "launch.h"
 
@@ -42,10 +46,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
       for (int i = 0; i < 4; ++i) v[q * 4 + i] = w[i];
     }
   }
-  uint32_t packed[4], s;
-  mx_quantize_block32(v, packed, &s);
-  u32x4_t o = {packed[0], packed[1], packed[2], packed[3]};
-  *reinterpret_cast<u32x4_t*>(a.codes + row * (a.K / 2) + blk * 16) = o;
+  uint32_t s;
+  if (a.fp8) {
+    uint32_t c8[8];
+    mx8_quantize_block32(v, c8, &s);
+    u32x4_t* o = reinterpret_cast<u32x4_t*>(a.codes + row * a.K + blk * 32);
+    o[0] = (u32x4_t){c8[0], c8[1], c8[2], c8[3]};
+    o[1] = (u32x4_t){c8[4], c8[5], c8[6], c8[7]};
+  } else {
+    uint32_t packed[4];
+    mx_quantize_block32(v, packed, &s);
+    u32x4_t o = {packed[0], packed[1], packed[2], packed[3]};
+    *reinterpret_cast<u32x4_t*>(a.codes + row * (a.K / 2) + blk * 16) = o;
+  }
   a.scales[row * nblk_row + blk] = (uint8_t)s;
 }
 

@@ -56,13 +56,18 @@ constexpr int kMT = 128;  // token rows per tile
 constexpr int kWaves = 8;  // 2 (rows) x 4 (weight row groups)
 constexpr int kThreads = 64 * kWaves;
 
-template <bool AFP4, int NRG_>
+// Activation formats: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 with E4M3 elements (A8).
+constexpr int kActBf16 = 0, kActFp4 = 1, kActFp8 = 2;
+// bytes of one activation row per k-tile (128 elements)
+constexpr int act_row_bytes(int af) { return af == kActFp4 ? 64 : af == kActFp8 ? 128 : 256; }
+
+template <int AF, int NRG_>
 struct Cfg {
   static constexpr int NRG = NRG_;                              // weight row groups per tile
   static constexpr int NT = 16 * NRG;
   static constexpr int WN = NRG / 4;                            // row groups per wave
-  static constexpr int A_BYTES = AFP4 ? kMT * 64 : kMT * 256;  // activation k-tile
-  static constexpr int AS_BYTES = AFP4 ? kMT * 4 : 0;           // activation scale bytes
+  static constexpr int A_BYTES = kMT * act_row_bytes(AF);       // activation k-tile
+  static constexpr int AS_BYTES = AF != kActBf16 ? kMT * 4 : 0; // activation scale bytes
   static constexpr int B_BYTES = NRG * 1024;                    // weight codes
   static constexpr int A_OFF = 0, AS_OFF = A_BYTES, B_OFF = A_BYTES + AS_BYTES;
   static constexpr int STAGE = B_OFF + B_BYTES;
@@ -70,7 +75,7 @@ struct Cfg {
   static constexpr int STAGES_FIT = (160 * 1024 - ROWS_BYTES) / STAGE;
   static constexpr int STAGES = STAGES_FIT > 4 ? 4 : STAGES_FIT;
   static constexpr int A_CP = A_BYTES / 1024 / kWaves;  // copies per wave per k-tile
-  static constexpr int AS_CP = AFP4 ? 1 : 0;            // 2 copies, made by even and odd waves alike
+  static constexpr int AS_CP = AF != kActBf16 ? 1 : 0;  // 2 copies, made by even and odd waves alike
   static constexpr int B_CP = NRG / kWaves;
   static constexpr int CP = A_CP + AS_CP + B_CP;
   static constexpr int SCP = WN / 4;                    // scale dword loads per wave per k-tile
@@ -147,10 +152,10 @@ __device__ __forceinline__ void zero_duty(const GemmArgs& a) {
 
 // The k-loop: acc[rb][cb] += A(rows 64 wm + 16 rb ..) * W(row group WN wn + cb)^T
 // over all of K.  rowidx (LDS): the A-matrix row of each tile row.
-template <bool AFP4, int NRG>
+template <int AF, int NRG>
 __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
                                               uint8_t* lds, f32x4_t (&acc)[4][NRG / 4]) {
-  using C = Cfg<AFP4, NRG>;
+  using C = Cfg<AF, NRG>;
   constexpr int WN = C::WN;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,7 +166,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
   // ---- per-lane copy sources (k-tile 0); k-tile kt adds kt * stride
   const uint8_t* a_src[C::A_CP];
   const uint8_t* as_src = nullptr;
-  if constexpr (!AFP4) {
+  if constexpr (AF == kActBf16) {
     const int64_t rb = K * 2;  // bytes per activation row
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
@@ -170,6 +175,19 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
       const int c = (lane & 15) ^ (row & 15);
       a_src[jj] = reinterpret_cast<const uint8_t*>(a.a_bf16) + (int64_t)rowidx[row] * rb + c * 16;
     }
+  } else if constexpr (AF == kActFp8) {
+    // 128-byte rows: copy j fills rows 8j .. 8j+7, lane i row 8j + i/8 at chunk
+    // i % 8, which holds the row's logical chunk (i % 8) ^ ((row >> 1) & 7)
+    const int64_t rb = K;
+#pragma unroll
+    for (int jj = 0; jj < C::A_CP; ++jj) {
+      const int j = wave * C::A_CP + jj;
+      const int row = 8 * j + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
+    }
+    const int row = 64 * (wave & 1) + lane;
+    as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);
   } else {
     const int64_t rb = K / 2;
 #pragma unroll
@@ -205,9 +223,9 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
       const int j = wave * C::A_CP + jj;
-      copy16(a_src[jj] + (int64_t)kt * (AFP4 ? 64 : 256), slot + C::A_OFF + j * 1024);
+      copy16(a_src[jj] + (int64_t)kt * act_row_bytes(AF), slot + C::A_OFF + j * 1024);
     }
-    if constexpr (AFP4) copy4(as_src + (int64_t)kt * 4, slot + C::AS_OFF + (wave & 1) * 256);
+    if constexpr (AF != kActBf16) copy4(as_src + (int64_t)kt * 4, slot + C::AS_OFF + (wave & 1) * 256);
 #pragma unroll
     for (int jj = 0; jj < C::B_CP; ++jj) {
       const int q = wave * C::B_CP + jj;
@@ -230,7 +248,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
       bw[cb] = *reinterpret_cast<const u32x4_t*>(slot + C::B_OFF + (wn * WN + cb) * 1024 + lane * 16);
       sbyte[cb] = (scur[cb] >> (8 * (kt & 3))) & 0xFFu;
     }
-    if constexpr (!AFP4) {
+    if constexpr (AF == kActBf16) {
       float sc[WN];
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) sc[cb] = e8m0_scale_operand(sbyte[cb]);
@@ -258,9 +276,22 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int row = wm * 64 + rb * 16 + (lane & 15);
-        const int phys = g ^ ((row >> 2) & 3);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 64 + phys * 16);
-        A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        if constexpr (AF == kActFp8) {
+          // 8-bit A elements: lane group g supplies K 16 g .. 16 g + 15 and
+          // 64 + 16 g .. 64 + 16 g + 15 (logical chunks g and 4 + g), with the
+          // scale of block g as for E2M1 (the MFMA reads block b's scale from
+          // lane group b)
+          const int sw = (row >> 1) & 7;
+          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 128 + (g ^ sw) * 16);
+          const u32x4_t v1 =
+              *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 128 + ((4 + g) ^ sw) * 16);
+          A[rb] = (i32x8_t){(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                            (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+        } else {
+          const int phys = g ^ ((row >> 2) & 3);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 64 + phys * 16);
+          A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        }
         as[rb] = slot[C::AS_OFF + row * 4 + g];
       }
 #pragma unroll
@@ -268,8 +299,8 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
         const i32x8_t B = {(int)bw[cb][0], (int)bw[cb][1], (int)bw[cb][2], (int)bw[cb][3], 0, 0, 0, 0};
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rb], B, acc[rb][cb], 4, 4, 0,
-                                                                         (int)as[rb], 0, (int)sbyte[cb]);
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              A[rb], B, acc[rb][cb], AF == kActFp8 ? 0 : 4, 4, 0, (int)as[rb], 0, (int)sbyte[cb]);
       }
     }
   };
@@ -324,10 +355,10 @@ int tile_nrg() {
 }  // namespace
 
 // gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
-template <bool AFP4, int NRG>
+template <int AF, int NRG>
 __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AFP4, NRG>;
+  using C = Cfg<AF, NRG>;
   constexpr int WN = C::WN;
   zero_duty(a);
   const int64_t H = a.K, I = a.N / 2;
@@ -343,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AFP4, NRG>(a, it, H, a.N, lds, acc);
+  tile_mainloop<AF, NRG>(a, it, H, a.N, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -370,10 +401,10 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
 }
 
 // down + combine.
-template <bool AFP4, bool ORDERED, int NRG>
+template <int AF, bool ORDERED, int NRG>
 __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AFP4, NRG>;
+  using C = Cfg<AF, NRG>;
   constexpr int WN = C::WN;
   const int64_t I = a.K, H = a.N;
   const int ntl = (int)((a.N + C::NT - 1) / C::NT);
@@ -388,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AFP4, NRG>(a, it, I, H, lds, acc);
+  tile_mainloop<AF, NRG>(a, it, I, H, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -442,33 +473,41 @@ hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a
   return hipGetLastError();
 }
 
-template <int NRG>
-hipError_t gate_up_nrg(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+template <int AF, int NRG>
+hipError_t gate_up_af(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
-  return a4 ? launch_lds(tile_gate_up_kernel<true, NRG>, grid, Cfg<true, NRG>::LDS, a, s)
-            : launch_lds(tile_gate_up_kernel<false, NRG>, grid, Cfg<false, NRG>::LDS, a, s);
+  return launch_lds(tile_gate_up_kernel<AF, NRG>, grid, Cfg<AF, NRG>::LDS, a, s);
+}
+template <int AF, int NRG>
+hipError_t down_af(const GemmArgs& a, int64_t max_tiles, bool ordered, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
+  return ordered ? launch_lds(tile_down_kernel<AF, true, NRG>, grid, Cfg<AF, NRG>::LDS, a, s)
+                 : launch_lds(tile_down_kernel<AF, false, NRG>, grid, Cfg<AF, NRG>::LDS, a, s);
 }
 
 template <int NRG>
-hipError_t down_nrg(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
-  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
-  if (a4)
-    return ordered ? launch_lds(tile_down_kernel<true, true, NRG>, grid, Cfg<true, NRG>::LDS, a, s)
-                   : launch_lds(tile_down_kernel<true, false, NRG>, grid, Cfg<true, NRG>::LDS, a, s);
-  return ordered ? launch_lds(tile_down_kernel<false, true, NRG>, grid, Cfg<false, NRG>::LDS, a, s)
-                 : launch_lds(tile_down_kernel<false, false, NRG>, grid, Cfg<false, NRG>::LDS, a, s);
+hipError_t gate_up_nrg(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t s) {
+  if (af == kActFp8) return gate_up_af<kActFp8, NRG>(a, max_tiles, s);
+  return af == kActFp4 ? gate_up_af<kActFp4, NRG>(a, max_tiles, s) : gate_up_af<kActBf16, NRG>(a, max_tiles, s);
+}
+
+template <int NRG>
+hipError_t down_nrg(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
+  if (af == kActFp8) return down_af<kActFp8, NRG>(a, max_tiles, ordered, s);
+  return af == kActFp4 ? down_af<kActFp4, NRG>(a, max_tiles, ordered, s)
+                       : down_af<kActBf16, NRG>(a, max_tiles, ordered, s);
 }
 }  // namespace
 
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, bool a4, hipStream_t s) {
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  return tile_nrg() == 16 ? gate_up_nrg<16>(a, max_tiles, a4, s) : gate_up_nrg<32>(a, max_tiles, a4, s);
+  return tile_nrg() == 16 ? gate_up_nrg<16>(a, max_tiles, af, s) : gate_up_nrg<32>(a, max_tiles, af, s);
 }
 
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, bool a4, bool ordered, hipStream_t s) {
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  return tile_nrg() == 16 ? down_nrg<16>(a, max_tiles, a4, ordered, s)
-                          : down_nrg<32>(a, max_tiles, a4, ordered, s);
+  return tile_nrg() == 16 ? down_nrg<16>(a, max_tiles, af, ordered, s)
+                          : down_nrg<32>(a, max_tiles, af, ordered, s);
 }
 
 }  // namespace mxmoe

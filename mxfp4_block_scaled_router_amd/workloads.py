@@ -23,6 +23,7 @@ Workloads (shapes and value distributions of the layer's five configurations):
   a4       T=4096 H=4096 I=1536 E=128/128 k=8  x~N(0,1); weights are Student-t(3)
            values times (3K)^-1/2 in fp32 (K = H for w13, K = I for w2), handed over
            unquantised: each side applies its own MXFP4 quantiser
+  a8       as a4 with the activations quantised to MXFP8 (E4M3) instead of MXFP4
   verify_bB  T=6B (B = 1, 8, 16, 32, 48) with decode's dims and distributions:
            speculative verification of 5 draft tokens + 1 per sequence
 
@@ -58,6 +59,7 @@ class Workload:
     logits_kind: str = "normal"     # "normal" | "zipf_bias"
     weight_kind: str = "uniform"    # "uniform" | "student_t"
     a4: bool = False
+    a8: bool = False
     seed: int = 1000
 
     def replace(self, **kw) -> "Workload":
@@ -81,6 +83,8 @@ WORKLOADS = {
     "a4": Workload("a4", 4096, 4096, 1536, 128, 128, 0, 8, weight_kind="student_t", a4=True,
                    seed=1004),
 }
+# MXFP8 activations (A8) on the a4 workload's shapes and weights
+WORKLOADS["a8"] = WORKLOADS["a4"].replace(name="a8", a4=False, a8=True, seed=1010)
 # Speculative-verify shapes: the decode layer's dims with T = 6 tokens per
 # sequence (5 draft tokens + 1) for batches 1..48.
 for _b, _seed in ((1, 1005), (8, 1006), (16, 1007), (32, 1008), (48, 1009)):

@@ -46,6 +46,7 @@ class Case:
                  deterministic: bool = False, shared: bool = False):
         self.wl = wl
         self.a4 = wl.a4 if a4 is None else a4
+        self.a8 = wl.a8
         self.deterministic = deterministic
         self.shared = shared
         if inp is not None:
@@ -60,7 +61,8 @@ class Case:
         if "w13" not in self.inp:
             self._quantise_student_t()
         self.dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local,
-                                 a4=self.a4, deterministic=deterministic, shared=shared)
+                                 a4=self.a4, deterministic=deterministic, shared=shared,
+                                 a8=self.a8)
         self.x = bf16_dev(self.inp["x"])
         self.logits = to_dev(self.inp["logits"])
         canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
@@ -110,8 +112,10 @@ class Case:
                                   self.inp["w13s"], self.inp["w2"], self.inp["w2s"],
                                   top_k=wl.top_k, clamp_limit=wl.clamp_limit,
                                   E_global=wl.E_global, first_local=wl.first_local, a4=self.a4,
+                                  a8=self.a8,
                                   shared=self.shared, token_mask=token_mask,
-                                  want_act=token_mask is None, actq_in=actq_in, acts_in=acts_in)
+                                  want_act=token_mask is None or self.a4 or self.a8,
+                                  actq_in=actq_in, acts_in=acts_in)
 
 
 def compare_route(g: dict, o) -> None:
@@ -125,14 +129,30 @@ def compare_route(g: dict, o) -> None:
     assert dw <= W_TOL, dw
 
 
-def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray) -> dict:
-    """>= 99.9% bit-equal; every other element within 1 bf16 ulp, or within
+# Smallest fraction of the SwiGLU output that must be bit-equal to the oracle's.
+# With bf16 or E2M1 activations every gate/up product is exact in fp32 and the
+# MFMA sums are correctly rounded fp32 sums in another order, so a bf16 result
+# moves only when an fp32 rounding lands on a bf16 rounding boundary.  With E4M3
+# activations the scaled MFMA's own sum of a 128-long chunk is not exact: on
+# gfx950 it lands up to 2^-15 * sum|products| away from the exact sum (394
+# units of 2^-24 * sum|p| at most over 524,288 random E4M3 x E2M1 chunks, 15%
+# of the chunk sums inexact, errors of either sign; with E2M1 x E2M1 every
+# chunk sum was exact), and about one bf16 SwiGLU output in a few hundred
+# rounds the other way (0.45% on 64 tokens, H = 512, I = 256).
+ACT_EQUAL_MIN = {"bf16": 0.999, "a4": 0.999, "a8": 0.99}
+
+
+def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray, rows=None,
+                min_equal: float = 0.999) -> dict:
+    """>= min_equal bit-equal; every other element within 1 bf16 ulp, or within
     2^-9 * rms(act) absolute where the fp32 gate/up sums cancel (their rounding
     error is bounded by K * 2^-24 * sum|x*w|, not by the size of the result, so a
     near-zero h may move by several bf16 ulps under another summation order).
-    NaN matches NaN."""
+    NaN matches NaN.  ``rows``: the sorted positions compared (default all)."""
     n = o_act_bits.shape[0]
     g = g_act_bits[:n]
+    if rows is not None:
+        g, o_act_bits = g[rows], o_act_bits[rows]
     gf, of = bf16_to_f32(g), bf16_to_f32(o_act_bits)
     both_nan = np.isnan(gf) & np.isnan(of)
     eq = (g == o_act_bits) | both_nan
@@ -149,7 +169,7 @@ def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray) -> dict:
     worst = float(absd[far].max() / rms) if far.any() and rms > 0 else 0.0
     stats = {"act_bit_equal": frac, "act_max_ulp": int(ulp.max()) if ulp.size else 0,
              "act_gt1ulp": int(far.sum()), "act_gt1ulp_max_abs_over_rms": worst}
-    assert eq.size == 0 or frac >= 0.999, stats
+    assert eq.size == 0 or frac >= min_equal, stats
     assert not (np.isnan(gf) ^ np.isnan(of)).any(), stats
     assert worst <= 2.0 ** -9, stats
     return stats

@@ -75,7 +75,8 @@ def ws_status(d, k=2):
     ({}, -1, BAD_TOP_K), ({}, 9, BAD_TOP_K), ({"E_global": 64, "E_local": 64}, 33, BAD_TOP_K),
     ({"T": 1 << 40}, 8, SHAPE_OVERFLOW), ({"T": 1 << 60, "H": 1 << 10}, 2, SHAPE_OVERFLOW),
     ({"first_local": (1 << 63) - 4}, 2, SHAPE_OVERFLOW),
-    ({"flags": 0x8}, 2, BAD_FLAGS),
+    ({"flags": 0x10}, 2, BAD_FLAGS),
+    ({"flags": 0x1 | 0x8}, 2, BAD_FLAGS),     # A4 and A8 exclude each other
 ])
 def test_dims_refusals(lib, kw, k, expect):
     st, _ = ws_status(dims(**kw), k)
@@ -108,6 +109,17 @@ def test_shared_expert_sizes(lib):
     assert st == 0 and sh > base
     d = dims(flags=mx.MXFP4_MOE_SHARED_EXPERT)
     assert mx.mxfp4_moe_plan(d, 2)["tile_rows"] in (16, 64, 128)
+
+
+def test_a8_workspace_holds_byte_codes(lib):
+    """A8 keeps one code byte per element: its workspace exceeds A4's by the
+    x and act code bytes (T*H/2 + T*k*I/2, each region 256-byte aligned)."""
+    _, a4 = ws_status(dims(flags=mx.MXFP4_MOE_A4))
+    st, a8 = ws_status(dims(flags=mx.MXFP4_MOE_A8))
+    assert st == 0
+    T, H, I, k = 16, 512, 256, 2
+    assert a8 - a4 >= T * H // 2 + T * k * I // 2
+    assert mx.mxfp4_moe_plan(dims(flags=mx.MXFP4_MOE_A8), 2)["tile_rows"] in (16, 128)
 
 
 def test_null_dims(lib):
