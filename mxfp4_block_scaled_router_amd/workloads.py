@@ -27,6 +27,12 @@ Workloads (shapes and value distributions of the layer's five configurations):
   verify_bB  T=6B (B = 1, 8, 16, 32, 48) with decode's dims and distributions:
            speculative verification of 5 draft tokens + 1 per sequence
 
+Experts kept in bf16 (per-expert exclusions inside a fused buffer): uniform-code
+workloads draw their bf16 weights from N(0, 0.16^2) (about the rms of their MXFP4
+experts' values), one generator per (expert, matrix); Student-t workloads round
+the expert's own Student-t draw to bf16.  `fuse` lays experts of both kinds back
+to back in one byte buffer, the format a loader has to split per expert.
+
 Every array comes from its own child stream of numpy's SeedSequence(seed), so an
 array does not depend on which other arrays were drawn.  The Student-t weights are
 drawn with torch generators, one per expert, so that any subset of experts can be
@@ -166,3 +172,40 @@ def make_inputs(wl: Workload, weights: bool = True) -> dict:
 def scaled_down(wl: Workload, **kw) -> Workload:
     """The same distributions at other sizes (for tests that must run in seconds)."""
     return wl.replace(**kw)
+
+
+# ---------------------------------------------------------------- bf16 experts
+
+BF16_EXPERT_STD = 0.16
+
+
+def bf16_expert(wl: Workload, expert: int, which: str, device="cpu") -> np.ndarray:
+    """bf16 bits of one expert kept in bf16: [2I, H] for "w13", [H, I] for "w2"."""
+    shape = (2 * wl.I, wl.H) if which == "w13" else (wl.H, wl.I)
+    if wl.weight_kind == "student_t":
+        t = student_t_expert(wl, expert, which, device=device)
+        return t.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    tag = 0 if which == "w13" else 1
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 0xB16, expert, tag])))
+    return bf16_bits_of(g.standard_normal(shape, dtype=np.float32) * np.float32(BF16_EXPERT_STD))
+
+
+def fuse(codes: np.ndarray, scales: np.ndarray, bf16: np.ndarray, excluded) -> tuple:
+    """One fused expert buffer with per-expert dtypes: experts back to back in
+    expert order, packed codes [R, K/2] for a packed expert or bf16 [R, K] (2
+    bytes each) for an excluded one; the scale tensor holds the packed experts'
+    [R, K/32] scale bytes back to back.  codes/scales: [E, R, K/2], [E, R, K/32]
+    (slots of excluded experts unused); bf16: [n, R, K] uint16, the j-th
+    excluded expert in slot j.  Returns (fused uint8 [bytes], scales uint8 [bytes])."""
+    ex = np.asarray(excluded, dtype=bool)
+    parts, sparts, j = [], [], 0
+    for e in range(ex.size):
+        if ex[e]:
+            parts.append(np.ascontiguousarray(bf16[j], dtype=np.uint16).reshape(-1).view(np.uint8))
+            j += 1
+        else:
+            parts.append(np.ascontiguousarray(codes[e], dtype=np.uint8).reshape(-1))
+            sparts.append(np.ascontiguousarray(scales[e], dtype=np.uint8).reshape(-1))
+    assert j == len(bf16)
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.uint8)
+    return cat(parts), cat(sparts)

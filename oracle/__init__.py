@@ -82,7 +82,8 @@ class _Dims(ctypes.Structure):
                 ("first_local", ctypes.c_int64), ("top_k", ctypes.c_int32),
                 ("clamp_limit", ctypes.c_float), ("a4", ctypes.c_int32),
                 ("shared", ctypes.c_int32), ("given_actq", ctypes.c_int32),
-                ("a8", ctypes.c_int32)]
+                ("a8", ctypes.c_int32), ("bf16_expert", ctypes.c_void_p),
+                ("w13_bf16", ctypes.c_void_p), ("w2_bf16", ctypes.c_void_p)]
 
 
 def _ptr(a):
@@ -220,9 +221,45 @@ class OracleResult:
     n_assign: int = 0
 
 
+def unfuse(fused, fused_scales, excluded, R: int, K: int):
+    """Split a fused expert buffer whose experts have their own dtype (campaign
+    page, section "A fused tensor with two dtypes in it": a packed expert's rows
+    are half the logical width in bytes, an excluded bf16 expert keeps the full
+    width, so one stride cannot slice both and the exclusion set has to be
+    carried per expert).  Expert e of the buffer takes R*K/2 bytes of packed
+    E2M1 codes, or R*K*2 bytes of bf16 when excluded, back to back in expert
+    order; the scale tensor holds R*K/32 bytes per packed expert, in order.
+    Returns (codes [E, R, K/2], scales [E, R, K/32], bf16 bits [n, R, K]), the
+    MXFP4 slots of excluded experts zero."""
+    ex = np.asarray(excluded, dtype=bool)
+    fused = np.ascontiguousarray(fused, dtype=np.uint8).reshape(-1)
+    fs = np.ascontiguousarray(fused_scales, dtype=np.uint8).reshape(-1)
+    E = ex.size
+    codes = np.zeros((E, R, K // 2), np.uint8)
+    scales = np.zeros((E, R, K // 32), np.uint8)
+    bf = np.zeros((int(ex.sum()), R, K), np.uint16)
+    off = soff = j = 0
+    for e in range(E):
+        if ex[e]:
+            nb = R * K * 2
+            bf[j] = fused[off:off + nb].view(np.uint16).reshape(R, K)
+            j += 1
+        else:
+            nb = R * K // 2
+            codes[e] = fused[off:off + nb].reshape(R, K // 2)
+            scales[e] = fs[soff:soff + R * K // 32].reshape(R, K // 32)
+            soff += R * K // 32
+        off += nb
+    if off != fused.size or soff != fs.size:
+        raise ValueError("fused buffer is %d bytes (scales %d), the exclusion set needs %d (%d)"
+                         % (fused.size, fs.size, off, soff))
+    return codes, scales, bf
+
+
 def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_global=None,
                 first_local=0, a4=False, shared=False, token_mask=None, want_act=True, nthreads=0,
-                actq_in=None, acts_in=None, a8=False):
+                actq_in=None, acts_in=None, a8=False, bf16_experts=None, w13_bf16=None,
+                w2_bf16=None):
     """The whole layer on canonical-layout inputs (see ``moe_oracle.h``).
 
     ``x_bits``: uint16 bf16 bits [T, H]; ``logits``: float32 [T, E_global];
@@ -238,6 +275,10 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     outputs instead of quantising its own, so a comparison downstream of that
     quantisation starts from the same codes on both sides.
     ``a8``: as ``a4`` with MXFP8 (E4M3) codes, one byte per element.
+    ``bf16_experts`` (bool [E]): experts stored in bf16 instead of MXFP4 (their
+    slots of the MXFP4 arrays are ignored); ``w13_bf16`` uint16 [n, 2I, H] and
+    ``w2_bf16`` uint16 [n, H, I] hold their weights, the j-th excluded expert in
+    slot j.  They compute on bf16 activations in every mode.
     """
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -256,8 +297,17 @@ def moe_forward(x_bits, logits, w13, w13s, w2, w2s, *, top_k, clamp_limit, E_glo
     assert w2.shape == (Ew, H, I // 2) and w2s.shape == (Ew, H, I // 32)
     given = actq_in is not None
     assert given == (acts_in is not None) and (a4 or a8 or not given) and not (a4 and a8)
+    xmask = b13 = b2 = None
+    if bf16_experts is not None:
+        xmask = np.ascontiguousarray(np.asarray(bf16_experts, dtype=bool).astype(np.uint8))
+        assert xmask.shape == (Ew,)
+        n_x = int(xmask.sum())
+        b13 = np.ascontiguousarray(w13_bf16, dtype=np.uint16)
+        b2 = np.ascontiguousarray(w2_bf16, dtype=np.uint16)
+        assert b13.shape == (n_x, 2 * I, H) and b2.shape == (n_x, H, I)
     d = _Dims(T, H, I, Eg, E_local, first_local, top_k, clamp_limit, 1 if a4 else 0, sh,
-              1 if given else 0, 1 if a8 else 0)
+              1 if given else 0, 1 if a8 else 0, None if xmask is None else xmask.ctypes.data,
+              None if b13 is None else b13.ctypes.data, None if b2 is None else b2.ctypes.data)
     k = top_k + sh
     S = T * k
     ids = np.empty((T, k), np.int32)

@@ -26,6 +26,10 @@
  *     set of the census formula (section "A file is a census; a decode step is
  *     a sample").  It enters the combine with weight 1 as one more slot per
  *     token, after the k routed ones.
+ *   - Per-expert exclusions (optional): an expert kept in bf16 inside a fused
+ *     buffer whose other experts are packed MXFP4, so the exclusion set is
+ *     carried per expert (campaign page, section "A fused tensor with two
+ *     dtypes in it").  Such an expert's contractions read its bf16 weights.
  *
  * Activation formats: bf16 (W4A16), or x and the SwiGLU output quantised per 32
  * along K to MXFP4 (A4) or MXFP8 with E4M3 elements (A8) before the contraction
@@ -437,6 +441,14 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       f + El > Eg || kr < 1 || kr > Eg || (d->a4 && d->a8) ||
       (d->given_actq && (!(d->a4 || d->a8) || !actq || !acts)))
     return -2;
+  /* bf16 slot of each excluded expert (j-th excluded in expert order), else -1 */
+  int64_t* xslot = (int64_t*)malloc(sizeof(int64_t) * (size_t)Ew);
+  int64_t n_bf16 = 0;
+  for (int64_t e = 0; e < Ew; ++e) xslot[e] = (d->bf16_expert && d->bf16_expert[e]) ? n_bf16++ : -1;
+  if (n_bf16 > 0 && (!d->w13_bf16 || !d->w2_bf16)) {
+    free(xslot);
+    return -2;
+  }
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -494,6 +506,12 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       for (int64_t i = 0; i < T * H; ++i) xf[i] = orc_f32_from_bf16(x[i]);
     }
   }
+  /* x as bf16 values, for the excluded experts of a quantised-activation layer */
+  float* xb = xf;
+  if (status == 0 && n_bf16 > 0 && (d->a4 || d->a8)) {
+    xb = (float*)malloc(sizeof(float) * nz(T * H));
+    for (int64_t i = 0; i < T * H; ++i) xb[i] = orc_f32_from_bf16(x[i]);
+  }
 
   /* which sorted positions need expert work */
   int64_t* yrow = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N ? N : 1));
@@ -513,24 +531,37 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
     int any = 0;
     for (int64_t p = off_[e]; p < off_[e + 1]; ++p) any |= (yrow[p] >= 0);
     if (!any) continue;
-    const uint8_t* c13 = w13 + e * (2 * I) * (H / 2);
-    const uint8_t* s13 = w13s + e * (2 * I) * (H / 32);
-    const uint8_t* c2 = w2 + e * H * (I / 2);
-    const uint8_t* s2 = w2s + e * H * (I / 32);
+    const int64_t xs_e = xslot[e];   /* >= 0: bf16 weights */
+    const float* xin = xs_e >= 0 ? xb : xf;
+    if (xs_e >= 0) {
+      const uint16_t* b13 = d->w13_bf16 + xs_e * (2 * I) * H;
+      const uint16_t* b2 = d->w2_bf16 + xs_e * H * I;
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < 2 * I; ++n) {
-      float tmp[32];
-      for (int64_t b = 0; b < H / 32; ++b) {
-        orc_dequant(c13 + n * (H / 2) + b * 16, s13 + n * (H / 32) + b, 1, 32, tmp);
-        for (int i = 0; i < 32; ++i) w13t[(b * 32 + i) * (2 * I) + n] = tmp[i];
+      for (int64_t n = 0; n < 2 * I; ++n)
+        for (int64_t kk = 0; kk < H; ++kk) w13t[kk * (2 * I) + n] = orc_f32_from_bf16(b13[n * H + kk]);
+#pragma omp parallel for schedule(static)
+      for (int64_t n = 0; n < H; ++n)
+        for (int64_t i = 0; i < I; ++i) w2t[i * H + n] = orc_f32_from_bf16(b2[n * I + i]);
+    } else {
+      const uint8_t* c13 = w13 + e * (2 * I) * (H / 2);
+      const uint8_t* s13 = w13s + e * (2 * I) * (H / 32);
+      const uint8_t* c2 = w2 + e * H * (I / 2);
+      const uint8_t* s2 = w2s + e * H * (I / 32);
+#pragma omp parallel for schedule(static)
+      for (int64_t n = 0; n < 2 * I; ++n) {
+        float tmp[32];
+        for (int64_t b = 0; b < H / 32; ++b) {
+          orc_dequant(c13 + n * (H / 2) + b * 16, s13 + n * (H / 32) + b, 1, 32, tmp);
+          for (int i = 0; i < 32; ++i) w13t[(b * 32 + i) * (2 * I) + n] = tmp[i];
+        }
       }
-    }
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < H; ++n) {
-      float tmp[32];
-      for (int64_t b = 0; b < I / 32; ++b) {
-        orc_dequant(c2 + n * (I / 2) + b * 16, s2 + n * (I / 32) + b, 1, 32, tmp);
-        for (int i = 0; i < 32; ++i) w2t[(b * 32 + i) * H + n] = tmp[i];
+      for (int64_t n = 0; n < H; ++n) {
+        float tmp[32];
+        for (int64_t b = 0; b < I / 32; ++b) {
+          orc_dequant(c2 + n * (I / 2) + b * 16, s2 + n * (I / 32) + b, 1, 32, tmp);
+          for (int i = 0; i < 32; ++i) w2t[(b * 32 + i) * H + n] = tmp[i];
+        }
       }
     }
 #pragma omp parallel for schedule(dynamic, 1)
@@ -543,7 +574,7 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       /* gate_up: h[n] = sum_k x[k] * W13[n][k], fp32, k ascending */
       for (int64_t n = 0; n < 2 * I; ++n) h[n] = 0.0f;
       for (int64_t kk = 0; kk < H; ++kk) {
-        float xv = xf[t * H + kk];
+        float xv = xin[t * H + kk];
         const float* wr = w13t + kk * (2 * I);
         for (int64_t n = 0; n < 2 * I; ++n) h[n] = h[n] + xv * wr[n];
       }
@@ -551,7 +582,9 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
       for (int64_t i = 0; i < I; ++i) ab[i] = orc_bf16_from_f32(orc_swiglu(h[i], h[I + i], d->clamp_limit));
       if (act)
         for (int64_t i = 0; i < I; ++i) act[p * I + i] = ab[i];
-      if (d->a4 && d->given_actq) {
+      if (xs_e >= 0) {
+        for (int64_t i = 0; i < I; ++i) a[i] = orc_f32_from_bf16(ab[i]);
+      } else if (d->a4 && d->given_actq) {
         orc_dequant(actq + p * (I / 2), acts + p * (I / 32), 1, I, a);
       } else if (d->a8 && d->given_actq) {
         orc_dequant8(actq + p * I, acts + p * (I / 32), 1, I, a);
@@ -614,7 +647,9 @@ int64_t orc_moe_forward(const orc_dims* d, const uint16_t* x, const float* logit
   free(w2t);
   free(y);
   free(yrow);
+  if (xb != xf) free(xb);
   free(xf);
+  free(xslot);
   if (!ids) free(ids_);
   if (!w) free(w_);
   if (!counts) free(cnt_);

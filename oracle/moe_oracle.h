@@ -39,6 +39,16 @@ typedef struct {
                          instead of quantising its own; everything else unchanged */
   int32_t a8; /* 1: as a4 with MXFP8 (E4M3 elements, one byte each): xq [T][H],
                  actq [N][I]; scales as for a4.  a4 and a8 exclude each other */
+  /* Per-expert exclusions (nullable): bf16_expert[e] != 0 marks expert e of the
+   * weight buffers as stored in bf16 instead of MXFP4.  Its weights are then
+   * read from w13_bf16 [n][2I][H] and w2_bf16 [n][H][I] (bf16 bits; slot j is
+   * the j-th excluded expert in expert order) and its slots in w13/w13s/w2/w2s
+   * are ignored.  Such an expert computes on the bf16 x and the bf16 SwiGLU
+   * output in every activation mode (no A4/A8 quantisation; its actq/acts rows
+   * are left untouched). */
+  const uint8_t* bf16_expert;
+  const uint16_t* w13_bf16;
+  const uint16_t* w2_bf16;
 } orc_dims;
 
 /* element and scale decoding */
