@@ -241,6 +241,65 @@ int mxfp4_moe_quantize(const void* in, int32_t in_dtype, int64_t rows, int64_t K
 int mxfp4_moe_quantize8(const void* in, int32_t in_dtype, int64_t rows, int64_t K, uint8_t* codes,
                         uint8_t* scales, hipStream_t stream);
 
+/*
+ * Per-expert bf16 exclusions.  A fused expert buffer may hold packed MXFP4
+ * experts and experts that were excluded from quantisation and kept in bf16;
+ * a packed row is half the logical width in bytes while a bf16 row keeps it,
+ * so one stride cannot slice the buffer and the exclusion set is carried per
+ * expert (campaign page "glm53-mxfp4-mi355x", section "A fused tensor with two
+ * dtypes in it").  E_w = E_local (+ 1 with MXFP4_MOE_SHARED_EXPERT) experts.
+ *
+ * Fused layout of one matrix with R rows and K columns per expert (w13: R = 2I,
+ * K = H; w2: R = H, K = I): experts 0 .. E_w-1 back to back, expert e taking
+ * R*K/2 bytes of canonical packed E2M1 codes ([R][K/2], as for
+ * mxfp4_moe_preshuffle) when packed, or R*K*2 bytes of bf16 ([R][K]) when
+ * excluded.  Its scale tensor holds R*K/32 bytes per packed expert ([R][K/32]),
+ * back to back in expert order; excluded experts have none.
+ */
+typedef struct mxfp4_moe_bf16_experts {
+  int64_t n;                  /* experts kept in bf16, 0 .. E_w (0: none, as mxfp4_moe_forward) */
+  const int32_t* expert_map;  /* device int32 [E_w + n]: entry e = bf16 slot of expert e or -1;
+                                 entry E_w + j = the expert in slot j (as written by
+                                 mxfp4_moe_preshuffle_fused) */
+  const void* w13;            /* device bf16 [n][2I][H], slot j = j-th excluded expert */
+  const void* w2;             /* device bf16 [n][H][I] */
+} mxfp4_moe_bf16_experts;
+
+/*
+ * Loader for a fused buffer with exclusions.  excluded: HOST uint8 [E_w], 1 =
+ * kept in bf16, 0 = packed (other values: BAD_ARGUMENT); E_w <= 544.
+ * Inputs (device, fused layout above): w13_fused, w13s_fused, w2_fused,
+ * w2s_fused (the scale tensors may be NULL when every expert is excluded).
+ * Outputs (device): w13/w13s/w2/w2s preshuffled as by mxfp4_moe_preshuffle
+ * (sizes from mxfp4_moe_preshuffled_bytes; the slots of excluded experts are
+ * left unwritten and never read), w13_bf16 [n][2I][H] and w2_bf16 [n][H][I]
+ * (may be NULL when n = 0), expert_map int32 [E_w + n].  Enqueued on stream,
+ * no host wait.
+ */
+int mxfp4_moe_preshuffle_fused(const mxfp4_moe_dims* d, const uint8_t* excluded,
+                               const uint8_t* w13_fused, const uint8_t* w13s_fused,
+                               const uint8_t* w2_fused, const uint8_t* w2s_fused, uint8_t* w13,
+                               uint8_t* w13s, uint8_t* w2, uint8_t* w2s, void* w13_bf16,
+                               void* w2_bf16, int32_t* expert_map, hipStream_t stream);
+
+/*
+ * The layer with experts kept in bf16 (bx from mxfp4_moe_preshuffle_fused's
+ * outputs; bx itself is host memory, read during the call).  Packed experts
+ * run as in mxfp4_moe_forward; an excluded expert's rows are computed from its
+ * bf16 weights on the bf16 x and the bf16 SwiGLU output in every activation
+ * mode (no A4/A8 quantisation for them).  Workspace as mxfp4_moe_forward.  The
+ * intermediates act, actq, acts, xq, xs and out32 are copied out as by
+ * mxfp4_moe_forward_debug when non-NULL (all may be NULL).  Errors as
+ * mxfp4_moe_forward, plus: bx NULL or, with n > 0, a NULL map or weight ->
+ * NULL_POINTER; n < 0 or n > E_w -> BAD_ARGUMENT.
+ */
+int mxfp4_moe_forward_mixed(const mxfp4_moe_dims* d, const mxfp4_moe_bf16_experts* bx,
+                            const void* x, const float* router_logits, const uint8_t* w13,
+                            const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
+                            int32_t top_k, float clamp_limit, void* out, void* workspace,
+                            size_t workspace_bytes, void* act, uint8_t* actq, uint8_t* acts,
+                            uint8_t* xq, uint8_t* xs, float* out32, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

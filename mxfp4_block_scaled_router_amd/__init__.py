@@ -59,10 +59,17 @@ class Dims(ctypes.Structure):
         return 1 if self.flags & MXFP4_MOE_SHARED_EXPERT else 0
 
 
+class Bf16Experts(ctypes.Structure):
+    """mxfp4_moe_bf16_experts: the experts kept in bf16 (device pointers)."""
+    _fields_ = [("n", ctypes.c_int64), ("expert_map", ctypes.c_void_p), ("w13", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p)]
+
+
 EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_hip_error",
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
             "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
-            "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_quantize8", "mxfp4_moe_plan")
+            "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_quantize8", "mxfp4_moe_plan",
+            "mxfp4_moe_preshuffle_fused", "mxfp4_moe_forward_mixed")
 
 
 def load_library(path: str = LIB_PATH):
@@ -105,6 +112,11 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_quantize.argtypes = [P, I32, I64, I64, P, P, P]
     lib.mxfp4_moe_quantize8.restype = ctypes.c_int
     lib.mxfp4_moe_quantize8.argtypes = [P, I32, I64, I64, P, P, P]
+    lib.mxfp4_moe_preshuffle_fused.restype = ctypes.c_int
+    lib.mxfp4_moe_preshuffle_fused.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.mxfp4_moe_forward_mixed.restype = ctypes.c_int
+    lib.mxfp4_moe_forward_mixed.argtypes = [D, ctypes.POINTER(Bf16Experts), P, P, P, P, P, P, I32,
+                                            ctypes.c_float, P, P, SZ, P, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -314,3 +326,75 @@ def mxfp4_moe_route(dims: Dims, router_logits, top_k: int, workspace=None):
                                 nbytes, _stream()))
     return {"ids": ids, "weights": w, "counts": counts, "offsets": offsets, "sorted": sorted_,
             "inv": inv}
+
+
+# ---------------------------------------------------------------- bf16 exclusions
+
+def mxfp4_moe_preshuffle_fused(dims: Dims, excluded, w13_fused, w13s_fused, w2_fused, w2s_fused):
+    """Fused expert buffers with per-expert dtypes (uint8 device tensors in the
+    layout of include/mxfp4_moe.h) and the host exclusion set (one bool per
+    expert of the buffers) -> (preshuffled (w13, w13s, w2, w2s), bx) where bx is
+    a dict of the bf16 experts: n, expert_map, w13, w2 (device tensors)."""
+    for t, n in ((w13_fused, "w13_fused"), (w2_fused, "w2_fused")):
+        _dev_tensor(t, torch.uint8, n)
+    Ew = dims.E_local + dims.shared
+    flags = [1 if v else 0 for v in excluded]
+    if len(flags) != Ew:
+        raise ValueError("excluded needs %d entries" % Ew)
+    n = sum(flags)
+    host = (ctypes.c_uint8 * Ew)(*flags)
+    dev = w13_fused.device
+    sizes = mxfp4_moe_preshuffled_bytes(dims)
+    outs = [torch.empty(z, dtype=torch.uint8, device=dev) for z in sizes]
+    H, I = dims.H, dims.I
+    w13x = torch.empty((n, 2 * I, H), dtype=torch.bfloat16, device=dev)
+    w2x = torch.empty((n, H, I), dtype=torch.bfloat16, device=dev)
+    xmap = torch.empty(Ew + n, dtype=torch.int32, device=dev)
+    _check("mxfp4_moe_preshuffle_fused",
+           _L().mxfp4_moe_preshuffle_fused(ctypes.byref(dims), host, _p(w13_fused),
+                                           _p(w13s_fused) if w13s_fused.numel() else None,
+                                           _p(w2_fused),
+                                           _p(w2s_fused) if w2s_fused.numel() else None,
+                                           *[_p(o) for o in outs],
+                                           _p(w13x) if n else None, _p(w2x) if n else None,
+                                           _p(xmap), _stream()))
+    return tuple(outs), {"n": n, "expert_map": xmap, "w13": w13x, "w2": w2x}
+
+
+def mxfp4_moe_forward_mixed(dims: Dims, bx: dict, x, router_logits, w13, w13s, w2, w2s,
+                            top_k: int, clamp_limit: float, out=None, workspace=None,
+                            debug: bool = False):
+    """The layer with experts kept in bf16 (bx from mxfp4_moe_preshuffle_fused).
+    Returns out, or with debug the dict of mxfp4_moe_forward_debug."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    T, H, I, k = dims.T, dims.H, dims.I, int(top_k)
+    ks = k + dims.shared
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = Bf16Experts(int(bx["n"]), bx["expert_map"].data_ptr() if bx["n"] else None,
+                     bx["w13"].data_ptr() if bx["n"] else None,
+                     bx["w2"].data_ptr() if bx["n"] else None)
+    inter = {"act": None, "actq": None, "acts": None, "xq": None, "xs": None, "out32": None}
+    if debug:
+        a8 = bool(dims.flags & MXFP4_MOE_A8)
+        mxa = bool(dims.flags & MXFP4_MOE_A4) or a8
+        q = 1 if a8 else 2
+        inter["act"] = torch.zeros((T * ks, I), dtype=torch.bfloat16, device=dev)
+        if mxa:
+            inter["actq"] = torch.zeros((T * ks, I // q), dtype=torch.uint8, device=dev)
+            inter["acts"] = torch.zeros((T * ks, I // 32), dtype=torch.uint8, device=dev)
+            inter["xq"] = torch.zeros((T, H // q), dtype=torch.uint8, device=dev)
+            inter["xs"] = torch.zeros((T, H // 32), dtype=torch.uint8, device=dev)
+        inter["out32"] = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    workspace, nbytes = _workspace(dims, top_k, workspace, dev)
+    _check("mxfp4_moe_forward_mixed",
+           _L().mxfp4_moe_forward_mixed(ctypes.byref(dims), ctypes.byref(st), _p(x),
+                                        _p(router_logits), _p(w13), _p(w13s), _p(w2), _p(w2s), k,
+                                        float(clamp_limit), _p(out), _p(workspace), nbytes,
+                                        *[_p(inter[n]) for n in ("act", "actq", "acts", "xq",
+                                                                  "xs", "out32")], _stream()))
+    if not debug:
+        return out
+    return dict(inter, out=out)

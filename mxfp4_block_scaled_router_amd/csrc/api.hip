@@ -259,6 +259,7 @@ RouteArgs route_args(const Shape& s, const float* logits, void* ws, const Layout
   r.tile_tok = L.tile_tok ? at<int32_t>(ws, L.tile_tok) : nullptr;
   r.sorted = at<int32_t>(ws, L.sorted);
   r.inv = at<int32_t>(ws, L.inv);
+  r.xmap = nullptr;
   return r;
 }
 
@@ -280,10 +281,35 @@ int check_forward_args(const mxfp4_moe_dims* d, const void* x, const float* logi
   return MXFP4_MOE_OK;
 }
 
+// The experts kept in bf16 (n > 0), or null.
+int check_bf16_experts(const Shape& s, const mxfp4_moe_bf16_experts* bx) {
+  if (!bx) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (bx->n < 0 || bx->n > s.El) return MXFP4_MOE_ERR_BAD_ARGUMENT;
+  if (bx->n == 0) return MXFP4_MOE_OK;
+  if (!bx->expert_map || !bx->w13 || !bx->w2) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(bx->expert_map, 4) || !aligned(bx->w13, 16) || !aligned(bx->w2, 16))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  return MXFP4_MOE_OK;
+}
+
+XArgs x_args(const Shape& s, const RouteArgs& r, const mxfp4_moe_bf16_experts& bx, float clamp_limit) {
+  XArgs xa{};
+  xa.xmap = bx.expert_map;
+  xa.E_local = (int32_t)s.El;
+  xa.n = (int32_t)bx.n;
+  xa.counts = r.counts;
+  xa.offsets = r.offsets;
+  xa.pos_tok = r.pos_tok;
+  xa.pos_w = r.pos_w;
+  xa.T = s.T;
+  xa.clamp_limit = clamp_limit;
+  return xa;
+}
+
 int run_forward(const Shape& s, const Layout& L, const void* x, const float* logits, const uint8_t* w13,
                 const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s, float clamp_limit, void* out,
                 void* ws, hipStream_t stream, float* out32_copy = nullptr,
-                hipEvent_t* events = nullptr) {
+                hipEvent_t* events = nullptr, const mxfp4_moe_bf16_experts* bx = nullptr) {
   if (s.T == 0) return MXFP4_MOE_OK;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(events[i], stream) : hipSuccess;
@@ -292,6 +318,9 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   const GemmPlan plan = choose_plan(s);
   const int mt = 16 * plan.ms;
   RouteArgs r = route_args(s, logits, ws, L, mt, mt);
+  // experts kept in bf16 get no MXFP4 tiles; their own kernels follow each GEMM
+  const bool has_x = bx && bx->n > 0;
+  if (has_x) r.xmap = bx->expert_map;
   // few tokens on the 16-row plan: the gate_up kernel routes them itself
   const bool fused_route = plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) && !separate_route_kernel();
   hipError_t e = fused_route ? hipSuccess : launch_route(r, stream);
@@ -342,6 +371,16 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
       : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (has_x) {
+    XArgs xa = x_args(s, r, *bx, clamp_limit);
+    xa.a = reinterpret_cast<const uint16_t*>(x);
+    xa.w = reinterpret_cast<const uint16_t*>(bx->w13);
+    xa.K = s.H;
+    xa.N = 2 * s.I;
+    xa.act = g.act;
+    e = launch_bf16x_gate_up(xa, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
 
   if (s.mx()) {
     QuantArgs q;
@@ -377,6 +416,17 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
       : plan.ms == 8 ? launch_down_tile(g, max_tiles(s, mt), s.af(), s.ordered, stream)
                      : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (has_x) {
+    XArgs xa = x_args(s, r, *bx, clamp_limit);
+    xa.a = at<uint16_t>(ws, L.act);
+    xa.w = reinterpret_cast<const uint16_t*>(bx->w2);
+    xa.K = s.I;
+    xa.N = s.H;
+    xa.out32 = g.out32;
+    xa.ybuf = g.ybuf;
+    e = launch_bf16x_down(xa, s.ordered, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if ((e = mark(3)) != hipSuccess) return hip_fail(e);
 
   CombineArgs c;
@@ -396,6 +446,21 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     e = launch_copy_rows(g.out32, out32_copy, s.T * s.H * 4, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
+  return MXFP4_MOE_OK;
+}
+
+// Copies of the intermediates the caller asked for (NULL: skipped).
+int copy_intermediates(const Shape& s, const Layout& L, void* ws, void* act, uint8_t* actq, uint8_t* acts,
+                       uint8_t* xq, uint8_t* xs, hipStream_t stream) {
+  if (s.T == 0) return MXFP4_MOE_OK;
+  hipError_t e = hipSuccess;
+  if (act) e = launch_copy_rows(at<uint8_t>(ws, L.act), act, s.S * s.I * 2, stream);
+  if (e == hipSuccess && s.mx() && actq)
+    e = launch_copy_rows(at<uint8_t>(ws, L.actq), actq, s.S * s.I / s.qdiv(), stream);
+  if (e == hipSuccess && s.mx() && acts) e = launch_copy_rows(at<uint8_t>(ws, L.acts), acts, s.S * s.I / 32, stream);
+  if (e == hipSuccess && s.mx() && xq) e = launch_copy_rows(at<uint8_t>(ws, L.xq), xq, s.T * s.H / s.qdiv(), stream);
+  if (e == hipSuccess && s.mx() && xs) e = launch_copy_rows(at<uint8_t>(ws, L.xs), xs, s.T * s.H / 32, stream);
+  if (e != hipSuccess) return hip_fail(e);
   return MXFP4_MOE_OK;
 }
 
@@ -527,6 +592,100 @@ int mxfp4_moe_forward_timed(const mxfp4_moe_dims* d, const void* x, const float*
                      events);
 }
 
+int mxfp4_moe_forward_mixed(const mxfp4_moe_dims* d, const mxfp4_moe_bf16_experts* bx, const void* x,
+                            const float* router_logits, const uint8_t* w13, const uint8_t* w13s,
+                            const uint8_t* w2, const uint8_t* w2s, int32_t top_k, float clamp_limit,
+                            void* out, void* workspace, size_t workspace_bytes, void* act, uint8_t* actq,
+                            uint8_t* acts, uint8_t* xq, uint8_t* xs, float* out32, hipStream_t stream) {
+  Shape s;
+  Layout L;
+  int st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, workspace,
+                              workspace_bytes, &s, &L);
+  if (st) return st;
+  st = check_bf16_experts(s, bx);
+  if (st) return st;
+  if (!aligned(out32, 16) || !aligned(act, 16)) return MXFP4_MOE_ERR_MISALIGNED;
+  st = check_device();
+  if (st) return st;
+  st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream, out32,
+                   nullptr, bx);
+  if (st) return st;
+  return copy_intermediates(s, L, workspace, act, actq, acts, xq, xs, stream);
+}
+
+int mxfp4_moe_preshuffle_fused(const mxfp4_moe_dims* d, const uint8_t* excluded, const uint8_t* w13_fused,
+                               const uint8_t* w13s_fused, const uint8_t* w2_fused, const uint8_t* w2s_fused,
+                               uint8_t* w13, uint8_t* w13s, uint8_t* w2, uint8_t* w2s, void* w13_bf16,
+                               void* w2_bf16, int32_t* expert_map, hipStream_t stream) {
+  Shape s;
+  int st = check_dims(d, 1, false, &s);
+  if (st) return st;
+  if (!excluded || !w13_fused || !w2_fused || !w13 || !w13s || !w2 || !w2s || !expert_map)
+    return MXFP4_MOE_ERR_NULL_POINTER;
+  if (s.El > kExpertMapMax) return MXFP4_MOE_ERR_UNSUPPORTED_SHAPE;
+  ExpertMapArgs m{};
+  m.E = (int32_t)s.El;
+  int64_t n = 0;
+  for (int64_t e = 0; e < s.El; ++e) {
+    if (excluded[e] > 1) return MXFP4_MOE_ERR_BAD_ARGUMENT;
+    if (excluded[e]) {
+      m.bits[e >> 5] |= 1u << (e & 31);
+      ++n;
+    }
+  }
+  if (n < s.El && (!w13s_fused || !w2s_fused)) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (n > 0 && (!w13_bf16 || !w2_bf16)) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(w13_fused, 16) || !aligned(w2_fused, 16) || !aligned(w13s_fused, 16) || !aligned(w2s_fused, 16) ||
+      !aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13s, 4) || !aligned(w2s, 4) || !aligned(w13_bf16, 16) ||
+      !aligned(w2_bf16, 16) || !aligned(expert_map, 4))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  st = check_device();
+  if (st) return st;
+  // per expert: packed codes (N K / 2 bytes) + scales (N K / 32), or bf16 (N K * 2)
+  const int64_t n13 = 2 * s.I * s.H, n2 = s.H * s.I;
+  int64_t o13 = 0, o2 = 0, so13 = 0, so2 = 0, j = 0;
+  for (int64_t e = 0; e < s.El; ++e) {
+    hipError_t err;
+    if (excluded[e]) {
+      err = launch_copy_rows(w13_fused + o13, static_cast<uint8_t*>(w13_bf16) + j * n13 * 2, n13 * 2, stream);
+      if (err == hipSuccess)
+        err = launch_copy_rows(w2_fused + o2, static_cast<uint8_t*>(w2_bf16) + j * n2 * 2, n2 * 2, stream);
+      o13 += n13 * 2;
+      o2 += n2 * 2;
+      ++j;
+    } else {
+      PreshuffleArgs p;
+      p.canon_codes = w13_fused + o13;
+      p.canon_scales = w13s_fused + so13;
+      p.codes = w13 + e * codes_per_expert(2 * s.I, s.H);
+      p.scales = w13s + e * scales_per_expert(2 * s.I, s.H);
+      p.E = 1;
+      p.N = 2 * s.I;
+      p.K = s.H;
+      p.interleave_gate_up = 1;
+      err = launch_preshuffle(p, stream);
+      if (err == hipSuccess) {
+        p.canon_codes = w2_fused + o2;
+        p.canon_scales = w2s_fused + so2;
+        p.codes = w2 + e * codes_per_expert(s.H, s.I);
+        p.scales = w2s + e * scales_per_expert(s.H, s.I);
+        p.N = s.H;
+        p.K = s.I;
+        p.interleave_gate_up = 0;
+        err = launch_preshuffle(p, stream);
+      }
+      o13 += n13 / 2;
+      o2 += n2 / 2;
+      so13 += n13 / 32;
+      so2 += n2 / 32;
+    }
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  hipError_t err = launch_expert_map(m, expert_map, stream);
+  if (err != hipSuccess) return hip_fail(err);
+  return MXFP4_MOE_OK;
+}
+
 int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
                             const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
                             int32_t top_k, float clamp_limit, void* out, void* workspace,
@@ -544,15 +703,7 @@ int mxfp4_moe_forward_debug(const mxfp4_moe_dims* d, const void* x, const float*
   if (!aligned(out32, 16)) return MXFP4_MOE_ERR_MISALIGNED;
   st = run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream, out32);
   if (st) return st;
-  hipError_t e = launch_copy_rows(at<uint8_t>(workspace, L.act), act, s.S * s.I * 2, stream);
-  if (e == hipSuccess && s.mx())
-    e = launch_copy_rows(at<uint8_t>(workspace, L.actq), actq, s.S * s.I / s.qdiv(), stream);
-  if (e == hipSuccess && s.mx()) e = launch_copy_rows(at<uint8_t>(workspace, L.acts), acts, s.S * s.I / 32, stream);
-  if (e == hipSuccess && s.mx())
-    e = launch_copy_rows(at<uint8_t>(workspace, L.xq), xq, s.T * s.H / s.qdiv(), stream);
-  if (e == hipSuccess && s.mx()) e = launch_copy_rows(at<uint8_t>(workspace, L.xs), xs, s.T * s.H / 32, stream);
-  if (e != hipSuccess) return hip_fail(e);
-  return MXFP4_MOE_OK;
+  return copy_intermediates(s, L, workspace, act, actq, acts, xq, xs, stream);
 }
 
 int mxfp4_moe_route(const mxfp4_moe_dims* d, const float* router_logits, int32_t top_k, int32_t* ids,

@@ -39,6 +39,10 @@ struct RouteArgs {
   float* pos_w;         // [S]
   // per tile of height mt1 (== mt2 when set): the token of each of its rows
   int32_t* tile_tok;    // [tile bound][16], or null
+  // experts kept in bf16: xmap[e] >= 0 for such an expert (null: none).  They
+  // keep their counts, offsets and sorted positions but get no tiles, so the
+  // MXFP4 GEMMs never see them; the bf16 expert kernels cover their rows.
+  const int32_t* xmap;  // [E_local]
 };
 
 struct GemmArgs {
@@ -73,6 +77,25 @@ struct GemmArgs {
   // 16-row kernels: shares weighted by dispatch slot (set by the launcher)
   int32_t slot_cus;
   float slot_c;
+};
+
+// Experts kept in bf16 (per-expert exclusions): weights [n][N][K] bf16, the
+// j-th excluded expert in slot j.
+struct XArgs {
+  const uint16_t* a;        // gate_up: x [T][H]; down: act [S][I] (sorted order)
+  const uint16_t* w;        // [n][N][K]
+  const int32_t* xmap;      // [E_local + n]; entry E_local + j = expert of slot j
+  int32_t E_local, n;
+  const int32_t* counts;    // [E_local] rows per expert
+  const int32_t* offsets;   // [E_local + 1] first sorted position per expert
+  const int32_t* pos_tok;   // [S] token of sorted position p
+  const float* pos_w;       // [S] router weight of sorted position p
+  int64_t K, N;             // gate_up: K = H, N = 2I; down: K = I, N = H
+  int64_t T;                // tokens: bound on the rows of one expert
+  float clamp_limit;
+  uint16_t* act;            // gate_up: bf16 [S][I]
+  float* out32;             // down, atomic combine: fp32 [T][H]
+  float* ybuf;              // down, ordered combine: fp32 [S][H]
 };
 
 struct CombineArgs {
@@ -132,6 +155,18 @@ hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool o
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
+// The expert map of the excluded experts from a bit set of E experts passed by
+// value: map[e] = bf16 slot of expert e (its rank among the excluded) or -1,
+// map[E + j] = expert of slot j.
+constexpr int kExpertMapMax = 544;  // 17 words
+struct ExpertMapArgs {
+  uint32_t bits[kExpertMapMax / 32];
+  int32_t E;
+};
+hipError_t launch_expert_map(const ExpertMapArgs& m, int32_t* map, hipStream_t stream);
+// gate_up + SwiGLU and down + combine of the experts kept in bf16 (bf16x.hip)
+hipError_t launch_bf16x_gate_up(const XArgs& a, hipStream_t stream);
+hipError_t launch_bf16x_down(const XArgs& a, bool ordered, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t stream);
 hipError_t launch_copy_rows(const void* src, void* dst, int64_t bytes, hipStream_t stream);

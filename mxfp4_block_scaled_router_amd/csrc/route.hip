@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
   for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < S; s += (int64_t)gridDim.x * blockDim.x) {
     const int e = a.lexp[s];
     if (e >= 0)
-      place_slot(a, s, offs[e] + a.chunk_cnt[(int64_t)e * nchunk + s / 64] + a.rank[s], a.w[s], offs[e], t1[e]);
+      place_slot(a, s, offs[e] + a.chunk_cnt[(int64_t)e * nchunk + s / 64] + a.rank[s], a.w[s], e, offs[e],
+                 t1[e]);
     else
       a.inv[s] = -1;
   }

@@ -209,12 +209,16 @@ __device__ __forceinline__ int32_t wave_incl_sum(int32_t v) {
   return v;
 }
 
+// Whether table expert e is kept in bf16 (its rows get no MXFP4 tiles).
+__device__ __forceinline__ bool bf16_expert(const RouteArgs& a, int e) { return a.xmap && a.xmap[e] >= 0; }
+
 // Exclusive scan of the per-expert counts v[0..n) by one wave: expert offsets
 // and, for the two token-tile heights mt1/mt2, tile offsets (prefix of
-// ceil(v/mt)) into offs_lds[0..n] and t1_lds[0..n] (entry n = total).  With
-// write_global it also writes a.offsets, a.tile_off1/2 and the flat tile
-// tables tiles1/tiles2: tile i -> {expert, rows, first sorted position, 0}.
-// tiles_lds (may be null) receives the mt1 tile table.
+// ceil(v/mt), 0 for an expert kept in bf16) into offs_lds[0..n] and
+// t1_lds[0..n] (entry n = total).  With write_global it also writes a.offsets,
+// a.tile_off1/2 and the flat tile tables tiles1/tiles2: tile i -> {expert,
+// rows, first sorted position, 0}.  tiles_lds (may be null) receives the mt1
+// tile table.
 __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, bool write_global,
                                   int32_t* offs_lds, int32_t* t1_lds, int4* tiles_lds = nullptr) {
   const int lane = lane_id();
@@ -225,9 +229,10 @@ __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, b
   for (int i = 0; i < per; ++i)
     if (b + i < n) {
       int32_t c = v[b + i];
+      const int32_t ct = bf16_expert(a, b + i) ? 0 : c;  // rows that get tiles
       s0 += c;
-      s1 += (c + mt1 - 1) / mt1;
-      s2 += (c + mt2 - 1) / mt2;
+      s1 += (ct + mt1 - 1) / mt1;
+      s2 += (ct + mt2 - 1) / mt2;
     }
   // inclusive wave prefix of the lane totals
   const int32_t i0 = wave_incl_sum(s0), i1 = wave_incl_sum(s1), i2 = wave_incl_sum(s2);
@@ -236,23 +241,24 @@ __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, b
     if (b + i < n) {
       const int e = b + i;
       const int32_t c = v[e];
+      const int32_t ct = bf16_expert(a, e) ? 0 : c;
       offs_lds[e] = r0;
       t1_lds[e] = r1;
       if (tiles_lds)
-        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt1, ++j)
-          tiles_lds[r1 + j] = make_int4(e, c - m0 < mt1 ? c - m0 : mt1, r0 + m0, 0);
+        for (int32_t m0 = 0, j = 0; m0 < ct; m0 += mt1, ++j)
+          tiles_lds[r1 + j] = make_int4(e, ct - m0 < mt1 ? ct - m0 : mt1, r0 + m0, 0);
       if (write_global) {
         a.offsets[e] = r0;
         a.tile_off1[e] = r1;
         a.tile_off2[e] = r2;
-        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt1, ++j)
-          a.tiles1[r1 + j] = make_int4(e, c - m0 < mt1 ? c - m0 : mt1, r0 + m0, 0);
-        for (int32_t m0 = 0, j = 0; m0 < c; m0 += mt2, ++j)
-          a.tiles2[r2 + j] = make_int4(e, c - m0 < mt2 ? c - m0 : mt2, r0 + m0, 0);
+        for (int32_t m0 = 0, j = 0; m0 < ct; m0 += mt1, ++j)
+          a.tiles1[r1 + j] = make_int4(e, ct - m0 < mt1 ? ct - m0 : mt1, r0 + m0, 0);
+        for (int32_t m0 = 0, j = 0; m0 < ct; m0 += mt2, ++j)
+          a.tiles2[r2 + j] = make_int4(e, ct - m0 < mt2 ? ct - m0 : mt2, r0 + m0, 0);
       }
       r0 += c;
-      r1 += (c + mt1 - 1) / mt1;
-      r2 += (c + mt2 - 1) / mt2;
+      r1 += (ct + mt1 - 1) / mt1;
+      r2 += (ct + mt2 - 1) / mt2;
     }
   if (lane == 63) {
     offs_lds[n] = i0;
@@ -267,16 +273,16 @@ __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, b
 
 // Sorted position pos of slot s: the permutation both ways, the side tables
 // (token and router weight w of pos) and -- for 16-row tiles -- the token of
-// that tile row.  off_e, tile_e: offset and first 16-row tile of the slot's
-// expert.
-__device__ __forceinline__ void place_slot(const RouteArgs& a, int64_t s, int32_t pos, float w, int32_t off_e,
-                                           int32_t tile_e) {
+// that tile row.  e, off_e, tile_e: the slot's expert, its offset and first
+// 16-row tile (an expert kept in bf16 has no tiles).
+__device__ __forceinline__ void place_slot(const RouteArgs& a, int64_t s, int32_t pos, float w, int e,
+                                           int32_t off_e, int32_t tile_e) {
   const int32_t t = (int32_t)(s / a.top_k);
   a.sorted[pos] = (int32_t)s;
   a.inv[s] = pos;
   a.pos_tok[pos] = t;
   a.pos_w[pos] = w;
-  if (a.tile_tok) {
+  if (a.tile_tok && !bf16_expert(a, e)) {
     const int32_t rel = pos - off_e;
     a.tile_tok[(int64_t)(tile_e + rel / 16) * 16 + rel % 16] = t;
   }
@@ -356,7 +362,7 @@ __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_gl
     if (e >= 0) {
       const int32_t pos = L.offs[e] + L.cnt[(s / 64) * E + e] + L.rank[s];
       L.ptok[pos] = (int32_t)(s / a.top_k);
-      if (write_global) place_slot(a, s, pos, L.wl[s], L.offs[e], L.t1[e]);
+      if (write_global) place_slot(a, s, pos, L.wl[s], e, L.offs[e], L.t1[e]);
     } else if (write_global) {
       a.inv[s] = -1;
     }

@@ -183,10 +183,10 @@ def bf16_expert(wl: Workload, expert: int, which: str, device="cpu") -> np.ndarr
     """bf16 bits of one expert kept in bf16: [2I, H] for "w13", [H, I] for "w2"."""
     shape = (2 * wl.I, wl.H) if which == "w13" else (wl.H, wl.I)
     if wl.weight_kind == "student_t":
-        t = student_t_expert(wl, expert, which, device=device)
+        t = student_t_expert(wl, int(expert), which, device=device)
         return t.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16).copy()
     tag = 0 if which == "w13" else 1
-    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 0xB16, expert, tag])))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 0xB16, int(expert), tag])))
     return bf16_bits_of(g.standard_normal(shape, dtype=np.float32) * np.float32(BF16_EXPERT_STD))
 
 

@@ -43,7 +43,7 @@ class Case:
     """Inputs of one parity case, on host (canonical numpy) and device."""
 
     def __init__(self, wl: W.Workload, inp: dict | None = None, a4: bool | None = None,
-                 deterministic: bool = False, shared: bool = False):
+                 deterministic: bool = False, shared: bool = False, excluded=None):
         self.wl = wl
         self.a4 = wl.a4 if a4 is None else a4
         self.a8 = wl.a8
@@ -65,9 +65,45 @@ class Case:
                                  a8=self.a8)
         self.x = bf16_dev(self.inp["x"])
         self.logits = to_dev(self.inp["logits"])
-        canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
-        self.pw = mx.mxfp4_moe_preshuffle(self.dims, *canon)
-        del canon
+        Ew = wl.E_local + (1 if shared else 0)
+        self.excluded = np.zeros(Ew, bool)
+        if excluded is not None:
+            self.excluded[list(excluded)] = True
+        self.bx = None
+        if excluded is not None:
+            self._load_fused()
+        else:
+            canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
+            self.pw = mx.mxfp4_moe_preshuffle(self.dims, *canon)
+            del canon
+
+    def _load_fused(self):
+        """Experts in self.excluded kept in bf16: both matrices laid out as fused
+        buffers with per-expert dtypes, loaded by the library's fused loader; the
+        oracle splits the same buffers with its own reading of the layout."""
+        wl = self.wl
+        H, I = wl.H, wl.I
+        idx = np.nonzero(self.excluded)[0]
+        dev = "cuda" if wl.weight_kind == "student_t" else "cpu"
+        b13 = np.stack([W.bf16_expert(wl, e, "w13", device=dev) for e in idx]) if idx.size \
+            else np.zeros((0, 2 * I, H), np.uint16)
+        b2 = np.stack([W.bf16_expert(wl, e, "w2", device=dev) for e in idx]) if idx.size \
+            else np.zeros((0, H, I), np.uint16)
+        f13, f13s = W.fuse(self.inp["w13"], self.inp["w13s"], b13, self.excluded)
+        f2, f2s = W.fuse(self.inp["w2"], self.inp["w2s"], b2, self.excluded)
+        c13, s13, ob13 = oracle.unfuse(f13, f13s, self.excluded, 2 * I, H)
+        c2, s2, ob2 = oracle.unfuse(f2, f2s, self.excluded, H, I)
+        self.oracle_w = dict(w13=c13, w13s=s13, w2=c2, w2s=s2, w13_bf16=ob13, w2_bf16=ob2)
+        self.fused = (f13, f13s, f2, f2s)
+        self.pw, self.bx = mx.mxfp4_moe_preshuffle_fused(
+            self.dims, list(self.excluded), *[to_dev(a) for a in self.fused])
+
+    def excluded_rows(self, o) -> np.ndarray:
+        """Sorted positions of the experts kept in bf16 (bool [N_assign])."""
+        rows = np.zeros(o.n_assign, bool)
+        for e in np.nonzero(self.excluded)[0]:
+            rows[o.offsets[e]:o.offsets[e + 1]] = True
+        return rows
 
     def _quantise_student_t(self):
         """Student-t weights: drawn on the GPU, quantised there by the library and
@@ -92,6 +128,11 @@ class Case:
 
     def run_gpu(self, debug=True):
         wl = self.wl
+        if self.bx is not None:
+            r = mx.mxfp4_moe_forward_mixed(self.dims, self.bx, self.x, self.logits, *self.pw,
+                                           wl.top_k, wl.clamp_limit, debug=debug)
+            torch.cuda.synchronize()
+            return r if debug else {"out": r}
         if debug:
             r = mx.mxfp4_moe_forward_debug(self.dims, self.x, self.logits, *self.pw, wl.top_k,
                                            wl.clamp_limit)
@@ -108,6 +149,17 @@ class Case:
 
     def run_oracle(self, token_mask=None, actq_in=None, acts_in=None):
         wl = self.wl
+        if self.bx is not None:
+            ow = self.oracle_w
+            return oracle.moe_forward(self.inp["x"], self.inp["logits"], ow["w13"], ow["w13s"],
+                                      ow["w2"], ow["w2s"], top_k=wl.top_k,
+                                      clamp_limit=wl.clamp_limit, E_global=wl.E_global,
+                                      first_local=wl.first_local, a4=self.a4, a8=self.a8,
+                                      shared=self.shared, token_mask=token_mask,
+                                      want_act=token_mask is None or self.a4 or self.a8,
+                                      actq_in=actq_in, acts_in=acts_in,
+                                      bf16_experts=self.excluded, w13_bf16=ow["w13_bf16"],
+                                      w2_bf16=ow["w2_bf16"])
         return oracle.moe_forward(self.inp["x"], self.inp["logits"], self.inp["w13"],
                                   self.inp["w13s"], self.inp["w2"], self.inp["w2s"],
                                   top_k=wl.top_k, clamp_limit=wl.clamp_limit,

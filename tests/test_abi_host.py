@@ -233,3 +233,58 @@ def test_no_gpu_gives_device_refusal_not_a_crash(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert fwd(lib, dims()) == UNSUPPORTED_DEVICE
+
+
+def mixed(lib, d, bx, k=2, ptrs=None):
+    p = dict(x=A, logits=A, w13=A, w13s=A, w2=A, w2s=A, out=A, ws=A)
+    if ptrs:
+        p.update(ptrs)
+    ws = ws_status(d, k)[1]
+    V = ctypes.c_void_p
+    return lib.mxfp4_moe_forward_mixed(ctypes.byref(d), None if bx is None else ctypes.byref(bx),
+                                       V(p["x"]), V(p["logits"]), V(p["w13"]), V(p["w13s"]),
+                                       V(p["w2"]), V(p["w2s"]), k, 7.0, V(p["out"]), V(p["ws"]),
+                                       ws, None, None, None, None, None, None, None)
+
+
+def test_forward_mixed_refusals(lib):
+    d = dims()
+    assert mixed(lib, d, None) == NULL_POINTER
+    assert mixed(lib, d, mx.Bf16Experts(-1, A, A, A)) == BAD_ARGUMENT
+    assert mixed(lib, d, mx.Bf16Experts(9, A, A, A)) == BAD_ARGUMENT      # > E_local
+    assert mixed(lib, d, mx.Bf16Experts(2, None, A, A)) == NULL_POINTER
+    assert mixed(lib, d, mx.Bf16Experts(2, A, None, A)) == NULL_POINTER
+    assert mixed(lib, d, mx.Bf16Experts(2, A, A + 8, A)) == MISALIGNED
+    assert mixed(lib, d, mx.Bf16Experts(2, A + 2, A, A)) == MISALIGNED
+    # with the shared expert the buffers hold E_local + 1 experts
+    ds = dims(flags=mx.MXFP4_MOE_SHARED_EXPERT)
+    assert mixed(lib, ds, mx.Bf16Experts(9, A, A, A)) in (OK, UNSUPPORTED_DEVICE)
+    assert mixed(lib, ds, mx.Bf16Experts(10, A, A, A)) == BAD_ARGUMENT
+    # n = 0 needs no map or weights; the usual forward checks come first
+    assert mixed(lib, d, mx.Bf16Experts(0, None, None, None)) in (OK, UNSUPPORTED_DEVICE)
+    assert mixed(lib, d, mx.Bf16Experts(0, None, None, None), ptrs={"w13": 0}) == NULL_POINTER
+    assert mixed(lib, dims(H=0), mx.Bf16Experts(0, None, None, None)) == EMPTY_SHAPE
+
+
+def test_preshuffle_fused_refusals(lib):
+    V = ctypes.c_void_p
+    d = dims()
+    f = lib.mxfp4_moe_preshuffle_fused
+
+    def call(flags, **kw):
+        p = dict(w13f=A, w13sf=A, w2f=A, w2sf=A, w13=A, w13s=A, w2=A, w2s=A, b13=A, b2=A, map=A)
+        p.update(kw)
+        ex = None if flags is None else (ctypes.c_uint8 * len(flags))(*flags)
+        return f(ctypes.byref(d), ex, *[V(p[n]) for n in ("w13f", "w13sf", "w2f", "w2sf", "w13",
+                                                          "w13s", "w2", "w2s", "b13", "b2", "map")],
+                 None)
+    ok = (OK, UNSUPPORTED_DEVICE)
+    assert call(None) == NULL_POINTER
+    assert call([0, 2, 0, 0, 0, 0, 0, 0]) == BAD_ARGUMENT
+    assert call([0, 1, 0, 0, 0, 0, 0, 0], b13=0) == NULL_POINTER
+    assert call([0] * 8, b13=0, b2=0) in ok                     # nothing excluded: no bf16 outputs
+    assert call([1] * 8, w13sf=0, w2sf=0) in ok                 # all excluded: no scale tensors
+    assert call([0, 1, 0, 0, 0, 0, 0, 0], w13sf=0) == NULL_POINTER
+    assert call([0] * 8, map=0) == NULL_POINTER
+    assert call([0] * 8, w2f=A + 8) == MISALIGNED
+    assert call([0, 1, 0, 0, 0, 0, 0, 0], map=A + 2) == MISALIGNED

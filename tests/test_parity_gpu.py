@@ -121,7 +121,9 @@ def _a4_output_checks(case, g, o, token_mask, stats):
     slots = o.ids.shape[1]
     tok = o.sorted // slots                      # token of each sorted position
     checked = np.ones(n, bool) if token_mask is None else np.asarray(token_mask)[tok]
-    div = ((gq != o.actq[:n]).any(axis=1) | (gs != o.acts[:n]).any(axis=1)) & checked
+    # rows of experts kept in bf16 have no codes on the oracle's side
+    div = ((gq != o.actq[:n]).any(axis=1) | (gs != o.acts[:n]).any(axis=1)) & checked & \
+        ~case.excluded_rows(o)
     stats["actq_rows_diverging"] = int(div.sum())
     act_differs = (bits_of(g["act"])[:n] != o.act[:n]).any(axis=1)
     assert not (div & ~act_differs).any(), stats
@@ -207,6 +209,65 @@ def test_forward_a8_full_sampled():
     case = Case(W.WORKLOADS["a8"])
     assert case.quant_mismatch == 0
     _check_case(case, token_mask=_sample_mask(case.wl.T, 16, 4))
+
+
+EXCLUSION_CASES = {
+    # (workload, excluded experts of the weight buffers, Case options)
+    "tiny": (W.WORKLOADS["tiny"], [1, 5], {}),
+    "tiny_all": (W.WORKLOADS["tiny"], list(range(8)), {}),
+    "decode": (W.WORKLOADS["decode"], [3, 17, 40, 63], {}),           # routing in gate_up
+    "decode_det": (W.WORKLOADS["decode"], [0, 33], {"deterministic": True}),
+    "decode_shared": (W.WORKLOADS["decode"], [5, 64], {"shared": True}),  # the shared one too
+    "ep_share_small": (SMALL_CASES["ep_share_small"], [2, 9], {}),
+    "mid_lds": (SMALL_CASES["mid_lds"], [0, 7, 12], {}),             # 64-row tiles
+    "prefill_small": (SMALL_CASES["prefill_small"], [4, 11], {}),    # 128-row tiles
+    "a4_mid": (A4_CASES["a4_mid"], [2, 9], {}),
+    "a8_mid": (A8_CASES["a8_mid"], [6], {}),
+    "a8_decode": (A8_CASES["a8_decode"], [1, 30], {}),
+}
+
+
+@pytest.mark.parametrize("name", list(EXCLUSION_CASES))
+def test_forward_bf16_exclusions(name):
+    """Experts kept in bf16 inside fused expert buffers: the fused loader, the
+    routing without their tiles and the bf16 expert kernels, through each tile
+    height, both combines, A4/A8 and the shared expert."""
+    wl, ex, kw = EXCLUSION_CASES[name]
+    case = Case(wl, excluded=ex, **kw)
+    log("excluded %s" % (list(np.nonzero(case.excluded)[0]),))
+    _check_case(case)
+
+
+def test_forward_bf16_exclusions_prefill_sampled():
+    case = Case(W.WORKLOADS["prefill"], excluded=[0, 64, 127])
+    _check_case(case, token_mask=_sample_mask(case.wl.T, 24, 5))
+
+
+def test_preshuffle_fused_matches_preshuffle():
+    """The fused loader: packed experts' preshuffled slots equal
+    mxfp4_moe_preshuffle's, the bf16 buffers hold the excluded experts in order,
+    and the expert map lists both directions."""
+    wl = W.WORKLOADS["tiny"]
+    excluded = [0, 3, 4, 7]
+    plain = Case(wl)
+    fused = Case(wl, inp=plain.inp, excluded=excluded)
+    sizes = mx.mxfp4_moe_preshuffled_bytes(plain.dims)
+    for i, n in enumerate(("w13", "w13s", "w2", "w2s")):
+        per = sizes[i] // wl.E_local
+        a = plain.pw[i].view(wl.E_local, per).cpu().numpy()
+        b = fused.pw[i].view(wl.E_local, per).cpu().numpy()
+        keep = ~fused.excluded
+        np.testing.assert_array_equal(a[keep], b[keep], err_msg=n)
+    ow = fused.oracle_w
+    np.testing.assert_array_equal(bits_of(fused.bx["w13"]).reshape(ow["w13_bf16"].shape),
+                                  ow["w13_bf16"])
+    np.testing.assert_array_equal(bits_of(fused.bx["w2"]).reshape(ow["w2_bf16"].shape),
+                                  ow["w2_bf16"])
+    m = fused.bx["expert_map"].cpu().numpy()
+    expect = [-1] * 8
+    for j, e in enumerate(excluded):
+        expect[e] = j
+    np.testing.assert_array_equal(m, expect + excluded)
 
 
 @pytest.mark.parametrize("name", list(SHARED_CASES))
