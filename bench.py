@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--deterministic", action="store_true", help="ordered combine")
     ap.add_argument("--shared", action="store_true",
                     help="with the shared expert (one more expert every token reads)")
+    ap.add_argument("--bf16-experts", type=int, default=0,
+                    help="keep this many experts (evenly spaced) in bf16 inside fused buffers; "
+                         "times the whole step only (no phase split, roofline null)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -157,6 +160,70 @@ def cpu_baseline(wl, inp, target_s, shared=False):
                       "combine of the sampled ones), %.1f s" % (n, wl.T, wl.name, t)}
 
 
+def bench_bf16_experts(args, wl):
+    """Whole-step timing of the layer with experts kept in bf16 inside fused
+    buffers (mxfp4_moe_forward_mixed), against the all-MXFP4 layer on the same
+    packed weights."""
+    import numpy as np
+    import torch
+    import mxfp4_block_scaled_router_amd as mx
+    from mxfp4_block_scaled_router_amd import workloads as W
+    inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies, args.shared)
+    if wl.weight_kind != "uniform" or args.shared:
+        sys.exit("--bf16-experts: uniform-code workloads without --shared only")
+    Ew = wl.E_local
+    n = min(args.bf16_experts, Ew)
+    excluded = np.zeros(Ew, bool)
+    excluded[(np.arange(n) * Ew) // n] = True
+    idx = np.nonzero(excluded)[0]
+    b13 = np.stack([W.bf16_expert(wl, e, "w13") for e in idx])
+    b2 = np.stack([W.bf16_expert(wl, e, "w2") for e in idx])
+    f13, f13s = W.fuse(inp["w13"], inp["w13s"], b13, excluded)
+    f2, f2s = W.fuse(inp["w2"], inp["w2s"], b2, excluded)
+    dev = [torch.from_numpy(a).cuda() for a in (f13, f13s, f2, f2s)]
+    mixed = [mx.mxfp4_moe_preshuffle_fused(dims, list(excluded), *dev) for _ in range(len(banks))]
+    del dev
+    k = wl.top_k
+    ws = torch.empty(mx.mxfp4_moe_workspace_bytes(dims, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def time_steps(step):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms_mixed = time_steps(lambda i: mx.mxfp4_moe_forward_mixed(
+        dims, mixed[i % len(mixed)][1], x, logits, *mixed[i % len(mixed)][0], k, wl.clamp_limit,
+        out=out, workspace=ws))
+    ms_packed = time_steps(lambda i: mx.mxfp4_moe_forward(
+        dims, x, logits, *banks[i % len(banks)], k, wl.clamp_limit, out=out, workspace=ws))
+    rt = mx.mxfp4_moe_route(dims, logits, k, workspace=ws)
+    counts = rt["counts"].cpu().numpy()
+    rec = {
+        "metric": METRIC, "value": wl.T / (ms_mixed * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_mixed,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded: x~N(0,1) bf16, logits~N(0,1), uniform E2M1 codes; bf16 "
+                "experts N(0, 0.16^2))",
+        "config": {"workload": "%s with %d of %d experts kept in bf16" % (wl.name, n, Ew),
+                   "bf16_experts": [int(e) for e in idx],
+                   "rows_on_bf16_experts": int(counts[idx].sum()),
+                   "rows_total": int(counts.sum()), "parallelism": "single GPU"},
+        "all_mxfp4_ms_per_step": ms_packed,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,6 +240,8 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     mx.load_library()
+    if args.bf16_experts:
+        return bench_bf16_experts(args, wl)
     inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies, args.shared)
     if args.deterministic:
         dims.flags |= mx.MXFP4_MOE_DETERMINISTIC

@@ -302,6 +302,7 @@ XArgs x_args(const Shape& s, const RouteArgs& r, const mxfp4_moe_bf16_experts& b
   xa.pos_tok = r.pos_tok;
   xa.pos_w = r.pos_w;
   xa.T = s.T;
+  xa.rows_per_expert = s.S / s.Eg;
   xa.clamp_limit = clamp_limit;
   return xa;
 }

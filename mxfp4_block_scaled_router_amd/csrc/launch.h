@@ -92,6 +92,7 @@ struct XArgs {
   const float* pos_w;       // [S] router weight of sorted position p
   int64_t K, N;             // gate_up: K = H, N = 2I; down: K = I, N = H
   int64_t T;                // tokens: bound on the rows of one expert
+  int64_t rows_per_expert;  // expected rows of one expert, T k / E_global
   float clamp_limit;
   uint16_t* act;            // gate_up: bf16 [S][I]
   float* out32;             // down, atomic combine: fp32 [T][H]
