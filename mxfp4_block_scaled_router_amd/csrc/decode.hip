@@ -580,13 +580,14 @@ struct GridKey {
   const void* fn;
   int block;
   size_t lds;
+  int cap;
   int grid;
 };
 std::mutex g_grid_mu;
 GridKey g_grid_cache[128];
 int g_grid_n = 0;
 
-hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
+hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid, int cap_per_cu = 0) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -594,7 +595,7 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
     std::lock_guard<std::mutex> lk(g_grid_mu);
     for (int i = 0; i < g_grid_n; ++i) {
       const GridKey& k = g_grid_cache[i];
-      if (k.dev == dev && k.fn == fn && k.block == block && k.lds == lds) {
+      if (k.dev == dev && k.fn == fn && k.block == block && k.lds == lds && k.cap == cap_per_cu) {
         *grid = k.grid;
         return hipSuccess;
       }
@@ -603,6 +604,7 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
   int cus = 0, per_cu = 0;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds)) != hipSuccess) return e;
+  if (cap_per_cu > 0 && cap_per_cu < per_cu) per_cu = cap_per_cu;
   if (const char* env = getenv("MXFP4_MOE_DECODE_WGS_PER_CU")) {
     const int cap = atoi(env);
     if (cap > 0 && cap < per_cu) per_cu = cap;
@@ -610,12 +612,12 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid) {
   if (per_cu < 1) per_cu = 1;
   *grid = cus * per_cu;
   std::lock_guard<std::mutex> lk(g_grid_mu);
-  if (g_grid_n < 128) g_grid_cache[g_grid_n++] = GridKey{dev, fn, block, lds, *grid};
+  if (g_grid_n < 128) g_grid_cache[g_grid_n++] = GridKey{dev, fn, block, lds, cap_per_cu, *grid};
   return hipSuccess;
 }
 
 // Slot weights c of the shares (measured on MI355X: with 3 workgroups per CU
-// the third streams ~1.35x slower than the first; c = 0.15 for gate_up and 0.1
+// the third streams ~1.35x slower than the first; c = 0.25 for gate_up and 0.1
 // for down took the kernels' last workgroups in by ~1 us).
 // MXFP4_MOE_SLOT_C_GU / MXFP4_MOE_SLOT_C_DN (benchmarks only) override them.
 float slot_c(const char* name, float dflt) {
@@ -640,20 +642,31 @@ int device_cus() {
 }
 
 template <typename Kernel, typename... Args>
-hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, hipStream_t s,
-                             const Args&... args) {
+hipError_t launch_persistent_capped(Kernel kernel, int nw, size_t lds, int64_t max_units, int cap_per_cu,
+                                    hipStream_t s, const Args&... args) {
   int grid = 0;
-  hipError_t e = resident_grid(reinterpret_cast<const void*>(kernel), nw * 64, lds, &grid);
+  hipError_t e = resident_grid(reinterpret_cast<const void*>(kernel), nw * 64, lds, &grid, cap_per_cu);
   if (e != hipSuccess) return e;
   if ((int64_t)grid > max_units) grid = (int)max_units;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), lds, s, args...);
   return hipGetLastError();
 }
+template <typename Kernel, typename... Args>
+hipError_t launch_persistent(Kernel kernel, int nw, size_t lds, int64_t max_units, hipStream_t s,
+                             const Args&... args) {
+  return launch_persistent_capped(kernel, nw, lds, max_units, 0, s, args...);
+}
+
+// The down kernel's occupancy allows 4 workgroups per CU, but at that size
+// some of the grid was measured (MI355X, decode dims) to start only as others
+// finished, up to 10 us late; a persistent grid must be resident, so down
+// takes at most 3 per CU.
+constexpr int kDownWgsPerCu = 3;
 
 template <int KPW, int D, int AF>
 hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, hipStream_t s) {
   GemmArgs a = a0;
-  static const float c_gu = slot_c("MXFP4_MOE_SLOT_C_GU", 0.15f);
+  static const float c_gu = slot_c("MXFP4_MOE_SLOT_C_GU", 0.25f);
   a.slot_c = c_gu;
   a.slot_cus = a.slot_c != 0.f ? device_cus() : 0;
   const int KT = (int)(a.K / kTileK);
@@ -686,8 +699,11 @@ hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 16 / NG);
   const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
-  return KT % KPW == 0 ? launch_persistent(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>, nw, lds, mu, s, a)
-                       : launch_persistent(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>, nw, lds, mu, s, a);
+  return KT % KPW == 0
+             ? launch_persistent_capped(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>, nw, lds, mu, kDownWgsPerCu,
+                                        s, a)
+             : launch_persistent_capped(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>, nw, lds, mu, kDownWgsPerCu,
+                                        s, a);
 }
 
 template <int KPW, int D>
