@@ -12,13 +12,16 @@
 // an LDS ring of STAGES slots by the gfx950 global->LDS load (a wave's
 // instruction writes 64 x 16 bytes, lane i at slot + 16 i, from any per-lane
 // address), so staging costs no registers.  The weight scale dwords (one per
-// lane and row group covers 4 k-tiles) are not staged: each wave loads its
-// own into registers, a quarter of the next 4-k-tile group per k-tile.  Every
-// wave issues the same loads in the same order per k-tile (scale loads, then
-// copies); before using slot kt a wave waits until only the later stages'
-// loads are outstanding, and one barrier per k-tile then publishes the slot
-// to the whole workgroup and frees the slot the next copy writes (it was
-// read in the previous iteration).
+// lane and row group covers a group of 4 k-tiles) go the same way into one
+// LDS buffer, a group at a time, and each wave reads its row groups' dwords
+// into registers at the group's first k-tile.  Every wave issues the same
+// copies in the same order per k-tile; before using slot kt a wave waits
+// until only the loads issued after slot kt's are outstanding, and one
+// barrier per k-tile then publishes the slot to the whole workgroup and frees
+// the slot the next copy writes (it was read in the previous iteration).
+// No per-lane global load feeds a register inside the loop: a register that
+// a pending load writes makes the compiler wait for it, and vmcnt counts in
+// issue order, so such a wait would also wait for every copy issued before.
 //
 // Bank conflicts.  The activation rows are stored with their 16-byte chunks
 // XOR-swizzled by the row (bf16: chunk c of row r at c ^ (r & 15); MXFP4:
@@ -72,18 +75,22 @@ struct Cfg {
   static constexpr int A_OFF = 0, AS_OFF = A_BYTES, B_OFF = A_BYTES + AS_BYTES;
   static constexpr int STAGE = B_OFF + B_BYTES;
   static constexpr int ROWS_BYTES = kMT * 4;  // int32 [kMT]: A row index of each tile row
-  static constexpr int STAGES_FIT = (160 * 1024 - ROWS_BYTES) / STAGE;
+  static constexpr int WS_BYTES = NRG * 256;   // weight scale dwords of one 4-k-tile group
+  static constexpr int STAGES_FIT = (160 * 1024 - ROWS_BYTES - WS_BYTES) / STAGE;
   static constexpr int STAGES = STAGES_FIT > 4 ? 4 : STAGES_FIT;
   static constexpr int A_CP = A_BYTES / 1024 / kWaves;  // copies per wave per k-tile
   static constexpr int AS_CP = AF != kActBf16 ? 1 : 0;  // 2 copies, made by even and odd waves alike
   static constexpr int B_CP = NRG / kWaves;
   static constexpr int CP = A_CP + AS_CP + B_CP;
-  static constexpr int SCP = WN / 4;                    // scale dword loads per wave per k-tile
-  static constexpr int ROWS_OFF = STAGES * STAGE;
+
+  static constexpr int WS_OFF = STAGES * STAGE;
+  static constexpr int ROWS_OFF = WS_OFF + WS_BYTES;
   static constexpr int LDS = ROWS_OFF + ROWS_BYTES;
   static_assert(STAGES >= 2 && LDS <= 160 * 1024, "LDS budget");
   static_assert(WN % 4 == 0 && NRG % kWaves == 0, "tile shape");
-  static_assert((STAGES - 2) * (CP + SCP) + SCP < 64, "vmcnt range");
+  static constexpr int WSCP = NRG / kWaves;             // weight scale copies per wave per group
+  static constexpr int MAXWAIT = (STAGES - 2) * (CP + WSCP);
+  static_assert(MAXWAIT < 64, "vmcnt range");
 };
 
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding:
@@ -94,19 +101,17 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// wait_vm<later * CP + since * SCP>() for later, since in [0, S-2] (S <= 4)
-template <int CP, int SCP, int S>
-__device__ __forceinline__ void wait_slot(int later, int since) {
-  static_assert(S >= 2 && S <= 4, "stages");
-  if constexpr (S == 2) {
+// wait_vm<n>() for a wave-uniform n in [0, MAX] (larger n: wait for all)
+template <int MAX, int N = 0>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  if constexpr (N > MAX) {
     wait_vm<0>();
   } else {
-#define MXMOE_W(L, T) \
-  if (later == L && since == T) { wait_vm<L * CP + T * SCP>(); return; }
-    MXMOE_W(0, 0) MXMOE_W(0, 1) MXMOE_W(1, 0) MXMOE_W(1, 1)
-    if constexpr (S == 4) { MXMOE_W(0, 2) MXMOE_W(1, 2) MXMOE_W(2, 0) MXMOE_W(2, 1) MXMOE_W(2, 2) }
-#undef MXMOE_W
-    wait_vm<0>();  // not reached
+    if (n == N) {
+      wait_vm<N>();
+      return;
+    }
+    wait_vm_dyn<MAX, N + 1>(n);
   }
 }
 
@@ -212,11 +217,16 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
   auto b_off = [&](int jj) -> int64_t {
     return codes_tile_offset(clamp_rg(it.n0 / 16 + wave * C::B_CP + jj), 0, K);
   };
-  // this wave's scale dwords: row group WN wn + cb, 4-k-tile group q
+  // scale dwords of 4-k-tile group q (clamped to the last group): wave w
+  // copies row groups w WSCP .. w WSCP + WSCP - 1 of the tile, 256 bytes each
   const int NQ = (KT + 3) / 4;
-  auto sload = [&](int cb, int q) -> uint32_t {
-    const int64_t off = scales_group_offset(clamp_rg(it.n0 / 16 + wn * WN + cb), q < NQ ? q : NQ - 1, K);
-    return *reinterpret_cast<const uint32_t*>(s_lane + off);
+  auto issue_scales = [&](int q) {
+    q = q < NQ ? q : NQ - 1;
+#pragma unroll
+    for (int i = 0; i < C::WSCP; ++i) {
+      const int rgl = wave * C::WSCP + i;
+      copy4(s_lane + scales_group_offset(clamp_rg(it.n0 / 16 + rgl), q, K), lds + C::WS_OFF + rgl * 256);
+    }
   };
 
   auto issue = [&](int kt, uint8_t* slot) {
@@ -233,11 +243,9 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     }
   };
 
-  // scale dwords of the current 4-k-tile group and of the next one; k-tile
-  // kt loads quarter kt % 4 of group kt/4 + 1
-  uint32_t scur[WN], snxt[WN];
-#pragma unroll
-  for (int cb = 0; cb < WN; ++cb) scur[cb] = sload(cb, 0);
+  // this wave's scale dwords of the current 4-k-tile group (row group
+  // WN wn + cb), read from LDS at the group's first k-tile
+  uint32_t scur[WN];
 
   auto compute = [&](int kt, const uint8_t* slot) {
     const int g = lane >> 4;
@@ -305,39 +313,53 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     }
   };
 
-  // ---- pipeline: stages 0 .. STAGES-2 in flight before the loop
+  // ---- pipeline: stages 0 .. STAGES-2 in flight before the loop.  Step kt:
+  // wait for slot kt's copies, barrier, scale loads (steps 0 and 1 of a
+  // group), the copies of k-tile kt + S - 1, compute k-tile kt.  Every step
+  // issues its copies, past K those of the last k-tile again (into the slot
+  // read in the previous step, free after the barrier): with the same
+  // instructions on every path the compiler's own waits for the scale
+  // registers count exactly and never fall back to waiting for everything.
   constexpr int S = C::STAGES;
+  issue_scales(0);
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < KT) issue(s, lds + s * C::STAGE);
-  for (int kt0 = 0; kt0 < KT; kt0 += S) {
+  for (int s = 0; s < S - 1; ++s) issue(s < KT ? s : KT - 1, lds + s * C::STAGE);
+  // vector-memory ops a step issues: the next group's scale copies (second
+  // k-tile of a group: every wave has read the buffer at the first, before
+  // this step's barrier), then the stage copies
+  auto ops_of_step = [&](int st) -> int { return ((st & 3) == 1 ? C::WSCP : 0) + C::CP; };
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int kt = kt0 + j;
       if (kt >= KT) break;
-      // loads issued after slot kt's copies: the copies of the later stages
-      // already issued (at most S-2) and the scale loads of the steps since
-      // (at most S-2 steps; fewer in the first ones)
-      const int later = KT - 1 - kt < S - 2 ? KT - 1 - kt : S - 2;
-      const int since = kt < S - 2 ? kt : S - 2;
-      wait_slot<C::CP, C::SCP, S>(later, since);
+      // ops issued after slot kt's copies (vmcnt counts in issue order): the
+      // prologue's later stages (k-tile kt < S - 1) or the ops of the steps
+      // between the one that issued slot kt and this one
+      int after = 0;
+      if (kt < S - 1) {
+        after = (S - 2 - kt) * C::CP;
+#pragma unroll
+        for (int st = 0; st < S - 2; ++st)
+          if (st < kt) after += ops_of_step(st);
+      } else {
+#pragma unroll
+        for (int d = 1; d <= S - 2; ++d) after += ops_of_step(kt - d);
+      }
+      wait_vm_dyn<C::MAXWAIT>(after);
       __builtin_amdgcn_s_barrier();
-      // a new 4-k-tile group starts: its scale dwords came in over the
-      // previous group's k-tiles
-      if ((kt & 3) == 0 && kt > 0) {
+      // a new 4-k-tile group starts: its scale dwords were copied at the
+      // previous group's second k-tile (before the stage copies waited for
+      // above), or in the prologue
+      if (j == 0) {
 #pragma unroll
-        for (int cb = 0; cb < WN; ++cb) scur[cb] = snxt[cb];
+        for (int cb = 0; cb < WN; ++cb)
+          scur[cb] = *reinterpret_cast<const uint32_t*>(lds + C::WS_OFF + (wn * WN + cb) * 256 + lane * 4);
       }
-      // quarter kt % 4 of the next group's scale dwords (before the copies,
-      // so waiting for a slot never waits for a newer scale load)
-#pragma unroll
-      for (int i = 0; i < C::SCP; ++i) {
-        const int cb = (kt & 3) * C::SCP + i;
-        snxt[cb] = sload(cb, (kt >> 2) + 1);
-      }
+      if (j == 1) issue_scales((kt >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + S - 1 < KT) issue(kt + S - 1, lds + ((j + S - 1) % S) * C::STAGE);
-      compute(kt, lds + j * C::STAGE);
+      issue(kt + S - 1 < KT ? kt + S - 1 : KT - 1, lds + ((kt + S - 1) % S) * C::STAGE);
+      compute(kt, lds + (kt % S) * C::STAGE);
     }
   }
 }
