@@ -322,13 +322,23 @@ __device__ __forceinline__ RouteLds route_lds(int32_t* base, int64_t S, int64_t 
   return L;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and
+// scalar) operations, not for its vector-memory loads, which may stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+  __builtin_amdgcn_s_barrier();
+}
+
 // The whole routing of a.T tokens by one workgroup (any number of waves),
 // everything after the logits kept in LDS: slot experts, weights and ranks,
 // chunk counts, counts, expert and tile offsets, the mt1 tile table and the
 // token of every sorted position.  With write_global the workgroup also writes
 // every global routing table (ids, w, counts, offsets, tile tables, sorted,
 // inv, pos_tok, pos_w, tile_tok).  Ends with the LDS results visible to the
-// whole workgroup.  MAXVPL: as in topk_any.
+// whole workgroup.  MAXVPL: as in topk_any.  The barriers after the top-k
+// wait only for LDS traffic (nothing here reads global memory written inside
+// the routing), so the global table stores stay in flight across them.
 template <int MAXVPL = 32>
 __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_global) {
   const int nwaves = blockDim.x / 64;
@@ -342,7 +352,7 @@ __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_gl
   __syncthreads();
   const int nbits = 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1));
   for (int64_t c = wave; c < nchunk; c += nwaves) chunk_ranks(S, c, L.lexp, L.cnt + c * E, 1, L.rank, nbits);
-  __syncthreads();
+  lds_barrier();
   // per expert: running sum over chunks -> chunk bases; totals -> counts
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int32_t run = 0;
@@ -354,9 +364,9 @@ __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_gl
     L.counts[e] = run;
     if (write_global) a.counts[e] = run;
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) wave_scan_experts(L.counts, E, a, write_global, L.offs, L.t1, L.tiles);
-  __syncthreads();
+  lds_barrier();
   for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = L.lexp[s];
     if (e >= 0) {
@@ -367,7 +377,7 @@ __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_gl
       a.inv[s] = -1;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 }  // namespace
