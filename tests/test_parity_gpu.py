@@ -47,6 +47,12 @@ SMALL_CASES = {
     "topk32": W.Workload("topk32", 8, 128, 128, 64, 64, 0, 32, seed=7),
     "no_clamp": W.Workload("no_clamp", 32, 512, 256, 8, 8, 0, 2, clamp_limit=float("inf"),
                            seed=8),
+    # K of 56 and 48 k-tiles: the 16-row kernels' 8-k-tiles-per-wave variant;
+    # 256 global experts: the routing kernel path (too many for the fused one)
+    "wide_h_e256": W.Workload("wide_h_e256", 4, 7168, 256, 256, 32, 64, 8, scale_lo=118,
+                              scale_hi=124, seed=9),
+    "wide_i": W.Workload("wide_i", 8, 256, 6144, 16, 16, 0, 2, scale_lo=118, scale_hi=124,
+                         seed=10),
 }
 A4_CASES = {
     "a4_tiny": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
