@@ -39,18 +39,39 @@ __device__ __forceinline__ int4 tile_entry(const GemmArgs& a, int t) {
   return make_int4(p[0], p[1], p[2], p[3]);
 }
 
-// A scale dword holds the scales of 4 k-tiles (one per byte).  With KPW
-// dividing 4 a wave's k-tiles [w*KPW, w*KPW + KPW) lie in one dword.
+// A scale dword holds the scales of 4 k-tiles (one per byte).  A wave's
+// k-tiles [w*KPW, w*KPW + KPW) cover at most kScaleWords<KPW> dwords: the
+// largest span over the residues w*KPW mod 4 (KPW 8: 2, KPW 7: 3, KPW 4: 1).
+constexpr int scale_words(int kpw) {
+  int m = 1;
+  for (int w = 0; w < 4; ++w) {
+    const int n = ((w * kpw) % 4 + kpw - 1) / 4 + 1;
+    m = n > m ? n : m;
+  }
+  return m;
+}
 template <int KPW>
-constexpr bool kOneScaleWord = (4 % KPW) == 0;
+constexpr int kScaleWords = scale_words(KPW);
+static_assert(kScaleWords<4> == 1 && kScaleWords<5> == 2 && kScaleWords<6> == 2 && kScaleWords<7> == 3 &&
+              kScaleWords<8> == 2);
 
 // One wave's slice of one weight unit: NG row groups x KPW k-tiles (packed
 // codes) plus the scale dwords covering those k-tiles.
 template <int NG, int KPW>
 struct WSlice {
   u32x4_t w[KPW][NG];
-  uint32_t sd[NG][2];
+  uint32_t sd[NG][kScaleWords<KPW>];
 };
+// The dword holding k-tile kt's scale in a wave whose range starts at kt0
+// (a select chain: no dynamic register indexing).
+template <int NSW>
+__device__ __forceinline__ uint32_t scale_word(const uint32_t (&sd)[NSW], int kt, int kt0) {
+  const int idx = (kt >> 2) - (kt0 >> 2);
+  uint32_t v = sd[0];
+#pragma unroll
+  for (int j = 1; j < NSW; ++j) v = idx == j ? sd[j] : v;
+  return v;
+}
 
 // Activation formats: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 with E4M3 elements (A8).
 constexpr int kActBf16 = 0, kActFp4 = 1, kActFp8 = 2;
@@ -94,18 +115,17 @@ __device__ __forceinline__ void load_wcodes(WSlice<NG, KPW>& t, __amdgpu_buffer_
 template <int NG, int KPW>
 __device__ __forceinline__ void load_wscales(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rs, uint32_t group_sbytes,
                                              int kt0, int KT) {
-  int q0 = kt0 >> 2;
-  int q1 = (kt0 + KPW - 1) >> 2;
+  const int q0 = kt0 >> 2;
   const int qmax = (KT - 1) >> 2;
-  q0 = q0 < qmax ? q0 : qmax;
-  q1 = q1 < qmax ? q1 : qmax;
   const uint32_t lo = (uint32_t)lane_id() * 4u;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const uint32_t base = gi * group_sbytes + lo;
-    t.sd[gi][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q0 * 256u, 0, kNonTemporal);
-    if constexpr (!kOneScaleWord<KPW>)
-      t.sd[gi][1] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q1 * 256u, 0, kNonTemporal);
+#pragma unroll
+    for (int j = 0; j < kScaleWords<KPW>; ++j) {
+      const int q = q0 + j < qmax ? q0 + j : qmax;
+      t.sd[gi][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q * 256u, 0, kNonTemporal);
+    }
   }
 }
 template <int NG, int KPW>
@@ -185,9 +205,9 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
     const int kt = FULL || kt0 + c < KT ? kt0 + c : KT - 1;
-    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) sc[c][gi] = e8m0_scale_operand((wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu);
+    for (int gi = 0; gi < NG; ++gi)
+      sc[c][gi] = e8m0_scale_operand((scale_word(wt.sd[gi], kt, kt0) >> (8 * (kt & 3))) & 0xFFu);
   }
   refill(-1);
 #pragma unroll
@@ -217,10 +237,9 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
   for (int c = 0; c < KPW; ++c) {
     const bool kin = FULL || kt0 + c < KT;
     const int kt = kin ? kt0 + c : KT - 1;
-    const int which = (kOneScaleWord<KPW> || (kt >> 2) == (kt0 >> 2)) ? 0 : 1;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const uint32_t sb = (wt.sd[gi][which] >> (8 * (kt & 3))) & 0xFFu;
+      const uint32_t sb = (scale_word(wt.sd[gi], kt, kt0) >> (8 * (kt & 3))) & 0xFFu;
       sbyte[c][gi] = kin ? sb : 127u;
     }
   }
@@ -562,7 +581,7 @@ struct Variant {
 
 Variant pick(int64_t K, bool defaults_only = false) {
   const int64_t KT = K / kTileK;
-  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : 8, 1};
+  Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : KT <= 48 ? 6 : KT <= 56 ? 7 : 8, 1};
   if (defaults_only) return v;
   if (const char* env = getenv("MXFP4_MOE_DECODE_VARIANT")) {
     int kpw = 0, d = 0;
@@ -740,6 +759,8 @@ hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int6
   MXMOE_DECODE_VARIANTS(F)
 #undef F
   if (v.kpw == 5) return gate_up_kd<5, 1>(a, route, max_tiles, af, s);
+  if (v.kpw == 6) return gate_up_kd<6, 1>(a, route, max_tiles, af, s);
+  if (v.kpw == 7) return gate_up_kd<7, 1>(a, route, max_tiles, af, s);
   return gate_up_kd<8, 1>(a, route, max_tiles, af, s);
 }
 
@@ -751,6 +772,8 @@ hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool
   MXMOE_DECODE_VARIANTS(F)
 #undef F
   if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, af, ordered, s);
+  if (v.kpw == 6) return down_kd<6, 1>(a, max_tiles, af, ordered, s);
+  if (v.kpw == 7) return down_kd<7, 1>(a, max_tiles, af, ordered, s);
   return down_kd<8, 1>(a, max_tiles, af, ordered, s);
 }
 

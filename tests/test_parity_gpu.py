@@ -47,8 +47,9 @@ SMALL_CASES = {
     "topk32": W.Workload("topk32", 8, 128, 128, 64, 64, 0, 32, seed=7),
     "no_clamp": W.Workload("no_clamp", 32, 512, 256, 8, 8, 0, 2, clamp_limit=float("inf"),
                            seed=8),
-    # K of 56 and 48 k-tiles: the 16-row kernels' 8-k-tiles-per-wave variant;
-    # 256 global experts: the routing kernel path (too many for the fused one)
+    # K of 56 and 48 k-tiles: the 16-row kernels' 7- and 6-k-tiles-per-wave
+    # variants; 256 global experts: the routing kernel path (too many for the
+    # fused one)
     "wide_h_e256": W.Workload("wide_h_e256", 4, 7168, 256, 256, 32, 64, 8, scale_lo=118,
                               scale_hi=124, seed=9),
     "wide_i": W.Workload("wide_i", 8, 256, 6144, 16, 16, 0, 2, scale_lo=118, scale_hi=124,
@@ -59,6 +60,9 @@ A4_CASES = {
     "a4_mid": W.WORKLOADS["a4"].replace(T=512, H=1024, I=512, E_global=16, E_local=16, top_k=4),
     # 32 rows per expert: the 64-row tiles
     "a4_rows32": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=4),
+    # 16-row kernels with 6 (gate_up, 48 k-tiles) and 7 (down, 56 k-tiles)
+    # k-tiles per wave: a wave's scale bytes span up to three dwords
+    "a4_wide": W.WORKLOADS["a4"].replace(T=4, H=6144, I=7168, E_global=4, E_local=4, top_k=2),
 }
 A8_CASES = {
     "a8_tiny": W.WORKLOADS["a8"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
@@ -67,6 +71,8 @@ A8_CASES = {
     "a8_rows32": W.WORKLOADS["a8"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=4),
     # decode dims, routing inside gate_up
     "a8_decode": W.WORKLOADS["a8"].replace(T=16, H=2048, I=1536, E_global=64, E_local=64, top_k=8),
+    # 16-row kernels with 7 (gate_up) and 5 (down) k-tiles per wave
+    "a8_wide": W.WORKLOADS["a8"].replace(T=4, H=7168, I=5120, E_global=4, E_local=4, top_k=2),
 }
 
 
@@ -140,8 +146,12 @@ def _a4_output_checks(case, g, o, token_mask, stats):
     stats.update(compare_out(g, o2, rows=rows))
     keep = np.ones(case.wl.T, bool) if token_mask is None else np.asarray(token_mask, bool).copy()
     keep[np.unique(tok[div])] = False
-    e2e = compare_out(g, o, rows=np.nonzero(keep)[0])
-    stats["end_to_end_max_err_over_rms"] = e2e["max_err_over_rms"]
+    stats["end_to_end_tokens"] = int(keep.sum())
+    # (3) needs a token with no diverged row: with E4M3 over a wide I every
+    # row may differ somewhere, and then (2) is the output check
+    if keep.any() or not case.a8:
+        e2e = compare_out(g, o, rows=np.nonzero(keep)[0])
+        stats["end_to_end_max_err_over_rms"] = e2e["max_err_over_rms"]
 
 
 @pytest.mark.parametrize("name", list(SMALL_CASES))
