@@ -66,20 +66,27 @@ __device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
       }
 }
 
+// (0, the identity of an unsigned maximum, as the DPP source of lanes out of
+// the row -- none here -- lets the compiler fold each step into one v_max_u32
+// with a DPP operand)
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  return ((uint64_t)dpp<CTRL>((uint32_t)(v >> 32)) << 32) | dpp<CTRL>((uint32_t)v);
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true));
 }
-template <int CTRL>
-__device__ __forceinline__ uint64_t max_step_u64(uint64_t v) {
-  const uint64_t o = dpp_u64<CTRL>(v);
-  return o > v ? o : v;
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max_dpp_u32<kDppXor1>(v);
+  v = max_dpp_u32<kDppXor2>(v);
+  v = max_dpp_u32<kDppHalfMirror>(v);
+  return max_dpp_u32<kDppMirror>(v);
 }
-__device__ __forceinline__ uint64_t row16_max_key(uint64_t v) {
-  v = max_step_u64<kDppXor1>(v);
-  v = max_step_u64<kDppXor2>(v);
-  v = max_step_u64<kDppHalfMirror>(v);
-  return max_step_u64<kDppMirror>(v);
+// The row's largest 64-bit key from 32-bit maxima: the largest high word,
+// then the largest low word among the lanes holding it (the same key as a
+// 64-bit maximum, in single-instruction DPP steps).
+__device__ __forceinline__ uint64_t row16_max_key32(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t bh = row16_max_u32(hi);
+  const uint32_t bl = row16_max_u32(hi == bh ? lo : 0u);
+  return ((uint64_t)bh << 32) | bl;
 }
 
 // Top-k of token t by the 16-lane row of this lane.  lexp_out[s - slot_base]
@@ -104,7 +111,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
   sort_desc<VPL>(key);
   uint64_t p0 = 0, p1 = 0, mx = 0;  // picks r and r + 16, first pick
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = row16_max_key(key[0]);
+    const uint64_t best = row16_max_key32(key[0]);
     const bool pop = key[0] == best;
 #pragma unroll
     for (int i = 0; i + 1 < VPL; ++i) key[i] = pop ? key[i + 1] : key[i];
@@ -223,6 +230,43 @@ __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, b
                                   int32_t* offs_lds, int32_t* t1_lds, int4* tiles_lds = nullptr) {
   const int lane = lane_id();
   const int mt1 = a.mt1, mt2 = a.mt2;
+  if (n <= 64 && ((mt1 & (mt1 - 1)) | (mt2 & (mt2 - 1))) == 0) {
+    // one expert per lane, tile counts by shifts (power-of-two tile heights)
+    const int sh1 = __builtin_ctz((unsigned)mt1), sh2 = __builtin_ctz((unsigned)mt2);
+    const bool in = lane < n;
+    const int32_t c = in ? v[lane] : 0;
+    const int32_t ct = in && !bf16_expert(a, lane) ? c : 0;  // rows that get tiles
+    const int32_t n1 = (ct + mt1 - 1) >> sh1, n2 = (ct + mt2 - 1) >> sh2;
+    const int32_t i0 = wave_incl_sum(c), i1 = wave_incl_sum(n1);
+    const int32_t i2 = mt2 == mt1 ? i1 : wave_incl_sum(n2);
+    const int32_t r0 = i0 - c, r1 = i1 - n1, r2 = i2 - n2;
+    if (in) {
+      offs_lds[lane] = r0;
+      t1_lds[lane] = r1;
+      if (tiles_lds)
+        for (int32_t j = 0; j < n1; ++j)
+          tiles_lds[r1 + j] = make_int4(lane, min(ct - (j << sh1), mt1), r0 + (j << sh1), 0);
+      if (write_global) {
+        a.offsets[lane] = r0;
+        a.tile_off1[lane] = r1;
+        a.tile_off2[lane] = r2;
+        for (int32_t j = 0; j < n1; ++j)
+          a.tiles1[r1 + j] = make_int4(lane, min(ct - (j << sh1), mt1), r0 + (j << sh1), 0);
+        for (int32_t j = 0; j < n2; ++j)
+          a.tiles2[r2 + j] = make_int4(lane, min(ct - (j << sh2), mt2), r0 + (j << sh2), 0);
+      }
+    }
+    if (lane == 63) {
+      offs_lds[n] = i0;
+      t1_lds[n] = i1;
+      if (write_global) {
+        a.offsets[n] = i0;
+        a.tile_off1[n] = i1;
+        a.tile_off2[n] = i2;
+      }
+    }
+    return;
+  }
   const int per = (n + 63) / 64;
   const int b = lane * per;
   int32_t s0 = 0, s1 = 0, s2 = 0;
