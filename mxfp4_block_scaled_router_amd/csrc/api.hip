@@ -149,12 +149,16 @@ int64_t max_tiles(const Shape& s, int mt) {
 // ---------------------------------------------------------------- workspace
 struct Layout {
   size_t ids, w, lexp, rank, sorted, inv, chunk_cnt, counts, offsets, tile1, tile2, tiles1, tiles2;
-  size_t pos_tok, pos_w, tile_tok;
+  size_t pos_tok, pos_w, tile_tok, dn_desc;
   size_t act, out32, ybuf, xq, xs, actq, acts;
   size_t total;
 };
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Down workgroups whose share descriptors the workspace holds (16-row plan
+// with the routing inside gate_up; a larger down grid reads the tile table).
+constexpr int kMaxDownDesc = 4096;
 
 Layout layout_of(const Shape& s) {
   Layout L;
@@ -178,6 +182,7 @@ Layout layout_of(const Shape& s) {
     L.tiles1 = take(nt * 16);
     L.tiles2 = take(nt * 16);
     L.tile_tok = p.ms == 1 ? take(nt * 16 * 4) : 0;
+    L.dn_desc = p.ms == 1 ? take((size_t)kMaxDownDesc * 32) : 0;
   }
   L.pos_tok = take(S * 4);
   L.pos_w = take(S * 4);
@@ -368,6 +373,23 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.act = at<uint16_t>(ws, L.act);
   g.zero_buf = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.zero_n = s.ordered ? 0 : s.T * s.H;
+  if (fused_route && r.mt1 == r.mt2) {
+    // gate_up's first workgroup writes the down shares (same tile table)
+    GemmArgs gd = g;
+    gd.K = s.I;
+    gd.N = s.H;
+    int grid = 0, fb = 0, cus = 0;
+    float c = 0.f;
+    e = down_ksplit_shares(gd, max_tiles(s, mt), s.af(), s.ordered, &grid, &fb, &cus, &c);
+    if (e != hipSuccess) return hip_fail(e);
+    if (grid > 0 && grid <= kMaxDownDesc) {
+      g.dn_desc = at<int4>(ws, L.dn_desc);
+      g.dn_grid = grid;
+      g.dn_fb = fb;
+      g.dn_cus = cus;
+      g.dn_c = c;
+    }
+  }
   e = plan.ms == 1   ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.af(), stream)
       : plan.ms == 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);

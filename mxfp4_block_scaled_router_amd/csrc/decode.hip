@@ -315,16 +315,19 @@ __device__ __forceinline__ double slot_weight_before(unsigned b, unsigned G, uns
   (void)G;
   return w;
 }
-__device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, int cus = 0, float c = 0.f) {
+__device__ __forceinline__ void share_bounds(int64_t U, unsigned b, unsigned G, int cus, float c, int64_t* ub,
+                                             int64_t* ue) {
   if (cus <= 0 || c == 0.f) {
-    *ub = U * blockIdx.x / gridDim.x;
-    *ue = U * (blockIdx.x + 1) / gridDim.x;
+    *ub = U * b / G;
+    *ue = U * (b + 1) / G;
     return;
   }
-  const unsigned G = gridDim.x, b = blockIdx.x;
   const double tot = slot_weight_before(G, G, cus, c);
   *ub = b == 0 ? 0 : (int64_t)((double)U * (slot_weight_before(b, G, cus, c) / tot));
   *ue = b + 1 == G ? U : (int64_t)((double)U * (slot_weight_before(b + 1, G, cus, c) / tot));
+}
+__device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, int cus = 0, float c = 0.f) {
+  share_bounds(U, blockIdx.x, gridDim.x, cus, c, ub, ue);
 }
 
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
@@ -335,6 +338,10 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, in
 template <int KPW, int D, int AF, bool FULL, bool ROUTE>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteArgs ra) {
   extern __shared__ float red[];  // [2][waves][2][64][4], then (ROUTE) the routing tables
+  // The routing runs at a raised wave priority: the workgroups dispatched
+  // last onto a CU route while the first ones already stream, and at equal
+  // priority the older waves' instructions go first and hold them back.
+  if constexpr (ROUTE) __builtin_amdgcn_s_setprio(3);
   if (a.zero_buf) {
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -356,7 +363,27 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     const int64_t bound = (ra.E_local < S ? ra.E_local : S) + S / 16;
     rl = route_lds(reinterpret_cast<int32_t*>(red + 2 * NW * 2 * 64 * 4), S, ra.E_local, bound);
     route_block<kFusedRouteMaxVpl>(ra, rl, blockIdx.x == 0);
+    __builtin_amdgcn_s_setprio(0);
     ntiles = __builtin_amdgcn_readfirstlane(rl.t1[ra.E_local]);
+    if (blockIdx.x == 0 && a.dn_desc) {
+      // the down kernel's shares and first tiles (its tile table is this one)
+      const int64_t Ud = (int64_t)ntiles * a.dn_fb;
+      for (int b = threadIdx.x; b < a.dn_grid; b += blockDim.x) {
+        int64_t dub, due;
+        share_bounds(Ud, (unsigned)b, (unsigned)a.dn_grid, a.dn_cus, a.dn_c, &dub, &due);
+        int4 d0 = make_int4((int)dub, (int)due, 0, 0), d1 = make_int4(0, 0, 0, 0);
+        if (dub < due) {
+          const int t = (int)(dub / a.dn_fb);
+          const int4 ti = rl.tiles[t];
+          d0.z = ti.x;
+          d0.w = ti.y;
+          d1.x = ti.z;
+          d1.y = t;
+        }
+        a.dn_desc[2 * b] = d0;
+        a.dn_desc[2 * b + 1] = d1;
+      }
+    }
   } else {
     ntiles = tile_count(a);
   }
@@ -469,7 +496,16 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   const int kt0 = wave * KPW;
   const int FB = (int)(H / (16 * NG));
   int64_t ub, ue;
-  share_of((int64_t)tile_count(a) * FB, &ub, &ue, a.slot_cus, a.slot_c);
+  int4 first = make_int4(0, 0, 0, 0);  // with descriptors: the first segment's tile entry
+  const bool desc = a.dn_desc && (int)gridDim.x == a.dn_grid;
+  if (desc) {
+    const_i32* dp = (const_i32*)a.dn_desc + 8 * (int64_t)blockIdx.x;
+    ub = dp[0];
+    ue = dp[1];
+    first = make_int4(dp[2], dp[3], dp[4], 0);
+  } else {
+    share_of((int64_t)tile_count(a) * FB, &ub, &ue, a.slot_cus, a.slot_c);
+  }
   const uint32_t gbytes = (uint32_t)(16 * (I / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(I) * 256);
   const int64_t cpe = codes_per_expert(H, I), spe = scales_per_expert(H, I);
@@ -480,7 +516,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   for (int64_t sb = ub; sb < ue;) {
     const int t = (int)(sb / FB);
     const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
-    const int4 ti = tile_entry(a, t);
+    const int4 ti = desc && sb == ub ? first : tile_entry(a, t);
     const int rows = ti.y;
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
@@ -706,8 +742,14 @@ hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, 
                        : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, false>, nw, lds, mu, s, a, none);
 }
 
+// Share parameters of a down launch (down_ksplit_shares).
+struct DownShares {
+  int grid, fb, cus;
+  float c;
+};
+
 template <int KPW, int D, int AF, bool ORDERED>
-hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
+hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s, DownShares* q = nullptr) {
   GemmArgs a = a0;
   static const float c_dn = slot_c("MXFP4_MOE_SLOT_C_DN", 0.10f);
   a.slot_c = c_dn;
@@ -718,11 +760,20 @@ hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s) {
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 16 / NG);
   const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
-  return KT % KPW == 0
-             ? launch_persistent_capped(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>, nw, lds, mu, kDownWgsPerCu,
-                                        s, a)
-             : launch_persistent_capped(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>, nw, lds, mu, kDownWgsPerCu,
-                                        s, a);
+  auto go = [&](auto kernel) -> hipError_t {
+    if (!q) return launch_persistent_capped(kernel, nw, lds, mu, kDownWgsPerCu, s, a);
+    // the grid launch_persistent_capped takes
+    int grid = 0;
+    const hipError_t e = resident_grid(reinterpret_cast<const void*>(kernel), nw * 64, lds, &grid, kDownWgsPerCu);
+    if (e != hipSuccess) return e;
+    q->grid = (int64_t)grid > mu ? (int)mu : grid;
+    q->fb = (int)(a.N / 16 / NG);
+    q->cus = a.slot_cus;
+    q->c = a.slot_c;
+    return hipSuccess;
+  };
+  return KT % KPW == 0 ? go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>)
+                       : go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>);
 }
 
 template <int KPW, int D>
@@ -734,17 +785,20 @@ hipError_t gate_up_kd(const GemmArgs& a, const RouteArgs* r, int64_t max_tiles, 
   return af == kActFp4 ? gate_up_v<KPW, D, kActFp4>(a, r, max_tiles, s) : gate_up_v<KPW, D, kActBf16>(a, r, max_tiles, s);
 }
 template <int KPW, int D>
-hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
+hipError_t down_kd(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s,
+                   DownShares* q = nullptr) {
   if (af == kActFp8) {
-    // A8 comes only in the default variants (KPW 4, 5 or 8 with one unit ahead)
+    // A8 comes only in the default variants (KPW 4, 5 or more with one unit ahead)
     if constexpr (KPW >= 4 && D == 1)
-      return ordered ? down_v<KPW, D, kActFp8, true>(a, max_tiles, s)
-                     : down_v<KPW, D, kActFp8, false>(a, max_tiles, s);
+      return ordered ? down_v<KPW, D, kActFp8, true>(a, max_tiles, s, q)
+                     : down_v<KPW, D, kActFp8, false>(a, max_tiles, s, q);
     return hipErrorInvalidValue;
   }
   if (af == kActFp4)
-    return ordered ? down_v<KPW, D, kActFp4, true>(a, max_tiles, s) : down_v<KPW, D, kActFp4, false>(a, max_tiles, s);
-  return ordered ? down_v<KPW, D, kActBf16, true>(a, max_tiles, s) : down_v<KPW, D, kActBf16, false>(a, max_tiles, s);
+    return ordered ? down_v<KPW, D, kActFp4, true>(a, max_tiles, s, q)
+                   : down_v<KPW, D, kActFp4, false>(a, max_tiles, s, q);
+  return ordered ? down_v<KPW, D, kActBf16, true>(a, max_tiles, s, q)
+                 : down_v<KPW, D, kActBf16, false>(a, max_tiles, s, q);
 }
 }  // namespace
 
@@ -764,17 +818,35 @@ hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int6
   return gate_up_kd<8, 1>(a, route, max_tiles, af, s);
 }
 
-hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
-  if (max_tiles <= 0) return hipSuccess;
+namespace {
+hipError_t down_dispatch(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s,
+                         DownShares* q) {
   const Variant v = pick(a.K, af == kActFp8);
 #define F(KPW, D) \
-  if (v.kpw == KPW && v.d == D) return down_kd<KPW, D>(a, max_tiles, af, ordered, s);
+  if (v.kpw == KPW && v.d == D) return down_kd<KPW, D>(a, max_tiles, af, ordered, s, q);
   MXMOE_DECODE_VARIANTS(F)
 #undef F
-  if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, af, ordered, s);
-  if (v.kpw == 6) return down_kd<6, 1>(a, max_tiles, af, ordered, s);
-  if (v.kpw == 7) return down_kd<7, 1>(a, max_tiles, af, ordered, s);
-  return down_kd<8, 1>(a, max_tiles, af, ordered, s);
+  if (v.kpw == 5) return down_kd<5, 1>(a, max_tiles, af, ordered, s, q);
+  if (v.kpw == 6) return down_kd<6, 1>(a, max_tiles, af, ordered, s, q);
+  if (v.kpw == 7) return down_kd<7, 1>(a, max_tiles, af, ordered, s, q);
+  return down_kd<8, 1>(a, max_tiles, af, ordered, s, q);
+}
+}  // namespace
+
+hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  return down_dispatch(a, max_tiles, af, ordered, s, nullptr);
+}
+
+hipError_t down_ksplit_shares(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, int* grid, int* fb,
+                              int* cus, float* c) {
+  DownShares q{0, 0, 0, 0.f};
+  const hipError_t e = max_tiles > 0 ? down_dispatch(a, max_tiles, af, ordered, nullptr, &q) : hipSuccess;
+  *grid = q.grid;
+  *fb = q.fb;
+  *cus = q.cus;
+  *c = q.c;
+  return e;
 }
 
 }  // namespace mxmoe

@@ -77,6 +77,14 @@ struct GemmArgs {
   // 16-row kernels: shares weighted by dispatch slot (set by the launcher)
   int32_t slot_cus;
   float slot_c;
+  // 16-row kernels with the routing inside gate_up: per down workgroup b,
+  // desc[2b] = {first unit, end unit, expert, rows} and desc[2b+1] = {first
+  // sorted position, tile, 0, 0} of its share, written by gate_up's first
+  // workgroup from the routing it holds and read by down in place of the tile
+  // count and first tile entry (two dependent loads).  Null: not used.
+  int4* dn_desc;
+  int32_t dn_grid, dn_fb, dn_cus;  // gate_up side: down's grid, units per tile, slot CUs
+  float dn_c;                      // and slot weight
 };
 
 // Experts kept in bf16 (per-expert exclusions): weights [n][N][K] bf16, the
@@ -153,6 +161,10 @@ hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int6
 // 128-token x 256-weight-row tiles, LDS ring fed by global->LDS copies (tile.hip)
 hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t stream);
 hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t stream);
+// The grid and share parameters launch_down_ksplit will use for these
+// arguments (for the gate_up side of dn_desc).
+hipError_t down_ksplit_shares(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, int* grid, int* fb,
+                              int* cus, float* c);
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);
