@@ -484,11 +484,15 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(CombineArgs a) {
     w[j] = ((c_f32*)a.route_w)[s];
   }
   const int64_t H = a.H;
+  // two column chunks in flight per thread; the rows are read once
+  // (non-temporal loads)
+#pragma unroll 2
   for (int64_t c = threadIdx.x * 4; c < H; c += 4 * blockDim.x) {
     f32x4_t y[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      y[j] = *reinterpret_cast<const f32x4_t*>(a.ybuf + (int64_t)(pos[j] >= 0 ? pos[j] : 0) * H + c);
+      y[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(a.ybuf + (int64_t)(pos[j] >= 0 ? pos[j] : 0) * H + c));
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
