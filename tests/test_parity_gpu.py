@@ -167,6 +167,20 @@ def test_forward_deterministic(name):
     np.testing.assert_array_equal(bits_of(g1["out"]), bits_of(g2["out"]))
 
 
+@pytest.mark.parametrize("name", ["decode", "verify_b1", "tiny"])
+def test_fused_routing_matches_routing_kernel(name, monkeypatch):
+    """Decode shapes route inside gate_up, whose first workgroup also writes the
+    down kernel's shares and first tiles; with the separate routing kernel
+    (down then reads the tile table itself) the ordered layer gives the same
+    bits, act and out."""
+    case = Case(W.WORKLOADS[name], deterministic=True)
+    fused = case.run_gpu(debug=True)
+    monkeypatch.setenv("MXFP4_MOE_ROUTE_KERNEL", "1")
+    separate = case.run_gpu(debug=True)
+    for k in ("act", "out"):
+        np.testing.assert_array_equal(bits_of(fused[k]), bits_of(separate[k]))
+
+
 @pytest.mark.parametrize("name", list(A4_CASES))
 def test_forward_a4(name):
     case = Case(A4_CASES[name])
