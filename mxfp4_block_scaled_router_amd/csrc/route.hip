@@ -33,10 +33,11 @@ __global__ __launch_bounds__(512) void route_small_kernel(RouteArgs a) {
 }
 
 // ---- routing for larger T*k*E, in three kernels
-// (1) top-k and chunk ranks: a workgroup of 256 threads (16 rows of 16 lanes)
-// takes `tpb` tokens, tpb*k a multiple of 64, so its slots are whole chunks.
-// Chunk counts are stored expert-major, chunk_cnt[e][chunk].
-__global__ __launch_bounds__(256) void route_topk_chunk_kernel(RouteArgs a, int tpb) {
+// (1) top-k and chunk ranks: a workgroup takes `tpb` tokens, tpb*k a multiple
+// of 64, so its slots are whole chunks; 256 threads (16 rows of 16 lanes, one
+// token per row) or, with more than 64 experts, one wave per token
+// (topk_wave).  Chunk counts are stored expert-major, chunk_cnt[e][chunk].
+__global__ __launch_bounds__(1024) void route_topk_chunk_kernel(RouteArgs a, int tpb) {
   extern __shared__ int32_t lds[];
   const int wave = threadIdx.x / 64;
   const int E = a.E_local, k = a.top_k;
@@ -53,8 +54,13 @@ __global__ __launch_bounds__(256) void route_topk_chunk_kernel(RouteArgs a, int 
     if (c < nchunk) a.chunk_cnt[(i / nch) * nchunk + c] = 0;
   }
   __syncthreads();
-  for (int64_t t = t0 + threadIdx.x / 16; t < t0 + tpb && t < a.T; t += blockDim.x / 16)
-    topk_any(a, t, lexp, nullptr, s0);
+  if (a.E_global > 64) {
+    for (int64_t t = t0 + wave; t < t0 + tpb && t < a.T; t += blockDim.x / 64)
+      topk_wave_any(a, t, lexp, nullptr, s0);
+  } else {
+    for (int64_t t = t0 + threadIdx.x / 16; t < t0 + tpb && t < a.T; t += blockDim.x / 16)
+      topk_any(a, t, lexp, nullptr, s0);
+  }
   __syncthreads();
   const int nbits = 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1));
   for (int c = wave; c < nch; c += blockDim.x / 64) {
@@ -144,7 +150,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   int64_t tpb = unit;
   while (tpb < 16) tpb += unit;
   const int64_t nblk = (a.T + tpb - 1) / tpb;
-  hipLaunchKernelGGL(route_topk_chunk_kernel, dim3((unsigned)nblk), dim3(256),
+  // more than 64 experts: one wave per token, up to 16 waves
+  const int64_t threads = a.E_global > 64 ? (tpb < 16 ? tpb : 16) * 64 : 256;
+  hipLaunchKernelGGL(route_topk_chunk_kernel, dim3((unsigned)nblk), dim3((unsigned)(threads < 256 ? 256 : threads)),
                      (size_t)(tpb * a.top_k) * sizeof(int32_t), stream, a, (int)tpb);
   hipLaunchKernelGGL(route_chunk_scan_kernel, dim3((unsigned)((a.E_local + 3) / 4)), dim3(256), 0, stream, a);
   const int64_t nscatter = (S + 255) / 256 < 1024 ? (S + 255) / 256 : 1024;

@@ -162,6 +162,95 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
   }
 }
 
+// Whole-wave reductions: the 16-lane row reduction, then the four row results
+// combined in scalar registers (wave-uniform results).  Every lane active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max_u32(v);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+__device__ __forceinline__ uint64_t wave_max_key32(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t bh = wave_max_u32(hi);
+  const uint32_t bl = wave_max_u32(hi == bh ? lo : 0u);
+  return ((uint64_t)bh << 32) | bl;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, l), hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = row16_sum_f64(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Top-k of token t by a whole wave, lane l holding logits l, l + 64, ...: with
+// many experts the per-lane sort and the per-round shifts are four times
+// shorter than with one 16-lane row per token.  Same keys, same picks and the
+// same fp64 weights as topk_row (the fp64 sum is taken in another order).
+// Every lane of the wave must call it for the same t.
+template <int VPL>
+__device__ void topk_wave(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
+                          bool write_global) {
+  const int l = lane_id();
+  const int E = a.E_global, k = a.picks;
+  const float* row = a.logits + t * (int64_t)E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = l + 64 * i;
+    const bool in = e < E;
+    const float v = in ? row[e] : 0.0f;
+    key[i] = in ? ((uint64_t)orderable(v) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  sort_desc<VPL>(key);
+  uint64_t p = 0, mx = 0;  // pick l, first pick
+  for (int j = 0; j < k; ++j) {
+    const uint64_t best = wave_max_key32(key[0]);
+    const bool pop = key[0] == best;
+#pragma unroll
+    for (int i = 0; i + 1 < VPL; ++i) key[i] = pop ? key[i + 1] : key[i];
+    key[VPL - 1] = pop ? 0ull : key[VPL - 1];
+    if (j == 0) mx = best;
+    if (j == l) p = best;
+  }
+  const double m = (double)from_orderable((uint32_t)(mx >> 32));
+  const bool has = l < k;
+  const double e0 = has ? exp((double)from_orderable((uint32_t)(p >> 32)) - m) : 0.0;
+  const double sum = wave_sum_f64(e0);
+  const int64_t s0 = t * a.top_k;  // slots per token (picks + shared)
+  if (has) {
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)p);
+    const float w = (float)(e0 / sum);
+    if (write_global) {
+      a.ids[s0 + l] = id;
+      a.w[s0 + l] = w;
+    }
+    if (w_out) w_out[s0 + l - slot_base] = w;
+    const int le = id - a.first_local;
+    lexp_out[s0 + l - slot_base] = (le >= 0 && le < a.E_route) ? le : -1;
+  }
+  // shared expert: the slot after the picks, table expert E_route, weight 1
+  if (a.top_k > k && l == 0) {
+    if (write_global) {
+      a.ids[s0 + k] = E;
+      a.w[s0 + k] = 1.0f;
+    }
+    if (w_out) w_out[s0 + k - slot_base] = 1.0f;
+    lexp_out[s0 + k - slot_base] = a.E_route;
+  }
+}
+__device__ void topk_wave_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
+                              bool write_global = true) {
+  const int vpl = (a.E_global + 63) / 64;
+  if (vpl <= 1) topk_wave<1>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (vpl <= 2) topk_wave<2>(a, t, lexp_out, w_out, slot_base, write_global);
+  else if (vpl <= 4) topk_wave<4>(a, t, lexp_out, w_out, slot_base, write_global);
+  else topk_wave<8>(a, t, lexp_out, w_out, slot_base, write_global);
+}
+
 // MAXVPL: largest logits-per-lane variant compiled in (E_global <= 16 MAXVPL)
 template <int MAXVPL = 32>
 __device__ void topk_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,

@@ -347,7 +347,10 @@ def test_forward_a4_full_sampled():
 
 
 def test_route_tables_full_sizes():
-    for name in ("decode", "ep_share", "prefill", "a4"):
+    """Routing tables at full sizes against the oracle: the one-workgroup
+    routing (decode), the three routing kernels at mid sizes (ep_share, verify
+    batches 16 and 48) and at prefill sizes."""
+    for name in ("decode", "ep_share", "verify_b16", "verify_b48", "prefill", "a4"):
         wl = W.WORKLOADS[name]
         inp = W.make_inputs(wl, weights=False)
         dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local)
