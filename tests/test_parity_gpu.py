@@ -350,8 +350,15 @@ def test_route_tables_full_sizes():
     """Routing tables at full sizes against the oracle: the one-workgroup
     routing (decode), the three routing kernels at mid sizes (ep_share, verify
     batches 16 and 48) and at prefill sizes."""
-    for name in ("decode", "ep_share", "verify_b16", "verify_b48", "prefill", "a4"):
-        wl = W.WORKLOADS[name]
+    extra = {
+        # the chunked kernels with a wave per token: 24 picks of 128 experts
+        # (two logits per lane, picks past 16), and 512 experts (eight per lane)
+        "e128_k24": W.Workload("e128_k24", 64, 256, 128, 128, 32, 96, 24, seed=61),
+        "e512_k4": W.Workload("e512_k4", 48, 256, 128, 512, 64, 0, 4, seed=62),
+    }
+    for name in ("decode", "ep_share", "verify_b16", "verify_b48", "prefill", "a4", "e128_k24",
+                 "e512_k4"):
+        wl = extra[name] if name in extra else W.WORKLOADS[name]
         inp = W.make_inputs(wl, weights=False)
         dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local)
         log("route %s" % name)
