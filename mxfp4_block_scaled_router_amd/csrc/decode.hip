@@ -357,12 +357,17 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
   const int kt0 = wave * KPW;
   const int FB = (int)(I / 16);
   RouteLds rl;
+  uint32_t* tmask = nullptr;  // with route_block_masks: each local expert's token mask
   int ntiles;
   if constexpr (ROUTE) {
     const int64_t S = ra.T * (int64_t)ra.top_k;
     const int64_t bound = (ra.E_local < S ? ra.E_local : S) + S / 16;
     rl = route_lds(reinterpret_cast<int32_t*>(red + 2 * NW * 2 * 64 * 4), S, ra.E_local, bound);
-    route_block<kFusedRouteMaxVpl>(ra, rl, blockIdx.x == 0);
+    tmask = reinterpret_cast<uint32_t*>(rl.cnt);  // [E_local] (the chunk counts' space)
+    if (masks_route_ok(ra))
+      route_block_masks<kFusedRouteMaxVpl>(ra, rl, tmask, blockIdx.x == 0);
+    else
+      route_block<kFusedRouteMaxVpl>(ra, rl, blockIdx.x == 0);
     __builtin_amdgcn_s_setprio(0);
     ntiles = __builtin_amdgcn_readfirstlane(rl.t1[ra.E_local]);
     if (blockIdx.x == 0 && a.dn_desc) {
@@ -426,9 +431,15 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     // this lane's tile row and its token (garbage past the tile's rows: unused)
     const bool valid = r < rows;
     int32_t tok_raw;
-    if constexpr (ROUTE)
-      tok_raw = rl.ptok[p0 + (valid ? r : 0)];
-    else
+    if constexpr (ROUTE) {
+      if (masks_route_ok(ra)) {
+        // row r of the tile: token bit (p0 - offs[e]) + r of the expert's mask
+        const int e = ti.x;
+        tok_raw = valid ? nth_set_bit32(tmask[e], (int)(p0 - rl.offs[e]) + r) : 0;
+      } else {
+        tok_raw = rl.ptok[p0 + (valid ? r : 0)];
+      }
+    } else
       tok_raw = a.tile_tok[(int64_t)t * 16 + r];
     const int64_t tok = valid ? tok_raw : 0;
     ASlice<KPW, AF> at;

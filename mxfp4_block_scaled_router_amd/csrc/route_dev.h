@@ -472,6 +472,108 @@ __device__ __forceinline__ void lds_barrier() {
 // whole workgroup.  MAXVPL: as in topk_any.  The barriers after the top-k
 // wait only for LDS traffic (nothing here reads global memory written inside
 // the routing), so the global table stores stay in flight across them.
+// Position of the n-th set bit of m (n < popcount(m)): a five-step binary
+// search on popcounts, the same instructions on every lane.
+__device__ __forceinline__ int nth_set_bit32(uint32_t m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int sh = 16; sh >= 1; sh >>= 1) {
+    const uint32_t lo = m & ((1u << sh) - 1u);
+    const int c = __builtin_popcount(lo);
+    const bool up = n >= c;
+    n = up ? n - c : n;
+    m = up ? m >> sh : lo;
+    pos = up ? pos + sh : pos;
+  }
+  return pos;
+}
+
+// Whether route_block_masks applies: at most 32 tokens (a token mask per
+// expert fits 32 bits), at most 64 local experts (one lane each), no experts
+// kept in bf16.
+__device__ __forceinline__ bool masks_route_ok(const RouteArgs& a) {
+  return a.T <= 32 && a.E_local <= 64 && !a.xmap && ((a.mt1 & (a.mt1 - 1)) | (a.mt2 & (a.mt2 - 1))) == 0;
+}
+
+// The routing of route_block for few tokens, from a token mask per local
+// expert instead of chunk ranks: a token picks an expert at most once, so the
+// expert's rows in slot order are its tokens in increasing order, a slot's rank
+// is the popcount of the mask below its token, and counts, offsets and tile
+// offsets follow from one wave's popcounts and prefix sums (power-of-two tile
+// heights).  Fills L.offs,
+// L.t1, L.counts, L.tiles and tmask[E_local] (LDS; the token of row r of an
+// expert's tile j is bit 16 j + r of its mask, nth_set_bit32); no L.ptok.  With
+// write_global the workgroup also writes every global routing table, as
+// route_block does.  Ends with the LDS results visible to the workgroup.
+template <int MAXVPL = 32>
+__device__ void route_block_masks(const RouteArgs& a, const RouteLds& L, uint32_t* tmask, bool write_global) {
+  const int nwaves = blockDim.x / 64;
+  const int wave = threadIdx.x / 64, lane = lane_id();
+  const int64_t S = a.T * (int64_t)a.top_k;
+  const int E = a.E_local, k = a.top_k;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
+  for (int64_t t = wave * 4 + (lane >> 4); t < a.T; t += nwaves * 4)
+    topk_any<MAXVPL>(a, t, L.lexp, L.wl, 0, write_global);
+  lds_barrier();
+  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = L.lexp[s];
+    if (e >= 0) atomicOr(&tmask[e], 1u << (int)(s / k));
+  }
+  lds_barrier();
+  if (wave == 0) {
+    const int mt1 = a.mt1, mt2 = a.mt2;
+    const int sh1 = __builtin_ctz((unsigned)mt1), sh2 = __builtin_ctz((unsigned)mt2);
+    const bool in = lane < E;
+    const uint32_t m = in ? tmask[lane] : 0u;
+    const int32_t c = __builtin_popcount(m);
+    const int32_t n1 = (c + mt1 - 1) >> sh1, n2 = (c + mt2 - 1) >> sh2;
+    const int32_t i0 = wave_incl_sum(c), i1 = wave_incl_sum(n1);
+    const int32_t i2 = mt2 == mt1 ? i1 : wave_incl_sum(n2);
+    const int32_t p0 = i0 - c, r1 = i1 - n1, r2 = i2 - n2;
+    if (in) {
+      L.counts[lane] = c;
+      L.offs[lane] = p0;
+      L.t1[lane] = r1;
+      for (int32_t j = 0; j < n1; ++j)
+        L.tiles[r1 + j] = make_int4(lane, min(c - (j << sh1), mt1), p0 + (j << sh1), 0);
+      if (write_global) {
+        a.counts[lane] = c;
+        a.offsets[lane] = p0;
+        a.tile_off1[lane] = r1;
+        a.tile_off2[lane] = r2;
+        for (int32_t j = 0; j < n1; ++j)
+          a.tiles1[r1 + j] = make_int4(lane, min(c - (j << sh1), mt1), p0 + (j << sh1), 0);
+        for (int32_t j = 0; j < n2; ++j)
+          a.tiles2[r2 + j] = make_int4(lane, min(c - (j << sh2), mt2), p0 + (j << sh2), 0);
+      }
+    }
+    if (lane == 63) {
+      L.offs[E] = i0;
+      L.t1[E] = i1;
+      if (write_global) {
+        a.offsets[E] = i0;
+        a.tile_off1[E] = i1;
+        a.tile_off2[E] = i2;
+      }
+    }
+  }
+  lds_barrier();
+  if (write_global) {
+    // the permutation and the per-position tables: slot s of token t on
+    // expert e sits at offs[e] + popcount(mask_e below t)
+    for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
+      const int e = L.lexp[s];
+      if (e >= 0) {
+        const int t = (int)(s / k);
+        const int32_t pos = L.offs[e] + __builtin_popcount(tmask[e] & ((1u << t) - 1u));
+        place_slot(a, s, pos, L.wl[s], e, L.offs[e], L.t1[e]);
+      } else {
+        a.inv[s] = -1;
+      }
+    }
+  }
+}
+
 template <int MAXVPL = 32>
 __device__ void route_block(const RouteArgs& a, const RouteLds& L, bool write_global) {
   const int nwaves = blockDim.x / 64;
