@@ -332,9 +332,11 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, in
 
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
 // up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
-// ROUTE: every workgroup first routes the tokens itself (route_block, tables in
-// LDS after the partial buffers; workgroup 0 also writes the global tables that
-// the down and combine kernels read), so no routing kernel runs before this one.
+// ROUTE: every workgroup first routes the tokens itself (route_block_masks, or
+// route_block past 32 tokens or 64 local experts; tables in LDS after the
+// partial buffers; workgroup 0 also writes the global tables that the down and
+// combine kernels read, and with dn_desc the down shares), so no routing kernel
+// runs before this one.
 template <int KPW, int D, int AF, bool FULL, bool ROUTE>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteArgs ra) {
   extern __shared__ float red[];  // [2][waves][2][64][4], then (ROUTE) the routing tables
