@@ -54,6 +54,12 @@ SMALL_CASES = {
                               scale_hi=124, seed=9),
     "wide_i": W.Workload("wide_i", 8, 256, 6144, 16, 16, 0, 2, scale_lo=118, scale_hi=124,
                          seed=10),
+    # the fused routing's token masks at their limits: 32 tokens (mask bit 31)
+    # on 64 local experts, 64 of 128 experts local from expert 32, and 33
+    # tokens (past the fused routing)
+    "masks_T32": W.Workload("masks_T32", 32, 256, 128, 64, 64, 0, 8, seed=11),
+    "masks_ep_T24": W.Workload("masks_ep_T24", 24, 256, 128, 128, 64, 32, 4, seed=12),
+    "T33": W.Workload("T33", 33, 256, 128, 64, 64, 0, 8, seed=13),
 }
 A4_CASES = {
     "a4_tiny": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
