@@ -144,9 +144,11 @@ def cpu_baseline(wl, inp, target_s, shared=False):
     t_probe = run(mask)
     per_tok = t_probe / n_probe
     if per_tok * wl.T <= target_s:
-        reps = max(1, int(target_s / max(per_tok * wl.T, 1e-6)))
-        reps = min(reps, 50)
-        t = sum(run(None) for _ in range(reps))
+        # one full step sizes the rest (a full step touches more experts than
+        # the probe, so the probe's per-token time overestimates it)
+        t = run(None)
+        reps = min(50, max(1, int(target_s / max(t, 1e-6))))
+        t += sum(run(None) for _ in range(reps - 1))
         return {"value": wl.T * reps / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                 "sample": "%d full steps of the %s workload (%d tokens each), %.1f s" %
                 (reps, wl.name, wl.T, t)}
