@@ -53,7 +53,7 @@ def parse():
                     help="keep this many experts (evenly spaced) in bf16 inside fused buffers; "
                          "times the whole step only (no phase split, roofline null)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
