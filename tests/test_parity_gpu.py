@@ -165,7 +165,7 @@ def test_forward_small(name):
     _check_case(Case(SMALL_CASES[name]))
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid_lds", "prefill_small"])
+@pytest.mark.parametrize("name", ["tiny", "decode_T5_H256", "mid_lds", "prefill_small"])
 def test_forward_deterministic(name):
     case = Case(SMALL_CASES[name], deterministic=True)
     g1, o = _check_case(case)
@@ -225,6 +225,9 @@ SHARED_CASES = {
     "prefill_small": (SMALL_CASES["prefill_small"], {}),          # 128-row tiles
     "a4_tiny": (A4_CASES["a4_tiny"], {}),
     "a4_mid": (A4_CASES["a4_mid"], {}),
+    # few tokens: the fused routing's token masks with the shared slot, A4 / A8
+    "a4_wide": (A4_CASES["a4_wide"], {}),
+    "a8_decode_det": (A8_CASES["a8_decode"], {"deterministic": True}),
 }
 
 
