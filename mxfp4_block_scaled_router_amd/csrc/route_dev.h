@@ -91,12 +91,13 @@ __device__ __forceinline__ uint64_t row16_max_key32(uint64_t v) {
 
 // Top-k of token t by the 16-lane row of this lane.  lexp_out[s - slot_base]
 // receives the local expert (or -1) of each of the token's k slots s; with
-// write_global the ids and weights also go to a.ids and a.w.
+// write_global the ids and weights also go to a.ids and a.w; tmask (LDS, may
+// be null) gets bit t set in the entry of each local expert picked.
 // Each lane holds logits r, r + 16, ... as sorted keys; a round takes the
 // row's largest head (16-lane butterfly) and the one lane that holds it pops.
 template <int VPL>
 __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
-                         bool write_global) {
+                         bool write_global, uint32_t* tmask = nullptr) {
   const int r = lane_id() & 15;
   const int E = a.E_global, k = a.picks;
   const float* row = a.logits + t * (int64_t)E;
@@ -139,6 +140,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
     if (w_out) w_out[s0 + r - slot_base] = w;
     int le = id - a.first_local;
     lexp_out[s0 + r - slot_base] = (le >= 0 && le < a.E_route) ? le : -1;
+    if (tmask && le >= 0 && le < a.E_route) atomicOr(&tmask[le], 1u << (uint32_t)t);
   }
   if (has1) {
     int id = (int)(0xFFFFFFFFu - p1lo);
@@ -150,6 +152,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
     if (w_out) w_out[s0 + r + 16 - slot_base] = w;
     int le = id - a.first_local;
     lexp_out[s0 + r + 16 - slot_base] = (le >= 0 && le < a.E_route) ? le : -1;
+    if (tmask && le >= 0 && le < a.E_route) atomicOr(&tmask[le], 1u << (uint32_t)t);
   }
   // shared expert: the slot after the picks, table expert E_route, weight 1
   if (a.top_k > k && r == 0) {
@@ -159,6 +162,7 @@ __device__ void topk_row(const RouteArgs& a, int64_t t, int32_t* lexp_out, float
     }
     if (w_out) w_out[s0 + k - slot_base] = 1.0f;
     lexp_out[s0 + k - slot_base] = a.E_route;
+    if (tmask) atomicOr(&tmask[a.E_route], 1u << (uint32_t)t);
   }
 }
 
@@ -254,14 +258,14 @@ __device__ void topk_wave_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, 
 // MAXVPL: largest logits-per-lane variant compiled in (E_global <= 16 MAXVPL)
 template <int MAXVPL = 32>
 __device__ void topk_any(const RouteArgs& a, int64_t t, int32_t* lexp_out, float* w_out, int64_t slot_base,
-                         bool write_global = true) {
+                         bool write_global = true, uint32_t* tmask = nullptr) {
   const int vpl = (a.E_global + 15) / 16;
-  if (vpl <= 1) topk_row<1>(a, t, lexp_out, w_out, slot_base, write_global);
-  else if (vpl <= 2) topk_row<2>(a, t, lexp_out, w_out, slot_base, write_global);
-  else if (MAXVPL <= 4 || vpl <= 4) topk_row<4>(a, t, lexp_out, w_out, slot_base, write_global);
-  else if (MAXVPL <= 8 || vpl <= 8) topk_row<8>(a, t, lexp_out, w_out, slot_base, write_global);
-  else if (MAXVPL <= 16 || vpl <= 16) topk_row<16>(a, t, lexp_out, w_out, slot_base, write_global);
-  else topk_row<32>(a, t, lexp_out, w_out, slot_base, write_global);
+  if (vpl <= 1) topk_row<1>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
+  else if (vpl <= 2) topk_row<2>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
+  else if (MAXVPL <= 4 || vpl <= 4) topk_row<4>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
+  else if (MAXVPL <= 8 || vpl <= 8) topk_row<8>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
+  else if (MAXVPL <= 16 || vpl <= 16) topk_row<16>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
+  else topk_row<32>(a, t, lexp_out, w_out, slot_base, write_global, tmask);
 }
 
 // Rank of each slot of chunk c among the chunk's slots with the same local
@@ -511,14 +515,11 @@ __device__ void route_block_masks(const RouteArgs& a, const RouteLds& L, uint32_
   const int wave = threadIdx.x / 64, lane = lane_id();
   const int64_t S = a.T * (int64_t)a.top_k;
   const int E = a.E_local, k = a.top_k;
+  // the masks are zero before any pick is ORed into them
   for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
-  for (int64_t t = wave * 4 + (lane >> 4); t < a.T; t += nwaves * 4)
-    topk_any<MAXVPL>(a, t, L.lexp, L.wl, 0, write_global);
   lds_barrier();
-  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) {
-    const int e = L.lexp[s];
-    if (e >= 0) atomicOr(&tmask[e], 1u << (int)(s / k));
-  }
+  for (int64_t t = wave * 4 + (lane >> 4); t < a.T; t += nwaves * 4)
+    topk_any<MAXVPL>(a, t, L.lexp, L.wl, 0, write_global, tmask);
   lds_barrier();
   if (wave == 0) {
     const int mt1 = a.mt1, mt2 = a.mt2;
