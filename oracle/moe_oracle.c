@@ -190,7 +190,10 @@ static void quantize_block(const double* v, uint8_t* codes4, uint8_t* scale) {
   }
 }
 
+/* The quantisers below treat every row on its own; with many rows they are
+ * spread over OpenMP threads (the same arithmetic on each row). */
 void orc_quantize_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static) if (rows > 64)
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < K / 32; ++b) {
       uint8_t c4[32];
@@ -202,8 +205,9 @@ void orc_quantize_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, 
 }
 
 void orc_quantize_f32(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
-  double blk[32];
+#pragma omp parallel for schedule(static) if (rows > 64)
   for (int64_t r = 0; r < rows; ++r) {
+    double blk[32];
     for (int64_t b = 0; b < K / 32; ++b) {
       for (int i = 0; i < 32; ++i) blk[i] = (double)v[r * K + b * 32 + i];
       uint8_t c4[32];
@@ -216,8 +220,9 @@ void orc_quantize_f32(const float* v, int64_t rows, int64_t K, uint8_t* codes, u
 
 void orc_quantize_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
                        uint8_t* scales) {
-  double blk[32];
+#pragma omp parallel for schedule(static) if (rows > 64)
   for (int64_t r = 0; r < rows; ++r) {
+    double blk[32];
     for (int64_t b = 0; b < K / 32; ++b) {
       for (int i = 0; i < 32; ++i) blk[i] = (double)orc_f32_from_bf16(v[r * K + b * 32 + i]);
       uint8_t c4[32];
@@ -402,15 +407,18 @@ static void quantize8_block(const double* v, uint8_t* codes, uint8_t* scale) {
 
 void orc_quantize8_bf16(const uint16_t* v, int64_t rows, int64_t K, uint8_t* codes,
                         uint8_t* scales) {
-  double blk[32];
-  for (int64_t r = 0; r < rows; ++r)
+#pragma omp parallel for schedule(static) if (rows > 64)
+  for (int64_t r = 0; r < rows; ++r) {
+    double blk[32];
     for (int64_t b = 0; b < K / 32; ++b) {
       for (int i = 0; i < 32; ++i) blk[i] = (double)orc_f32_from_bf16(v[r * K + b * 32 + i]);
       quantize8_block(blk, codes + r * K + b * 32, scales + r * (K / 32) + b);
     }
+  }
 }
 
 void orc_quantize8_f64(const double* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static) if (rows > 64)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t b = 0; b < K / 32; ++b)
       quantize8_block(v + r * K + b * 32, codes + r * K + b * 32, scales + r * (K / 32) + b);

@@ -58,6 +58,7 @@ class Case:
             self.inp.update(zip(("w13", "w13s", "w2", "w2s"), W.make_uniform_weights(wlw)))
         else:
             self.inp = W.make_inputs(wl)
+        self.gpu_canon = None
         if "w13" not in self.inp:
             self._quantise_student_t()
         self.dims = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local,
@@ -73,9 +74,11 @@ class Case:
         if excluded is not None:
             self._load_fused()
         else:
-            canon = [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
+            canon = getattr(self, "gpu_canon", None) or \
+                [to_dev(self.inp[k]) for k in ("w13", "w13s", "w2", "w2s")]
             self.pw = mx.mxfp4_moe_preshuffle(self.dims, *canon)
             del canon
+        self.gpu_canon = None
 
     def _load_fused(self):
         """Experts in self.excluded kept in bf16: both matrices laid out as fused
@@ -106,25 +109,33 @@ class Case:
         return rows
 
     def _quantise_student_t(self):
-        """Student-t weights: drawn on the GPU, quantised there by the library and
-        on the host by the oracle; both codes must agree bit for bit."""
+        """Student-t weights: drawn on the GPU in fp32, quantised there by the
+        library (the load-time step) and, for every expert, on the host by the
+        oracle's own quantiser.  The two codes must agree bit for bit for every
+        expert; the GPU keeps its own codes, the oracle gets its own."""
         wl = self.wl
         E, H, I = wl.E_local + (1 if self.shared else 0), wl.H, wl.I
         w13 = np.empty((E, 2 * I, H // 2), np.uint8)
         w13s = np.empty((E, 2 * I, H // 32), np.uint8)
         w2 = np.empty((E, H, I // 2), np.uint8)
         w2s = np.empty((E, H, I // 32), np.uint8)
+        g13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+        g13s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device="cuda")
+        g2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda")
+        g2s = torch.empty((E, H, I // 32), dtype=torch.uint8, device="cuda")
         self.quant_mismatch = 0
         for e in range(E):
-            for which, (c_arr, s_arr) in (("w13", (w13, w13s)), ("w2", (w2, w2s))):
+            for which, (oc_arr, os_arr), (gc_arr, gs_arr) in (
+                    ("w13", (w13, w13s), (g13, g13s)), ("w2", (w2, w2s), (g2, g2s))):
                 v = W.student_t_expert(wl, e, which, device="cuda")
                 gc, gs = mx.mxfp4_moe_quantize(v)
-                gc, gs = gc.cpu().numpy(), gs.cpu().numpy()
-                if e < 4 or e == E - 1:   # oracle cross-check on a few experts
-                    oc, os_ = oracle.quantize(v.cpu().numpy())
-                    self.quant_mismatch += int((oc != gc).sum() + (os_ != gs).sum())
-                c_arr[e], s_arr[e] = gc, gs
+                gc_arr[e].copy_(gc)
+                gs_arr[e].copy_(gs)
+                oc_arr[e], os_arr[e] = oracle.quantize(v.cpu().numpy())
+                self.quant_mismatch += int((oc_arr[e] != gc.cpu().numpy()).sum() +
+                                           (os_arr[e] != gs.cpu().numpy()).sum())
         self.inp.update(w13=w13, w13s=w13s, w2=w2, w2s=w2s)
+        self.gpu_canon = (g13, g13s, g2, g2s)
 
     def run_gpu(self, debug=True):
         wl = self.wl
@@ -227,10 +238,11 @@ def compare_act(g_act_bits: np.ndarray, o_act_bits: np.ndarray, rows=None,
     return stats
 
 
-def compare_out(g: dict, o, rows=None) -> dict:
+def compare_out(g: dict, o, rows=None, slack=None) -> dict:
     """The layer output, in two parts:
       1. the GPU's fp32 output before its bf16 rounding against the oracle's out32:
-         max |gpu32 - oracle32| <= 2e-2 * rms(oracle32) over the compared rows;
+         |gpu32 - oracle32| <= 2e-2 * rms(oracle32) (+ slack, element by element,
+         where given: float64 [T, H]) over the compared rows;
       2. the GPU's bf16 output is exactly the round-to-nearest-even of its fp32
          output (checked with the oracle's pinned bf16 rounding).
     Also reported, not gated: max |gpu bf16 - oracle32| / rms and the number of
@@ -243,8 +255,18 @@ def compare_out(g: dict, o, rows=None) -> dict:
     finite = np.isfinite(ref)
     np.testing.assert_array_equal(np.isfinite(g32), finite)
     rms = float(np.sqrt(np.mean(ref[finite] ** 2))) if finite.any() else 0.0
-    err = float(np.abs(g32[finite] - ref[finite]).max()) if finite.any() else 0.0
+    d = np.abs(g32 - ref)
+    if slack is not None:
+        sl = sel(slack)
+        stats_slack = float(sl.max() / rms) if rms and sl.size else 0.0
+        over = np.where(finite, d - sl, 0.0)
+        err = float(over.max()) if finite.any() else 0.0
+    else:
+        err = float(d[finite].max()) if finite.any() else 0.0
     stats = {"max_err_over_rms": err / rms if rms else 0.0, "compared": int(ref.size)}
+    if slack is not None:
+        stats["max_slack_over_rms"] = stats_slack
+        stats["max_raw_err_over_rms"] = float(d[finite].max() / rms) if rms else 0.0
     rounded = oracle.bf16_from_f32(np.ascontiguousarray(sel(g["out32"].cpu().numpy())))
     stats["cast_mismatch"] = int((rounded != gb).sum())
     gbf = bf16_to_f32(gb).astype(np.float64)
@@ -255,3 +277,118 @@ def compare_out(g: dict, o, rows=None) -> dict:
     assert err <= TOL_REL_RMS * rms, stats
     assert stats["cast_mismatch"] == 0, stats
     return stats
+
+
+# ---------------------------------------------------------------- A4 / A8 output bound
+
+def _bf16_toward(f: np.ndarray, up: bool) -> np.ndarray:
+    """float32 -> bf16 bits rounded towards +inf (up) or -inf (down)."""
+    f = np.asarray(f, np.float32)
+    b = f.view(np.uint32)
+    t = (b >> 16).astype(np.uint16)
+    exact = (b & 0xFFFF) == 0
+    neg = (b >> 31) == 1
+    # truncation rounds towards zero; one more unit of magnitude goes outward
+    outward = ~exact & (neg != up)
+    return np.where(outward, t + np.uint16(1), t).astype(np.uint16)
+
+
+def _act_candidates(bits: int, tol: float, e_lo: int) -> list:
+    """bf16 values within tol of bits's value, as the bounding set the quantiser
+    needs: the interval's outer bf16 endpoints, the value itself, zero when the
+    interval holds it, and both sides of the powers of two 2^e_lo and
+    2^(e_lo + 1) (where a block's scale changes) inside the interval."""
+    v = float(bf16_to_f32(np.array([bits], np.uint16))[0])
+    lo = float(bf16_to_f32(_bf16_toward(np.float32(v - tol), False).reshape(1))[0])
+    hi = float(bf16_to_f32(_bf16_toward(np.float32(v + tol), True).reshape(1))[0])
+    vals = {lo, v, hi}
+    if lo <= 0.0 <= hi:
+        vals.add(0.0)
+    for e in (e_lo, e_lo + 1):
+        p = 2.0 ** e
+        for c in (p, p * (1.0 - 2.0 ** -8), -p, -p * (1.0 - 2.0 ** -8)):
+            if lo <= c <= hi:
+                vals.add(c)
+    f = np.array(sorted(vals), np.float32)
+    return list((f.view(np.uint32) >> 16).astype(np.uint16))
+
+
+def quant_step_bound(case, o, g_act_bits: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Bound on |layer output - oracle out32| that the A4/A8 quantisation of the
+    SwiGLU output adds where the GPU's bf16 act differs from the oracle's.
+
+    The act comparison holds every GPU act element within one bf16 ulp of the
+    oracle's, or within 2^-9 rms(act) where the gate/up sums cancel.  Such a
+    move can carry the element across a quantisation boundary, and a move of a
+    block's largest element across a power of two changes the block's scale.
+    For each block holding a changed element, every act vector in that
+    tolerance box is represented by the combinations of the changed elements'
+    candidates (_act_candidates: endpoints and scale-change points; at a fixed
+    scale the quantised value is monotone in the input), each quantised and
+    dequantised by the oracle.  D_i = the largest |dequantised value - the
+    oracle's own| over them.  The output bound of token t, column n is
+    sum over its rows p of |w_p| * sum_i D_{p,i} * |W2_e[n, i]|, with W2
+    dequantised by the oracle.  Everything priced comes from the oracle; the
+    GPU's act only says which elements moved.  Zero for a token none of whose
+    act elements differs.  rows: bool [N_assign], the positions to bound."""
+    wl = case.wl
+    n = o.n_assign
+    H, I = wl.H, wl.I
+    k = o.ids.shape[1]
+    B = np.zeros((wl.T, H), np.float64)
+    ga = np.asarray(g_act_bits)[:n]
+    oa = o.act[:n]
+    of = bf16_to_f32(oa)
+    fin = np.isfinite(of)
+    rms = float(np.sqrt(np.mean(of[fin].astype(np.float64) ** 2))) if fin.any() else 0.0
+    abs_tol = rms * 2.0 ** -9
+    changed = (ga != oa) & ~(np.isnan(bf16_to_f32(ga)) & np.isnan(of))
+    rows = rows & ~case.excluded_rows(o) & changed.any(axis=1)
+    if not rows.any():
+        return B
+    a8 = case.a8
+    quant = oracle.quantize8 if a8 else oracle.quantize
+    emax = 448.0 if a8 else 6.0
+    ow = case.oracle_w if case.bx is not None else case.inp
+    w2, w2s = ow["w2"], ow["w2s"]
+
+    def deq(block_bits):                     # [m, 32] bf16 bits -> [m, 32] float64
+        c, sc = quant(np.ascontiguousarray(block_bits))
+        d = oracle.dequant8(c, sc) if a8 else oracle.dequant(c, sc, 32)
+        return d.astype(np.float64)
+
+    for p in np.nonzero(rows)[0]:
+        e = int(np.searchsorted(o.offsets, p, side="right") - 1)
+        t, j = divmod(int(o.sorted[p]), k)
+        wt = abs(float(o.w[t, j]))
+        for b in np.unique(np.nonzero(changed[p])[0] // 32):
+            base = oa[p, 32 * b:32 * b + 32].copy()
+            d0 = deq(base[None])[0]
+            bf = np.abs(bf16_to_f32(base).astype(np.float64))
+            amax = bf[np.isfinite(bf)].max() if np.isfinite(bf).any() else 0.0
+            e_lo = int(np.floor(np.log2(amax))) if amax > 0 else -133
+            idx = np.nonzero(changed[p, 32 * b:32 * b + 32])[0]
+            cands = []
+            for i in idx:
+                v = float(bf16_to_f32(base[i:i + 1])[0])
+                ulp = abs(float(bf16_to_f32(np.array([base[i] + 1], np.uint16))[0]) - v) \
+                    if base[i] & 0x7FFF else 2.0 ** -133
+                cands.append(_act_candidates(int(base[i]), max(ulp, abs_tol), e_lo))
+            ncomb = int(np.prod([len(c) for c in cands]))
+            if ncomb <= 4096:
+                grids = np.meshgrid(*[np.array(c, np.uint16) for c in cands], indexing="ij")
+                blocks = np.repeat(base[None], ncomb, axis=0)
+                for col, gsel in zip(idx, grids):
+                    blocks[:, col] = gsel.reshape(-1)
+                D = np.abs(deq(blocks) - d0[None]).max(axis=0)
+            else:
+                # too many combinations: any element may take any value of the
+                # grid at up to twice the scale
+                D = np.abs(d0) + emax * 2.0 ** (e_lo - (8 if a8 else 2) + 1)
+            nz = np.nonzero(D)[0]
+            if nz.size == 0:
+                continue
+            wcol = oracle.dequant(np.ascontiguousarray(w2[e][:, 16 * b:16 * b + 16]),
+                                  np.ascontiguousarray(w2s[e][:, b:b + 1]), 32).astype(np.float64)
+            B[t] += wt * (np.abs(wcol[:, nz]) @ D[nz])
+    return B

@@ -18,7 +18,7 @@ import oracle
 import mxfp4_block_scaled_router_amd as mx
 from mxfp4_block_scaled_router_amd import workloads as W
 from tests.gpu_helpers import (ACT_EQUAL_MIN, Case, bits_of, compare_act, compare_out,
-                               compare_route, log, to_dev)
+                               compare_route, log, quant_step_bound, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,18 +121,20 @@ def _check_case(case: Case, token_mask=None):
 
 
 def _a4_output_checks(case, g, o, token_mask, stats):
-    """A4 / A8 output parity.  Each side quantises its own SwiGLU output along I,
-    and the two act values may differ by a rounding (the fp32 sums run in
-    another order), so an element near a code boundary, or a block whose
-    largest element sits at a power of two, can get another code or scale byte
-    on the two sides: from there on the down inputs differ by a whole
-    quantisation step.  The quantisation itself is checked above (the GPU's
-    codes equal the oracle's quantiser on the GPU's act).  Here: (1) only rows
-    whose act differs can have other codes, and with E2M1 (a step of a quarter
-    of the block maximum, so a 1-ulp bf16 move rarely crosses it) such rows are
-    rare; (2) the output equals the oracle's down and combine run on the GPU's
-    codes, for every compared token; (3) end to end, for every compared token
-    none of whose rows diverged."""
+    """A4 / A8 output parity, end to end against the oracle's own quantisation
+    for every compared token.  Each side quantises its own SwiGLU output along
+    I; the act comparison holds the GPU's act within a rounding of the
+    oracle's, and an element that moved by a rounding can land on the other
+    side of a quantisation boundary (or move its block's scale), after which
+    the down inputs differ by a whole quantisation step.  The bar is therefore
+    max |gpu32 - oracle out32| <= 2e-2 rms + B, where B (quant_step_bound) is
+    the largest effect those moved elements can have, computed from the
+    oracle's act, quantiser and w2 alone; B is zero for every token none of
+    whose act elements moved.  Also: only rows whose act differs may get other
+    codes, and with E2M1 (a step of a quarter of the block maximum, so a 1-ulp
+    move rarely crosses it) such rows are rare.  The oracle's down and combine
+    run on the GPU's own codes (given_actq) is reported as a diagnostic, not
+    gated on."""
     n = o.n_assign
     gq = np.ascontiguousarray(g["actq"].cpu().numpy()[:n])
     gs = np.ascontiguousarray(g["acts"].cpu().numpy()[:n])
@@ -143,21 +145,22 @@ def _a4_output_checks(case, g, o, token_mask, stats):
     div = ((gq != o.actq[:n]).any(axis=1) | (gs != o.acts[:n]).any(axis=1)) & checked & \
         ~case.excluded_rows(o)
     stats["actq_rows_diverging"] = int(div.sum())
-    act_differs = (bits_of(g["act"])[:n] != o.act[:n]).any(axis=1)
+    gact = bits_of(g["act"])[:n]
+    act_differs = (gact != o.act[:n]).any(axis=1)
     assert not (div & ~act_differs).any(), stats
     if not case.a8:
         assert div.sum() <= max(2, n // 1000), stats
-    o2 = case.run_oracle(token_mask=token_mask, actq_in=gq, acts_in=gs)
+    slack = quant_step_bound(case, o, gact, checked)
     rows = None if token_mask is None else np.nonzero(token_mask)[0]
-    stats.update(compare_out(g, o2, rows=rows))
-    keep = np.ones(case.wl.T, bool) if token_mask is None else np.asarray(token_mask, bool).copy()
-    keep[np.unique(tok[div])] = False
-    stats["end_to_end_tokens"] = int(keep.sum())
-    # (3) needs a token with no diverged row: with E4M3 over a wide I every
-    # row may differ somewhere, and then (2) is the output check
-    if keep.any() or not case.a8:
-        e2e = compare_out(g, o, rows=np.nonzero(keep)[0])
-        stats["end_to_end_max_err_over_rms"] = e2e["max_err_over_rms"]
+    e2e = compare_out(g, o, rows=rows, slack=slack)
+    sel_tok = np.ones(case.wl.T, bool) if token_mask is None else np.asarray(token_mask, bool)
+    stats["end_to_end_tokens"] = int(sel_tok.sum())
+    stats["tokens_with_zero_slack"] = int((sel_tok & ~(slack > 0).any(axis=1)).sum())
+    stats.update({"e2e_" + k: v for k, v in e2e.items()})
+    # diagnostic: the oracle's down + combine on the GPU's codes
+    o2 = case.run_oracle(token_mask=token_mask, actq_in=gq, acts_in=gs)
+    d = compare_out(g, o2, rows=rows, slack=np.full((case.wl.T, case.wl.H), np.inf))
+    stats["diag_given_actq_max_err_over_rms"] = d["max_raw_err_over_rms"]
 
 
 @pytest.mark.parametrize("name", list(SMALL_CASES))
