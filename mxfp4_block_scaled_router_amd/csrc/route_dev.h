@@ -459,12 +459,15 @@ __device__ __forceinline__ RouteLds route_lds(int32_t* base, int64_t S, int64_t 
   return L;
 }
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and
-// scalar) operations, not for its vector-memory loads, which may stay in
-// flight across it.
+// Workgroup barrier for LDS traffic only: a release fence before and an
+// acquire fence after the barrier, both limited to workgroup scope and the
+// LDS address space, so the compiler keeps LDS accesses on their side of it
+// and the hardware waits for this wave's LDS operations (lgkmcnt(0)) but not
+// for its vector-memory loads, which may stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // The whole routing of a.T tokens by one workgroup (any number of waves),
