@@ -2,28 +2,42 @@
 """Benchmark of the MXFP4 routed-expert MoE layer on one MI355X (gfx950).
 
     python bench.py [--steps K] [--warmup W] [--workload decode|tiny|ep_share|prefill|a4|a8|verify_bB]
+    python bench.py --summarize WORKLOAD      (rocprofv3 output -> profiles/, see below)
 
 A step is one whole forward of the layer (route, permutation, gate_up + clamped
 SwiGLU, down + weighted combine, output cast) over one batch of seeded synthetic
 inputs that are resident in HBM before timing starts.  The default workload is
 the decode step (T=16, H=2048, I=1536, 64 experts, top-8).  Expert weights are
 rotated over several copies so that the 256 MB MALL cannot serve a step from the
-previous one.  Prints one JSON line.
+previous one, and the router logits over several batches of tokens, so that
+each step routes afresh.  Exactly K steps are timed between two device
+synchronisations; then R repeats of the same loop give the median and the
+p10-p90 spread.  Prints one JSON line.
 
 Roofline: per-phase durations come from HIP events that the library records
 around its phases on the stream it launches on (mxfp4_moe_forward_timed), in a
-second timed loop.  The dominant phase's achieved rate is its algorithmic
-bytes (or flops) per launch divided by its mean duration.  Algorithmic bytes
-count only the experts the routing touches: each touched expert's packed codes
-plus scale bytes of the matrix the kernel streams, plus the activations it must
-read and write once.
+separate timed loop.  The dominant phase's achieved rate is its algorithmic
+bytes (or flops) per launch divided by its mean duration.  An event pair
+brackets the kernel plus its dispatch latency, so the kernel-only rate from the
+committed rocprofv3 summary of the same workload (profiles/<workload>_kernels.json,
+used only while its source digest matches the sources) is reported beside it.
+Algorithmic bytes count only the experts the routing touches: each touched
+expert's packed codes plus scale bytes of the matrix the kernel streams, plus
+the activations it must read and write once.
 
 cpu_baseline: the CPU oracle (test infrastructure, plain C + OpenMP) timed on a
 bounded sample of the same workload on this host's cores.
+
+--summarize WORKLOAD reads the rocprofv3 CSV output written under
+gpurun_out/prof/WORKLOAD/{stats,fetch,write} (and the copy calibration under
+gpurun_out/prof/calib/{fetch,write}) by the commands printed into the summary,
+and writes profiles/WORKLOAD_kernels.txt and profiles/WORKLOAD_kernels.json.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -37,6 +51,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 METRIC = "MXFP4 MoE tokens/s; decode HBM TB/s and prefill MFMA util vs peak"
+CALIB_BYTES = 256 << 20        # the plain device copy that calibrates the traffic counters
 
 
 def parse():
@@ -46,6 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
+    ap.add_argument("--logit-sets", type=int, default=8, help="batches of router logits to rotate")
+    ap.add_argument("--repeats", type=int, default=7, help="repeats of the timed loop for the spread")
     ap.add_argument("--deterministic", action="store_true", help="ordered combine")
     ap.add_argument("--shared", action="store_true",
                     help="with the shared expert (one more expert every token reads)")
@@ -57,6 +74,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--summarize", metavar="WORKLOAD", default=None,
+                    help="turn gpurun_out/prof/WORKLOAD rocprofv3 output into profiles/ files")
     return ap.parse_args()
 
 
@@ -80,7 +99,9 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 10}), flush=True)
 
 
-def build_inputs(wl, copies, shared=False):
+# ---------------------------------------------------------------- inputs
+
+def build_inputs(wl, copies, shared=False, logit_sets=1):
     import numpy as np
     import torch
     import mxfp4_block_scaled_router_amd as mx
@@ -90,7 +111,8 @@ def build_inputs(wl, copies, shared=False):
                         shared=shared, a8=wl.a8)
     nw = wl.E_local + (1 if shared else 0)  # experts in the weight buffers
     x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).cuda()
-    logits = torch.from_numpy(inp["logits"]).cuda()
+    logits = [torch.from_numpy(inp["logits"]).cuda()] + \
+        [torch.from_numpy(W.make_logits(wl, v)).cuda() for v in range(1, max(1, logit_sets))]
     if wl.weight_kind == "uniform":
         if shared:
             inp.update(zip(("w13", "w13s", "w2", "w2s"),
@@ -121,26 +143,62 @@ def build_inputs(wl, copies, shared=False):
     return inp, dims, x, logits, banks, bank
 
 
+def host_student_t_weights(wl, inp, experts, shared=False):
+    """Canonical host weights of a Student-t workload for the oracle: the listed
+    experts drawn as the GPU path draws them and quantised by the oracle's own
+    quantiser (the others stay zero: the sample never reads them)."""
+    import numpy as np
+    import oracle
+    from mxfp4_block_scaled_router_amd import workloads as W
+    E, H, I = wl.E_local + (1 if shared else 0), wl.H, wl.I
+    if "w13" not in inp:
+        inp.update(w13=np.zeros((E, 2 * I, H // 2), np.uint8), w13s=np.zeros((E, 2 * I, H // 32), np.uint8),
+                   w2=np.zeros((E, H, I // 2), np.uint8), w2s=np.zeros((E, H, I // 32), np.uint8),
+                   _done=set())
+    for e in experts:
+        if e in inp["_done"]:
+            continue
+        for which, c, s in (("w13", "w13", "w13s"), ("w2", "w2", "w2s")):
+            v = W.student_t_expert(wl, int(e), which, device="cuda").cpu().numpy()
+            inp[c][e], inp[s][e] = oracle.quantize(v)
+        inp["_done"].add(e)
+
+
 def cpu_baseline(wl, inp, target_s, shared=False):
     """Oracle on a bounded sample: whole steps when one step is small enough,
-    else a subset of tokens (token_mask); returns tokens/s on this host."""
+    else a subset of tokens (token_mask); returns tokens/s on this host.  The
+    weights' preparation (Student-t workloads: drawing and quantising the
+    sampled tokens' experts on the host) is outside the timed calls."""
     import numpy as np
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    student = wl.weight_kind != "uniform"
+    ids, _ = oracle.route(inp["logits"], wl.top_k) if student else (None, None)
+
+    def need(mask):
+        if student:
+            sel = ids if mask is None else ids[mask]
+            loc = sel - wl.first_local
+            experts = sorted(set(int(e) for e in loc[(loc >= 0) & (loc < wl.E_local)].ravel()))
+            if shared:
+                experts.append(wl.E_local)
+            host_student_t_weights(wl, inp, experts, shared)
 
     def run(mask):
+        need(mask)
         t0 = time.perf_counter()
         oracle.moe_forward(inp["x"], inp["logits"], inp["w13"], inp["w13s"], inp["w2"], inp["w2s"],
                            top_k=wl.top_k, clamp_limit=wl.clamp_limit, E_global=wl.E_global,
                            first_local=wl.first_local, a4=wl.a4, a8=wl.a8, shared=shared,
-                           token_mask=mask,
-                           want_act=False, nthreads=threads)
+                           token_mask=mask, want_act=False, nthreads=threads)
         return time.perf_counter() - t0
 
+    rng = np.random.default_rng(0)
+    order = rng.permutation(wl.T)
     # probe with a few tokens to size the sample
     n_probe = min(wl.T, 4)
     mask = np.zeros(wl.T, bool)
-    mask[:n_probe] = True
+    mask[order[:n_probe]] = True
     t_probe = run(mask)
     per_tok = t_probe / n_probe
     if per_tok * wl.T <= target_s:
@@ -153,13 +211,41 @@ def cpu_baseline(wl, inp, target_s, shared=False):
                 "sample": "%d full steps of the %s workload (%d tokens each), %.1f s" %
                 (reps, wl.name, wl.T, t)}
     n = max(1, min(wl.T, int(target_s / max(per_tok, 1e-6))))
-    rng = np.random.default_rng(0)
     mask = np.zeros(wl.T, bool)
-    mask[rng.choice(wl.T, size=n, replace=False)] = True
+    mask[order[:n]] = True
     t = run(mask)
+    what = ("; weights of the sampled tokens' experts quantised on the host by the oracle"
+            if student else "")
     return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d tokens of one %s step (routing of all tokens, expert work and "
-                      "combine of the sampled ones), %.1f s" % (n, wl.T, wl.name, t)}
+                      "combine of the sampled ones%s), %.1f s" % (n, wl.T, wl.name, what, t)}
+
+
+# ---------------------------------------------------------------- timing
+
+def time_loop(step, n):
+    import torch
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
+def repeats(step, K, ms_per_step, R):
+    """R repeats of a loop of at least K steps and about 20 ms each."""
+    import numpy as np
+    if R <= 0:
+        return None
+    n = max(K, int(math.ceil(20.0 / max(ms_per_step, 1e-6))))
+    v = np.array([time_loop(step, n) for _ in range(R)])
+    return {"R": R, "steps_each": n, "median_ms": float(np.median(v)),
+            "p10_ms": float(np.percentile(v, 10)), "p90_ms": float(np.percentile(v, 90)),
+            "min_ms": float(v.min()), "max_ms": float(v.max())}
 
 
 def bench_bf16_experts(args, wl):
@@ -186,28 +272,24 @@ def bench_bf16_experts(args, wl):
     mixed = [mx.mxfp4_moe_preshuffle_fused(dims, list(excluded), *dev) for _ in range(len(banks))]
     del dev
     k = wl.top_k
+    lg = logits[0]
     ws = torch.empty(mx.mxfp4_moe_workspace_bytes(dims, k), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
 
-    def time_steps(step):
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(args.steps):
-            step(i)
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps
+    def mixed_step(i):
+        mx.mxfp4_moe_forward_mixed(dims, mixed[i % len(mixed)][1], x, lg, *mixed[i % len(mixed)][0],
+                                   k, wl.clamp_limit, out=out, workspace=ws)
 
-    ms_mixed = time_steps(lambda i: mx.mxfp4_moe_forward_mixed(
-        dims, mixed[i % len(mixed)][1], x, logits, *mixed[i % len(mixed)][0], k, wl.clamp_limit,
-        out=out, workspace=ws))
-    ms_packed = time_steps(lambda i: mx.mxfp4_moe_forward(
-        dims, x, logits, *banks[i % len(banks)], k, wl.clamp_limit, out=out, workspace=ws))
-    rt = mx.mxfp4_moe_route(dims, logits, k, workspace=ws)
+    def packed_step(i):
+        mx.mxfp4_moe_forward(dims, x, lg, *banks[i % len(banks)], k, wl.clamp_limit, out=out,
+                             workspace=ws)
+
+    for i in range(args.warmup):
+        mixed_step(i)
+        packed_step(i)
+    ms_mixed = time_loop(mixed_step, args.steps)
+    ms_packed = time_loop(packed_step, args.steps)
+    rt = mx.mxfp4_moe_route(dims, lg, k, workspace=ws)
     counts = rt["counts"].cpu().numpy()
     rec = {
         "metric": METRIC, "value": wl.T / (ms_mixed * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -226,8 +308,22 @@ def bench_bf16_experts(args, wl):
     print(json.dumps(rec), flush=True)
 
 
+def profile_record(workload):
+    """The committed rocprofv3 summary of this workload, if it was taken from
+    the current sources."""
+    path = os.path.join(ROOT, "profiles", "%s_kernels.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    return rec if rec.get("source_digest") == source_digest() else None
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -244,35 +340,32 @@ def main():
     mx.load_library()
     if args.bf16_experts:
         return bench_bf16_experts(args, wl)
-    inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies, args.shared)
+    inp, dims, x, logits, banks, bank_bytes = build_inputs(wl, args.copies, args.shared,
+                                                           args.logit_sets)
     if args.deterministic:
         dims.flags |= mx.MXFP4_MOE_DETERMINISTIC
     k = wl.top_k
     ws = torch.empty(mx.mxfp4_moe_workspace_bytes(dims, k), dtype=torch.uint8, device="cuda")
     plan = mx.mxfp4_moe_plan(dims, k)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    nb, nl = len(banks), len(logits)
 
-    # routing statistics (same logits every step)
-    rt = mx.mxfp4_moe_route(dims, logits, k, workspace=ws)
-    counts = rt["counts"].cpu().numpy()
-    touched = int((counts > 0).sum())
-    n_assign = int(counts.sum())
+    # routing statistics of every logit batch
+    touched_l, assign_l = [], []
+    for lg in logits:
+        rt = mx.mxfp4_moe_route(dims, lg, k, workspace=ws)
+        counts = rt["counts"].cpu().numpy()
+        touched_l.append(int((counts > 0).sum()))
+        assign_l.append(int(counts.sum()))
 
     def step(i):
-        mx.mxfp4_moe_forward(dims, x, logits, *banks[i % len(banks)], k, wl.clamp_limit, out=out,
+        mx.mxfp4_moe_forward(dims, x, logits[i % nl], *banks[i % nb], k, wl.clamp_limit, out=out,
                              workspace=ws)
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = time_loop(step, args.steps)
+    spread = repeats(step, args.steps, ms_per_step, args.repeats)
 
     # per-phase timing loop
     nph = len(mx.PHASES)
@@ -282,14 +375,17 @@ def main():
             e.record()
     torch.cuda.synchronize()
     for i in range(args.steps):
-        mx.mxfp4_moe_forward_timed(dims, x, logits, *banks[i % len(banks)], k, wl.clamp_limit,
+        mx.mxfp4_moe_forward_timed(dims, x, logits[i % nl], *banks[i % nb], k, wl.clamp_limit,
                                    evs[i], out=out, workspace=ws)
     torch.cuda.synchronize()
     phase_ms = {p: float(np.mean([row[j].elapsed_time(row[j + 1]) for row in evs]))
                 for j, p in enumerate(mx.PHASES)}
 
-    # algorithmic work
+    # algorithmic work, averaged over the steps' logit batches
     H, I, T = wl.H, wl.I, wl.T
+    sel = [i % nl for i in range(args.steps)]
+    touched = float(np.mean([touched_l[j] for j in sel]))
+    n_assign = float(np.mean([assign_l[j] for j in sel]))
     w13_b = 2 * I * H // 2 + 2 * I * H // 32
     w2_b = H * I // 2 + H * I // 32
     bytes_ = {
@@ -305,25 +401,39 @@ def main():
     dominant = max(("gate_up", "down"), key=lambda p: phase_ms[p])
     # an FP8 x FP4 product issues at the FP8 rate
     mfma_dtype = "fp4" if wl.a4 else ("fp8" if wl.a8 else "bf16")
-    if wl.name in ("prefill", "a4", "a8"):
-        achieved = flops[dominant] / (phase_ms[dominant] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[mfma_dtype],
-                "unit": "TFLOP/s"}
+    compute_bound = wl.name in ("prefill", "a4", "a8")
+    work = flops if compute_bound else bytes_
+
+    def rate(p, ms):
+        return work[p] / (ms * 1e-3) / (1e12 if compute_bound else 1e9)
+
+    if compute_bound:
+        roof = {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS[mfma_dtype], "unit": "TFLOP/s"}
     else:
-        achieved = bytes_[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["achieved"] = rate(dominant, phase_ms[dominant])
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dominant
-    roof["algorithmic_per_launch"] = bytes_[dominant] if roof["bound"] == "hbm" else flops[dominant]
+    roof["timing"] = ("HIP events on the library's stream around the phase (kernel plus its "
+                      "dispatch latency), mean over the phase-timed loop")
+    roof["algorithmic_per_launch"] = work[dominant]
     roof["mean_launch_ms"] = phase_ms[dominant]
     roof["traffic"] = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("source_digest") == source_digest() and tr.get("kernel_phase") == dominant:
-            roof["traffic"] = tr.get("traffic_bytes_per_launch")
+    prof = profile_record(wl.name)
+    if prof is not None and not args.shared and not args.deterministic:
+        ph = prof.get("phases", {}).get(dominant)
+        if ph and ph.get("avg_us"):
+            roof["kernel_rocprof"] = ph["kernel"]
+            roof["mean_launch_ms_rocprof"] = ph["avg_us"] * 1e-3
+            roof["achieved_rocprof"] = rate(dominant, ph["avg_us"] * 1e-3)
+            roof["frac_rocprof"] = roof["achieved_rocprof"] / roof["peak"]
+            roof["rocprof_summary"] = "profiles/%s_kernels.txt" % wl.name
+            if ph.get("traffic_bytes") is not None:
+                roof["traffic"] = ph["traffic_bytes"]
+        if prof.get("mfma_busy") and dominant in prof["mfma_busy"]:
+            roof["mfma_busy_counter"] = prof["mfma_busy"][dominant]
 
+    ms_rep = spread["median_ms"] if spread else ms_per_step
     rec = {
         "metric": METRIC,
         "value": wl.T / (ms_per_step * 1e-3),
@@ -336,22 +446,25 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": mfma_dtype,
-        "data": "synthetic (seeded: %s)" % ("x~N(0,1) bf16, logits~N(0,1), uniform E2M1 codes"
-                                            if wl.weight_kind == "uniform" else
-                                            "Student-t(3) weights quantised on the GPU"),
+        "data": "synthetic (seeded: %s; %d router-logit batches rotated)" % (
+            "x~N(0,1) bf16, logits~N(0,1), uniform E2M1 codes" if wl.weight_kind == "uniform"
+            else "Student-t(3) weights quantised on the GPU", nl),
         "config": {"workload": "%s T=%d H=%d I=%d E=%d/%d top-%d clamp=%g%s" % (
             wl.name, T, H, I, wl.E_local, wl.E_global, k, wl.clamp_limit,
             (" A4" if wl.a4 else "") + (" A8" if wl.a8 else "") +
             (" +shared expert" if args.shared else "")),
             "T": T, "H": H, "I": I, "E_local": wl.E_local, "shared_expert": bool(args.shared),
-            "E_global": wl.E_global, "top_k": k, "touched_experts": touched,
-            "local_assignments": n_assign, "weight_copies_rotated": len(banks),
+            "E_global": wl.E_global, "top_k": k, "touched_experts_mean": touched,
+            "touched_experts_per_batch": touched_l, "local_assignments_mean": n_assign,
+            "weight_copies_rotated": nb, "logit_batches_rotated": nl,
             "bank_bytes": bank_bytes, "combine": "ordered" if plan["ordered_combine"] else "atomic",
             "tile_rows": plan["tile_rows"],
             "parallelism": "single GPU"},
+        "repeats": spread,
         "roofline": roof,
         "step": {"hbm_bytes": step_bytes, "hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
                  "hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "hbm_frac_median_repeat": step_bytes / (ms_rep * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "flops": flops["gate_up"] + flops["down"],
                  "mfma_frac": (flops["gate_up"] + flops["down"]) / (ms_per_step * 1e-3) / 1e12 /
                  MFMA_PEAK_TFLOPS[mfma_dtype]},
@@ -359,11 +472,151 @@ def main():
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline:
-        if "w13" not in inp:
-            rec["cpu_baseline"] = None   # Student-t weights live on the GPU only
-        else:
-            rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.shared)
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.shared)
     print(json.dumps(rec), flush=True)
+
+
+# ---------------------------------------------------------------- rocprof summaries
+
+PHASE_KERNELS = {   # kernel-name fragments of each phase (first match wins)
+    "route": ("route_",),
+    "quantize": ("quantize_kernel",),
+    "gate_up": ("gate_up",),
+    "down": ("down_",),
+    "combine": ("cast_out", "combine_gather"),
+}
+
+
+def _csv_rows(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _col(row, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError("none of %s in %s" % (names, list(row)))
+
+
+def _per_dispatch(d, counter):
+    """{kernel name: [value per dispatch]} of one --pmc pass (counter summed
+    over its instances within a dispatch)."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if _col(r, "Counter_Name") != counter:
+            continue
+        key = (_col(r, "Dispatch_Id"), _col(r, "Kernel_Name"))
+        acc[key] = acc.get(key, 0.0) + float(_col(r, "Counter_Value"))
+    out = {}
+    for (disp, name), v in acc.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize(workload):
+    """profiles/<workload>_kernels.{txt,json} from the rocprofv3 runs below."""
+    base = os.path.join(ROOT, "gpurun_out", "prof", workload)
+    cal = os.path.join(ROOT, "gpurun_out", "prof", "calib")
+    bench_cmd = "python3 bench.py --workload %s --steps 20 --warmup 5 --repeats 1 --no-cpu-baseline" % workload
+    cmds = [
+        "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/%s/stats -o run -- %s"
+        % (workload, bench_cmd),
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/%s/fetch -o run -- %s"
+        % (workload, bench_cmd),
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/%s/write -o run -- %s"
+        % (workload, bench_cmd),
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/calib/fetch -o run -- "
+        "python3 bench.py --copy-calibration %d" % CALIB_BYTES,
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/calib/write -o run -- "
+        "python3 bench.py --copy-calibration %d" % CALIB_BYTES,
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+        "-d gpurun_out/prof/%s/mfma -o run -- %s" % (workload, bench_cmd),
+    ]
+    stats = []
+    for r in _csv_rows(os.path.join(base, "stats"), "kernel_stats.csv"):
+        stats.append((_col(r, "Name", "KernelName", "Kernel_Name"), int(_col(r, "Calls")),
+                      float(_col(r, "AverageNs", "Average_Ns")) / 1e3,
+                      float(_col(r, "MinNs", "Min_Ns")) / 1e3, float(_col(r, "MaxNs", "Max_Ns")) / 1e3,
+                      float(_col(r, "Percentage"))))
+    stats.sort(key=lambda s: -s[1] * s[2])
+    traffic = {}
+    have_pmc = os.path.isdir(os.path.join(base, "fetch")) and os.path.isdir(os.path.join(base, "write"))
+    factors = None
+    if have_pmc:
+        cf = _per_dispatch(os.path.join(cal, "fetch"), "FETCH_SIZE")
+        cw = _per_dispatch(os.path.join(cal, "write"), "WRITE_SIZE")
+        copy = [n for n in cf if "copyBuffer" in n]
+        kib = CALIB_BYTES / 1024.0
+        import statistics
+        f_fac = kib / statistics.median(max(cf[n]) for n in copy)
+        w_fac = kib / statistics.median(max(cw[n]) for n in copy)
+        factors = (f_fac, w_fac)
+        fetch = _per_dispatch(os.path.join(base, "fetch"), "FETCH_SIZE")
+        write = _per_dispatch(os.path.join(base, "write"), "WRITE_SIZE")
+        for name in fetch:
+            fb = statistics.median(fetch[name]) * 1024.0 * f_fac
+            wb = statistics.median(write.get(name, [0.0])) * 1024.0 * w_fac
+            traffic[name] = (fb, wb)
+    mfma = {}
+    mdir = os.path.join(base, "mfma")
+    if os.path.isdir(mdir):
+        busy = _per_dispatch(mdir, "SQ_VALU_MFMA_BUSY_CYCLES")
+        cu = _per_dispatch(mdir, "SQ_BUSY_CU_CYCLES")
+        gui = _per_dispatch(mdir, "GRBM_GUI_ACTIVE")
+        for name in busy:
+            import statistics
+            mfma[name] = {"SQ_VALU_MFMA_BUSY_CYCLES": statistics.median(busy[name]),
+                          "SQ_BUSY_CU_CYCLES": statistics.median(cu.get(name, [0])),
+                          "GRBM_GUI_ACTIVE": statistics.median(gui.get(name, [0]))}
+    phases = {}
+    for ph, frags in PHASE_KERNELS.items():
+        for name, calls, avg, mn, mxv, pct in stats:
+            if any(f in name for f in frags) and "preshuffle" not in name:
+                tr = traffic.get(name)
+                phases[ph] = {"kernel": name, "avg_us": avg, "calls": calls,
+                              "traffic_bytes": (tr[0] + tr[1]) if tr else None}
+                break
+    mfma_busy = {}
+    for ph, v in phases.items():
+        m = mfma.get(v["kernel"])
+        if m and m["GRBM_GUI_ACTIVE"]:
+            # MFMA-busy cycles summed over the CUs, per CU and GPU-active cycle
+            mfma_busy[ph] = dict(m, frac=m["SQ_VALU_MFMA_BUSY_CYCLES"] / (256.0 * m["GRBM_GUI_ACTIVE"]))
+    rec = {"workload": workload, "source_digest": source_digest(), "commands": cmds,
+           "phases": phases, "mfma_busy": mfma_busy,
+           "counter_factors": {"fetch": factors[0], "write": factors[1]} if factors else None}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "%s_kernels.json" % workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# %s workload: rocprofv3 kernel durations%s (source digest %s)" % (
+        workload, " and HBM traffic per dispatch" if traffic else "", rec["source_digest"]),
+        "# commands (repo root, after `cd /tmp && export TMPDIR=/tmp`), then "
+        "`python3 bench.py --summarize %s`:" % workload]
+    lines += ["#   " + c for c in cmds]
+    if factors:
+        lines.append("# traffic: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (KiB per dispatch; factors from "
+                     "the %d MiB copy calibration), median over dispatches" % (
+                         factors[0], factors[1], CALIB_BYTES >> 20))
+    lines.append("%-72s %6s %10s %10s %10s %7s %11s %11s" % (
+        "kernel", "calls", "avg_us", "min_us", "max_us", "pct", "fetch_MB", "write_MB"))
+    for name, calls, avg, mn, mxv, pct in stats:
+        tr = traffic.get(name)
+        lines.append("%-72s %6d %10.2f %10.2f %10.2f %7.2f %11s %11s" % (
+            name[:72], calls, avg, mn, mxv, pct,
+            "%.2f" % (tr[0] / 1e6) if tr else "-", "%.2f" % (tr[1] / 1e6) if tr else "-"))
+    for ph, m in mfma_busy.items():
+        lines.append("# %s: SQ_VALU_MFMA_BUSY_CYCLES / (256 CUs x GRBM_GUI_ACTIVE) = %.3f" % (ph, m["frac"]))
+    with open(os.path.join(ROOT, "profiles", "%s_kernels.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":

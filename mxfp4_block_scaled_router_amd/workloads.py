@@ -120,8 +120,13 @@ def make_x(wl: Workload) -> np.ndarray:
     return bf16_bits_of(x)
 
 
-def make_logits(wl: Workload) -> np.ndarray:
-    lg = _rng(wl, "logits").standard_normal((wl.T, wl.E_global), dtype=np.float32)
+def make_logits(wl: Workload, variant: int = 0) -> np.ndarray:
+    """Router logits [T, E_global].  variant > 0 draws another batch of tokens'
+    logits from its own stream; the per-expert bias (a property of the
+    experts, not of the tokens) is the same for every variant."""
+    rng = _rng(wl, "logits") if variant == 0 else \
+        np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 0x106175, variant])))
+    lg = rng.standard_normal((wl.T, wl.E_global), dtype=np.float32)
     if wl.logits_kind == "zipf_bias":
         rank = _rng(wl, "bias").permutation(wl.E_global) + 1
         bias = (-1.1 * np.log(rank.astype(np.float64))).astype(np.float32)
