@@ -72,6 +72,8 @@ extern "C" {
 #define MXFP4_MOE_ERR_HIP (-10)                /* a HIP call failed (see last_hip_error) */
 #define MXFP4_MOE_ERR_BAD_FLAGS (-11)          /* unknown flag bits */
 #define MXFP4_MOE_ERR_BAD_ARGUMENT (-12)       /* any other invalid scalar argument */
+#define MXFP4_MOE_ERR_SCRATCH_LIMIT (-13)      /* mxfp4_moe_forward_noalloc: the call needs more
+                                                  workspace than its static scratch holds */
 
 /* flags */
 #define MXFP4_MOE_A4 0x1u            /* quantise x (along H) and the SwiGLU output (along
@@ -170,6 +172,30 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* route
                       const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
                       const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxfp4_moe_forward for callers that cannot allocate or pass device memory
+ * beyond the layer's own tensors (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): no workspace argument.  Its
+ * workspace is a static device array of MXFP4_MOE_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, created when the library's code is loaded on that
+ * GPU and held until the process ends; its device address is looked up on the
+ * first call on each device.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ * Arguments, results and errors as mxfp4_moe_forward, plus
+ * MXFP4_MOE_ERR_SCRATCH_LIMIT when mxfp4_moe_workspace_bytes for these dims
+ * and top_k exceeds MXFP4_MOE_NOALLOC_SCRATCH_BYTES (checked before any GPU
+ * work; decode, verify and expert-parallel-share shapes fit, large prefill
+ * chunks do not).  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on one GPU (other streams, other host threads) race and must
+ * be ordered by the caller.  The array keeps the last call's contents; the
+ * layer clears what it needs cleared itself.
+ */
+#define MXFP4_MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                              const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2,
+                              const uint8_t* w2s, int32_t top_k, float clamp_limit, void* out,
+                              hipStream_t stream);
 
 /*
  * mxfp4_moe_forward that also copies the intermediates out, in canonical order

@@ -69,7 +69,7 @@ EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
             "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
             "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_quantize8", "mxfp4_moe_plan",
-            "mxfp4_moe_preshuffle_fused", "mxfp4_moe_forward_mixed")
+            "mxfp4_moe_preshuffle_fused", "mxfp4_moe_forward_mixed", "mxfp4_moe_forward_noalloc")
 
 
 def load_library(path: str = LIB_PATH):
@@ -100,6 +100,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_plan.argtypes = [D, I32, PI32, PI32]
     lib.mxfp4_moe_forward.restype = ctypes.c_int
     lib.mxfp4_moe_forward.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]
+    lib.mxfp4_moe_forward_noalloc.restype = ctypes.c_int
+    lib.mxfp4_moe_forward_noalloc.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P]
     lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
     lib.mxfp4_moe_forward_debug.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ,
                                             P, P, P, P, P, P, P]
@@ -250,6 +252,21 @@ def mxfp4_moe_forward(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: i
            _L().mxfp4_moe_forward(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13), _p(w13s),
                                   _p(w2), _p(w2s), int(top_k), float(clamp_limit), _p(out),
                                   _p(workspace), nbytes, _stream()))
+    return out
+
+
+def mxfp4_moe_forward_noalloc(dims: Dims, x, router_logits, w13, w13s, w2, w2s, top_k: int,
+                              clamp_limit: float, out):
+    """The layer without a workspace argument: the library's static per-GPU
+    scratch serves as workspace, and the call allocates nothing (``out`` is
+    required).  Calls that overlap on one GPU race on that scratch."""
+    _dev_tensor(x, torch.bfloat16, "x")
+    _dev_tensor(router_logits, torch.float32, "router_logits")
+    _dev_tensor(out, torch.bfloat16, "out")
+    _check("mxfp4_moe_forward_noalloc",
+           _L().mxfp4_moe_forward_noalloc(ctypes.byref(dims), _p(x), _p(router_logits), _p(w13),
+                                          _p(w13s), _p(w2), _p(w2s), int(top_k),
+                                          float(clamp_limit), _p(out), _stream()))
     return out
 
 

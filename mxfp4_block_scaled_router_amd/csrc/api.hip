@@ -487,6 +487,34 @@ int copy_intermediates(const Shape& s, const Layout& L, void* ws, void* act, uin
   return MXFP4_MOE_OK;
 }
 
+// ---------------------------------------------------------------- scratch
+// The workspace of mxfp4_moe_forward_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it is only a stand-in for
+// the device symbol): the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[MXFP4_MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of scratch on each device (null: not looked up yet)
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return MXFP4_MOE_ERR_UNSUPPORTED_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MXFP4_MOE_OK;
+}
+
 }  // namespace
 
 // ==================================================================== ABI
@@ -511,6 +539,7 @@ const char* mxfp4_moe_status_string(int status) {
     case MXFP4_MOE_ERR_HIP: return "MXFP4_MOE_ERR_HIP";
     case MXFP4_MOE_ERR_BAD_FLAGS: return "MXFP4_MOE_ERR_BAD_FLAGS";
     case MXFP4_MOE_ERR_BAD_ARGUMENT: return "MXFP4_MOE_ERR_BAD_ARGUMENT";
+    case MXFP4_MOE_ERR_SCRATCH_LIMIT: return "MXFP4_MOE_ERR_SCRATCH_LIMIT";
     default: return "MXFP4_MOE_ERR_UNKNOWN";
   }
 }
@@ -595,6 +624,26 @@ int mxfp4_moe_forward(const mxfp4_moe_dims* d, const void* x, const float* route
   st = check_device();
   if (st) return st;
   return run_forward(s, L, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, workspace, stream);
+}
+
+int mxfp4_moe_forward_noalloc(const mxfp4_moe_dims* d, const void* x, const float* router_logits,
+                              const uint8_t* w13, const uint8_t* w13s, const uint8_t* w2, const uint8_t* w2s,
+                              int32_t top_k, float clamp_limit, void* out, hipStream_t stream) {
+  Shape s;
+  int st = check_dims(d, top_k, true, &s);
+  if (st) return st;
+  const Layout L = layout_of(s);
+  if (L.total > (size_t)MXFP4_MOE_NOALLOC_SCRATCH_BYTES) return MXFP4_MOE_ERR_SCRATCH_LIMIT;
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  Layout L2;
+  st = check_forward_args(d, x, router_logits, w13, w13s, w2, w2s, top_k, clamp_limit, out, ws,
+                          (size_t)MXFP4_MOE_NOALLOC_SCRATCH_BYTES, &s, &L2);
+  if (st) return st;
+  return run_forward(s, L2, x, router_logits, w13, w13s, w2, w2s, clamp_limit, out, ws, stream);
 }
 
 int mxfp4_moe_forward_timed(const mxfp4_moe_dims* d, const void* x, const float* router_logits,

@@ -288,3 +288,27 @@ def test_preshuffle_fused_refusals(lib):
     assert call([0] * 8, map=0) == NULL_POINTER
     assert call([0] * 8, w2f=A + 8) == MISALIGNED
     assert call([0, 1, 0, 0, 0, 0, 0, 0], map=A + 2) == MISALIGNED
+
+
+def test_noalloc_refusals(lib):
+    """mxfp4_moe_forward_noalloc: a call whose workspace exceeds the static
+    scratch is refused by name before anything else; other refusals as
+    mxfp4_moe_forward; in range, without a GPU, the device refusal."""
+    f = lib.mxfp4_moe_forward_noalloc
+    P = 1 << 20
+    big = dims(T=8192, H=4096, I=1536, E_global=128, E_local=128)
+    assert f(ctypes.byref(big), P, P, P, P, P, P, 8, 7.0, P, None) == -13
+    assert mx.status_string(-13) == "MXFP4_MOE_ERR_SCRATCH_LIMIT"
+    d = dims()
+    assert f(ctypes.byref(d), P, P, P, P, P, P, 9, 7.0, P, None) == BAD_TOP_K
+    assert f(None, P, P, P, P, P, P, 2, 7.0, P, None) == NULL_POINTER
+    assert f(ctypes.byref(d), P, P, P, P, P, P, 2, float("nan"), P, None) in (BAD_CLAMP, UNSUPPORTED_DEVICE)
+    st = f(ctypes.byref(d), P, P, P, P, P, P, 2, 7.0, P, None)
+    assert st == UNSUPPORTED_DEVICE
+    # the limit admits the decode, verify and expert-parallel-share workloads
+    for kw, k in ((dict(T=16, H=2048, I=1536, E_global=64, E_local=64), 8),
+                  (dict(T=288, H=2048, I=1536, E_global=64, E_local=64), 8),
+                  (dict(T=256, H=5120, I=1536, E_global=256, E_local=64), 8),
+                  (dict(T=256, H=5120, I=1536, E_global=256, E_local=64, flags=0x2), 8)):
+        st, n = ws_status(dims(**kw), k)
+        assert st == OK and n <= 64 << 20, (kw, n)
