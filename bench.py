@@ -506,15 +506,17 @@ def _col(row, *names):
     raise KeyError("none of %s in %s" % (names, list(row)))
 
 
-def _per_dispatch(d, counter):
-    """{kernel name: [value per dispatch]} of one --pmc pass (counter summed
-    over its instances within a dispatch)."""
-    acc = {}
+def _per_dispatch(d, counter, reduce=sum):
+    """{kernel name: [value per dispatch]} of one --pmc pass (the counter's
+    instances within a dispatch combined by reduce: sum, or max for a
+    per-XCD clock counter such as GRBM_GUI_ACTIVE)."""
+    inst = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         if _col(r, "Counter_Name") != counter:
             continue
         key = (_col(r, "Dispatch_Id"), _col(r, "Kernel_Name"))
-        acc[key] = acc.get(key, 0.0) + float(_col(r, "Counter_Value"))
+        inst.setdefault(key, []).append(float(_col(r, "Counter_Value")))
+    acc = {k: reduce(v) for k, v in inst.items()}
     out = {}
     for (disp, name), v in acc.items():
         out.setdefault(name, []).append(v)
@@ -537,7 +539,7 @@ def summarize(workload):
         "python3 bench.py --copy-calibration %d" % CALIB_BYTES,
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/calib/write -o run -- "
         "python3 bench.py --copy-calibration %d" % CALIB_BYTES,
-        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE MfmaUtil --output-format csv "
         "-d gpurun_out/prof/%s/mfma -o run -- %s" % (workload, bench_cmd),
     ]
     stats = []
@@ -570,12 +572,19 @@ def summarize(workload):
     if os.path.isdir(mdir):
         busy = _per_dispatch(mdir, "SQ_VALU_MFMA_BUSY_CYCLES")
         cu = _per_dispatch(mdir, "SQ_BUSY_CU_CYCLES")
-        gui = _per_dispatch(mdir, "GRBM_GUI_ACTIVE")
+        # the CSV holds one value per dispatch, summed over the counter's
+        # instances: GRBM_GUI_ACTIVE over the 8 XCDs, whose maximum (rocprof's
+        # MfmaUtil definition) the dispatch-wide sum / 8 stands for
+        gui = {k: [x / 8.0 for x in v] for k, v in _per_dispatch(mdir, "GRBM_GUI_ACTIVE").items()}
+        util = _per_dispatch(mdir, "MfmaUtil") if any(
+            _col(r, "Counter_Name") == "MfmaUtil" for r in _csv_rows(mdir, "counter_collection.csv")) else {}
         for name in busy:
             import statistics
             mfma[name] = {"SQ_VALU_MFMA_BUSY_CYCLES": statistics.median(busy[name]),
                           "SQ_BUSY_CU_CYCLES": statistics.median(cu.get(name, [0])),
                           "GRBM_GUI_ACTIVE": statistics.median(gui.get(name, [0]))}
+            if name in util:
+                mfma[name]["MfmaUtil"] = statistics.median(util[name])
     phases = {}
     for ph, frags in PHASE_KERNELS.items():
         for name, calls, avg, mn, mxv, pct in stats:
@@ -588,8 +597,9 @@ def summarize(workload):
     for ph, v in phases.items():
         m = mfma.get(v["kernel"])
         if m and m["GRBM_GUI_ACTIVE"]:
-            # MFMA-busy cycles summed over the CUs, per CU and GPU-active cycle
-            mfma_busy[ph] = dict(m, frac=m["SQ_VALU_MFMA_BUSY_CYCLES"] / (256.0 * m["GRBM_GUI_ACTIVE"]))
+            # rocprof's MfmaUtil: MFMA-busy cycles summed over the SIMDs (4 per
+            # CU, 1024) per GPU-active cycle
+            mfma_busy[ph] = dict(m, frac=m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * m["GRBM_GUI_ACTIVE"]))
     rec = {"workload": workload, "source_digest": source_digest(), "commands": cmds,
            "phases": phases, "mfma_busy": mfma_busy,
            "counter_factors": {"fetch": factors[0], "write": factors[1]} if factors else None}
@@ -613,7 +623,8 @@ def summarize(workload):
             name[:72], calls, avg, mn, mxv, pct,
             "%.2f" % (tr[0] / 1e6) if tr else "-", "%.2f" % (tr[1] / 1e6) if tr else "-"))
     for ph, m in mfma_busy.items():
-        lines.append("# %s: SQ_VALU_MFMA_BUSY_CYCLES / (256 CUs x GRBM_GUI_ACTIVE) = %.3f" % (ph, m["frac"]))
+        lines.append("# %s: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE per XCD) = %.3f%s"
+                     % (ph, m["frac"], " (rocprof MfmaUtil %.1f%%)" % m["MfmaUtil"] if "MfmaUtil" in m else ""))
     with open(os.path.join(ROOT, "profiles", "%s_kernels.txt" % workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
