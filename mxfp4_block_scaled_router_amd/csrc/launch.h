@@ -143,6 +143,8 @@ struct GemmPlan {
   int fg;        // 16-feature groups per wave
   int nw;        // waves per workgroup
   int direct_a;  // 1: activation operands loaded straight from global memory
+  int ms_dn = 0; // down's token tile in 16-row subtiles when it differs from gate_up's (0: ms)
+  int down_ms() const { return ms_dn ? ms_dn : ms; }
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
@@ -158,9 +160,14 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, 
 // af: activation format, 0 bf16, 1 MXFP4 (A4), 2 MXFP8 (A8)
 hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, int af,
                                  hipStream_t stream);
-// 128-token x 256-weight-row tiles, LDS ring fed by global->LDS copies (tile.hip)
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t stream);
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t stream);
+// Large token tiles through an LDS ring fed by global->LDS copies (tile.hip):
+// mt = 128 (128 x 512 tiles) or, with MX activations, 320 (320 x 128 tiles)
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, hipStream_t stream);
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool ordered,
+                            hipStream_t stream);
+// whether the tile kernels of height mt take a contraction of length K with
+// activation format af (the 320-row tiles hold their rows' scale bytes in LDS)
+bool tile_fits(int af, int mt, int64_t K);
 // The grid and share parameters launch_down_ksplit will use for these
 // arguments (for the gate_up side of dn_desc).
 hipError_t down_ksplit_shares(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, int* grid, int* fb,

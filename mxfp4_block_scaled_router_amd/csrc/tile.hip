@@ -55,42 +55,109 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
-constexpr int kMT = 128;  // token rows per tile
-constexpr int kWaves = 8;  // 2 (rows) x 4 (weight row groups)
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr size_t kTileLdsMax = 160 * 1024;
 
 // Activation formats: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 with E4M3 elements (A8).
 constexpr int kActBf16 = 0, kActFp4 = 1, kActFp8 = 2;
 // bytes of one activation row per k-tile (128 elements)
 constexpr int act_row_bytes(int af) { return af == kActFp4 ? 64 : af == kActFp8 ? 128 : 256; }
 
-template <int AF, int NRG_>
+// Tile shape.  The eight waves form a WMW x (8 / WMW) grid; a wave owns RB
+// 16-row blocks of the token tile and WN weight row groups.  IL: the row
+// blocks of wave wm are wm, wm + WMW, wm + 2 WMW, ... (interleaved, so a
+// partly filled tile spreads its rows over all waves); else the contiguous
+// RB wm .. RB wm + RB - 1.
+//   128-row tiles:  WMW 2, RB 4, WN NRG / 4 (128 x 512 with NRG 32)
+//   320-row tiles:  WMW 4, RB 5, WN 4, interleaved (320 x 128): with MX
+//                   activations one tile holds all rows of an expert of the
+//                   A4 prefill workload, so its weights stream once (a wider
+//                   weight block needs more accumulator registers than two
+//                   waves per SIMD leave).
+template <int AF, int WMW_, int RB_, int WN_, bool IL_, int SA_, int SB_, bool PF_ = false, bool RS_ = false>
 struct Cfg {
-  static constexpr int NRG = NRG_;                              // weight row groups per tile
+  // RS (PF only): all activation scale bytes of the tile's rows are copied
+  // into LDS once per tile ([MT][K/32], whole rows: full cache lines) instead
+  // of a 4-byte-per-row gather per k-tile, which touches one cache line per
+  // row for 4 useful bytes and dominated the copy path
+  static constexpr bool RS = RS_;
+  // PF: MX activations only, SA == SB: a step waits one k-tile ahead and
+  // reads the next k-tile's operands from LDS into a second register set
+  // while its MFMAs run on the current one (tile_mainloop_pf)
+  static constexpr bool PF = PF_;
+  static constexpr int WMW = WMW_, WNW = kWaves / WMW_, RB = RB_, WN = WN_;
+  static constexpr bool IL = IL_;
+  static constexpr int MT = 16 * RB * WMW;                      // token rows per tile
+  static constexpr int NRG = WN * WNW;                          // weight row groups per tile
   static constexpr int NT = 16 * NRG;
-  static constexpr int WN = NRG / 4;                            // row groups per wave
-  static constexpr int A_BYTES = kMT * act_row_bytes(AF);       // activation k-tile
-  static constexpr int AS_BYTES = AF != kActBf16 ? kMT * 4 : 0; // activation scale bytes
-  static constexpr int B_BYTES = NRG * 1024;                    // weight codes
-  static constexpr int A_OFF = 0, AS_OFF = A_BYTES, B_OFF = A_BYTES + AS_BYTES;
-  static constexpr int STAGE = B_OFF + B_BYTES;
-  static constexpr int ROWS_BYTES = kMT * 4;  // int32 [kMT]: A row index of each tile row
-  static constexpr int WS_BYTES = NRG * 256;   // weight scale dwords of one 4-k-tile group
-  static constexpr int STAGES_FIT = (160 * 1024 - ROWS_BYTES - WS_BYTES) / STAGE;
-  static constexpr int STAGES = STAGES_FIT > 4 ? 4 : STAGES_FIT;
-  static constexpr int A_CP = A_BYTES / 1024 / kWaves;  // copies per wave per k-tile
-  static constexpr int AS_CP = AF != kActBf16 ? 1 : 0;  // 2 copies, made by even and odd waves alike
+  static constexpr int ARB = act_row_bytes(AF);
+  static constexpr int A_BYTES = MT * ARB;                      // activation k-tile
+  static constexpr int AS_BYTES = AF != kActBf16 && !RS ? MT * 4 : 0;  // activation scale bytes
+  static constexpr int A_STAGE = A_BYTES + AS_BYTES;
+  static constexpr int B_BYTES = NRG * 1024;                    // weight codes of one k-tile
+  // two rings: SA activation slots (their copies hit L2: the rows are shared
+  // by the tile's weight blocks) and SB weight slots (a stream from HBM,
+  // which needs more bytes in flight)
+  static constexpr int SA = SA_, SB = SB_;
+  static constexpr int A_RING = 0, B_RING = SA * A_STAGE;
+  static constexpr int ROWS_BYTES = MT * 4;  // int32 [MT]: A row index of each tile row
+  static constexpr int WS_BYTES = 2 * NRG * 256;  // weight scale dwords of two 4-k-tile groups
+  // activation copies of 1 KiB (a wave instruction: 64 lanes x 16 bytes) per
+  // k-tile, spread over the waves; a wave whose share is short repeats the
+  // last copy (same bytes to the same place), so every wave issues A_CP
+  static constexpr int A_COPIES = A_BYTES / 1024;
+  static constexpr int A_CP = (A_COPIES + kWaves - 1) / kWaves;
+  // activation scale copies of 256 bytes (64 rows): one per wave, wave w
+  // taking chunk w % AS_CHUNKS
+  static constexpr int AS_CHUNKS = MT / 64;
+  static constexpr int AS_CP = AF != kActBf16 && !RS ? 1 : 0;
   static constexpr int B_CP = NRG / kWaves;
-  static constexpr int CP = A_CP + AS_CP + B_CP;
+  static constexpr int OPS_A = A_CP + AS_CP;  // vector-memory ops of one k-tile's activation copies
 
-  static constexpr int WS_OFF = STAGES * STAGE;
+  static constexpr int WS_OFF = B_RING + SB * B_BYTES;
   static constexpr int ROWS_OFF = WS_OFF + WS_BYTES;
-  static constexpr int LDS = ROWS_OFF + ROWS_BYTES;
-  static_assert(STAGES >= 2 && LDS <= 160 * 1024, "LDS budget");
-  static_assert(WN % 4 == 0 && NRG % kWaves == 0, "tile shape");
+  static constexpr int RS_OFF = ROWS_OFF + ROWS_BYTES;  // RS: [MT][K/32] activation scale bytes
+  static constexpr int LDS = RS_OFF;                     // without the row scales
+  static constexpr size_t lds_bytes(int64_t K) { return (size_t)LDS + (RS ? (size_t)MT * (size_t)(K / 32) : 0); }
+  static_assert(SA >= 2 && SA <= 5 && SB >= SA && LDS <= 160 * 1024, "LDS budget");
+  static_assert(!RS || PF, "row scales need the PF pipeline");
+  static_assert(WN % 2 == 0 && NRG % kWaves == 0 && kWaves % WMW == 0, "tile shape");
+  static_assert(A_BYTES % 1024 == 0 && MT % 64 == 0 && AS_CHUNKS <= kWaves, "copy shape");
   static constexpr int WSCP = NRG / kWaves;             // weight scale copies per wave per group
-  static constexpr int MAXWAIT = (STAGES - 2) * (CP + WSCP);
+  // bound on the ops a wait lets stay outstanding (see tile_mainloop)
+  static constexpr int MAXWAIT = (SB - 2) * B_CP + (SA - 1) * (WSCP + B_CP + 2 * OPS_A);
   static_assert(MAXWAIT < 64, "vmcnt range");
+  // vector-memory ops of pipeline step st (the next group's scale copies at
+  // a group's first k-tile, then the weight and activation copies)
+  static constexpr int ops_of_step(int st) { return ((st & 3) == 0 ? WSCP : 0) + B_CP + OPS_A; }
+  // ops issued after the activation copies of the k-tile a steady-state step
+  // at position j of its group waits for: those of the SA - 2 steps before
+  static constexpr int steady_after(int j) {
+    int n = 0;
+    for (int d = 1; d <= SA - 2; ++d) n += ops_of_step(j - d + 4);
+    return n;
+  }
+  // PF pipeline: ops issued after the activation copies of k-tile kt + 1,
+  // waited for at step kt (see tile_mainloop_pf)
+  static constexpr int pf_after(int kt) {
+    int n = 0;
+    if (kt + 1 <= SA - 1) {
+      n = (SA - 2 - kt) * (B_CP + OPS_A);
+      for (int st = 0; st < kt; ++st) n += ops_of_step(st);
+    } else {
+      for (int d = 1; d <= SA - 2; ++d) n += ops_of_step(kt - d + 4);
+    }
+    return n;
+  }
+  static constexpr int pf_max_after() {
+    int m = (SA - 1) * (B_CP + OPS_A);
+    for (int kt = 0; kt < 8; ++kt) m = pf_after(kt) > m ? pf_after(kt) : m;
+    return m;
+  }
+  static_assert(!PF || (AF != kActBf16 && SA == SB && pf_max_after() < 64), "PF pipeline");
+  // 16-row block of the tile held as the wave's rb-th
+  __device__ static constexpr int rowblock(int wm, int rb) { return IL ? wm + WMW * rb : RB * wm + rb; }
 };
 
 // s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding:
@@ -120,6 +187,13 @@ __device__ __forceinline__ void copy16(const void* src, uint8_t* lds_dst) {
 }
 __device__ __forceinline__ void copy4(const void* src, uint8_t* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+// weight streams are read once per step: non-temporal (cache policy nt), so
+// they do not displace the activation rows that a tile's weight blocks share
+// in L2
+constexpr int kCpolNT = 2;
+__device__ __forceinline__ void copy16_nt(const void* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, kCpolNT);
 }
 
 struct TileItem {
@@ -155,16 +229,16 @@ __device__ __forceinline__ void zero_duty(const GemmArgs& a) {
   for (int64_t i = tid; i < a.zero_n / 4; i += nthreads) reinterpret_cast<f32x4_t*>(a.zero_buf)[i] = z;
 }
 
-// The k-loop: acc[rb][cb] += A(rows 64 wm + 16 rb ..) * W(row group WN wn + cb)^T
-// over all of K.  rowidx (LDS): the A-matrix row of each tile row.
-template <int AF, int NRG>
+// The k-loop: acc[rb][cb] += A(row block C::rowblock(wm, rb)) * W(row group
+// WN wn + cb)^T over all of K.  rowidx (LDS): the A-matrix row of each tile
+// row.  Row blocks wholly past the tile's rows skip their MFMAs.
+template <int AF, typename C>
 __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
-                                              uint8_t* lds, f32x4_t (&acc)[4][NRG / 4]) {
-  using C = Cfg<AF, NRG>;
-  constexpr int WN = C::WN;
+                                              uint8_t* lds, f32x4_t (&acc)[C::RB][C::WN]) {
+  constexpr int WN = C::WN, RB = C::RB;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::WMW, wn = wave / C::WMW;
   const int KT = (int)(K / kTileK);
   const int32_t* rowidx = reinterpret_cast<const int32_t*>(lds + C::ROWS_OFF);
 
@@ -175,7 +249,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     const int64_t rb = K * 2;  // bytes per activation row
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
-      const int j = wave * C::A_CP + jj;  // rows 4j .. 4j+3
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);  // rows 4j .. 4j+3
       const int row = 4 * j + (lane >> 4);
       const int c = (lane & 15) ^ (row & 15);
       a_src[jj] = reinterpret_cast<const uint8_t*>(a.a_bf16) + (int64_t)rowidx[row] * rb + c * 16;
@@ -186,23 +260,23 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     const int64_t rb = K;
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
-      const int j = wave * C::A_CP + jj;
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);
       const int row = 8 * j + (lane >> 3);
       const int c = (lane & 7) ^ ((row >> 1) & 7);
       a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
     }
-    const int row = 64 * (wave & 1) + lane;
+    const int row = 64 * (wave % C::AS_CHUNKS) + lane;
     as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);
   } else {
     const int64_t rb = K / 2;
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
-      const int j = wave * C::A_CP + jj;  // rows 16j .. 16j+15
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);  // rows 16j .. 16j+15
       const int row = 16 * j + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
       a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
     }
-    const int row = 64 * (wave & 1) + lane;
+    const int row = 64 * (wave % C::AS_CHUNKS) + lane;
     as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);
   }
   const int64_t cpe = codes_per_expert(N, K), spe = scales_per_expert(N, K);
@@ -225,21 +299,27 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
 #pragma unroll
     for (int i = 0; i < C::WSCP; ++i) {
       const int rgl = wave * C::WSCP + i;
-      copy4(s_lane + scales_group_offset(clamp_rg(it.n0 / 16 + rgl), q, K), lds + C::WS_OFF + rgl * 256);
+      copy4(s_lane + scales_group_offset(clamp_rg(it.n0 / 16 + rgl), q, K),
+            lds + C::WS_OFF + ((q & 1) * C::NRG + rgl) * 256);
     }
   };
 
-  auto issue = [&](int kt, uint8_t* slot) {
+  // activation copies of k-tile kt into slot (A rows, then their scale bytes)
+  auto issue_a = [&](int kt, uint8_t* slot) {
 #pragma unroll
     for (int jj = 0; jj < C::A_CP; ++jj) {
-      const int j = wave * C::A_CP + jj;
-      copy16(a_src[jj] + (int64_t)kt * act_row_bytes(AF), slot + C::A_OFF + j * 1024);
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);
+      copy16(a_src[jj] + (int64_t)kt * act_row_bytes(AF), slot + j * 1024);
     }
-    if constexpr (AF != kActBf16) copy4(as_src + (int64_t)kt * 4, slot + C::AS_OFF + (wave & 1) * 256);
+    if constexpr (AF != kActBf16)
+      copy4(as_src + (int64_t)kt * 4, slot + C::A_BYTES + (wave % C::AS_CHUNKS) * 256);
+  };
+  // weight-code copies of k-tile kt into slot
+  auto issue_b = [&](int kt, uint8_t* slot) {
 #pragma unroll
     for (int jj = 0; jj < C::B_CP; ++jj) {
       const int q = wave * C::B_CP + jj;
-      copy16(b_lane + b_off(jj) + (int64_t)kt * 1024, slot + C::B_OFF + q * 1024);
+      copy16(b_lane + b_off(jj) + (int64_t)kt * 1024, slot + q * 1024);
     }
   };
 
@@ -247,13 +327,13 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
   // WN wn + cb), read from LDS at the group's first k-tile
   uint32_t scur[WN];
 
-  auto compute = [&](int kt, const uint8_t* slot) {
+  auto compute = [&](int kt, const uint8_t* aslot, const uint8_t* bslot) {
     const int g = lane >> 4;
     u32x4_t bw[WN];
     uint32_t sbyte[WN];
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) {
-      bw[cb] = *reinterpret_cast<const u32x4_t*>(slot + C::B_OFF + (wn * WN + cb) * 1024 + lane * 16);
+      bw[cb] = *reinterpret_cast<const u32x4_t*>(bslot + (wn * WN + cb) * 1024 + lane * 16);
       sbyte[cb] = (scur[cb] >> (8 * (kt & 3))) & 0xFFu;
     }
     if constexpr (AF == kActBf16) {
@@ -262,145 +342,354 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
       for (int cb = 0; cb < WN; ++cb) sc[cb] = e8m0_scale_operand(sbyte[cb]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        bf16x8_t av[4];
+        bf16x8_t av[RB];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int row = wm * 64 + rb * 16 + (lane & 15);
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = C::rowblock(wm, rb) * 16 + (lane & 15);
           const int phys = (4 * g + m) ^ (lane & 15);
           av[rb] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 256 + phys * 16));
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(aslot + row * 256 + phys * 16));
         }
 #pragma unroll
         for (int cb = 0; cb < WN; ++cb) {
           const bf16x8_t bv = unpack8_e2m1(bw[cb][m], sc[cb]);
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bv, acc[rb][cb], 0, 0, 0);
         }
       }
     } else {
-      i32x8_t A[4];
-      uint32_t as[4];
+      i32x8_t A[RB];
+      uint32_t as[RB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int row = wm * 64 + rb * 16 + (lane & 15);
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = C::rowblock(wm, rb) * 16 + (lane & 15);
         if constexpr (AF == kActFp8) {
           // 8-bit A elements: lane group g supplies K 16 g .. 16 g + 15 and
           // 64 + 16 g .. 64 + 16 g + 15 (logical chunks g and 4 + g), with the
           // scale of block g as for E2M1 (the MFMA reads block b's scale from
           // lane group b)
           const int sw = (row >> 1) & 7;
-          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 128 + (g ^ sw) * 16);
-          const u32x4_t v1 =
-              *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 128 + ((4 + g) ^ sw) * 16);
+          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(aslot + row * 128 + (g ^ sw) * 16);
+          const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(aslot + row * 128 + ((4 + g) ^ sw) * 16);
           A[rb] = (i32x8_t){(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
                             (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
         } else {
           const int phys = g ^ ((row >> 2) & 3);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slot + C::A_OFF + row * 64 + phys * 16);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(aslot + row * 64 + phys * 16);
           A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
         }
-        as[rb] = slot[C::AS_OFF + row * 4 + g];
+        as[rb] = aslot[C::A_BYTES + row * 4 + g];
       }
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) {
         const i32x8_t B = {(int)bw[cb][0], (int)bw[cb][1], (int)bw[cb][2], (int)bw[cb][3], 0, 0, 0, 0};
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              A[rb], B, acc[rb][cb], AF == kActFp8 ? 0 : 4, 4, 0, (int)as[rb], 0, (int)sbyte[cb]);
+                A[rb], B, acc[rb][cb], AF == kActFp8 ? 0 : 4, 4, 0, (int)as[rb], 0, (int)sbyte[cb]);
       }
     }
   };
 
-  // ---- pipeline: stages 0 .. STAGES-2 in flight before the loop.  Step kt:
-  // wait for slot kt's copies, barrier, scale loads (steps 0 and 1 of a
-  // group), the copies of k-tile kt + S - 1, compute k-tile kt.  Every step
-  // issues its copies, past K those of the last k-tile again (into the slot
-  // read in the previous step, free after the barrier): with the same
-  // instructions on every path the compiler's own waits for the scale
+  // ---- pipeline.  Prologue: the first scale group, then for p = 0, 1, ...
+  // the weight copies of k-tile p (p <= SB - 2) and the activation copies of
+  // k-tile p (p <= SA - 2).  Step kt: wait until k-tile kt's activation
+  // copies -- issued after its weight copies -- have landed, barrier, scale
+  // dwords (steps 0 and 1 of a group), the weight copies of k-tile kt + SB - 1
+  // and the activation copies of k-tile kt + SA - 1, compute k-tile kt.
+  // Every step issues its copies, past K those of the last k-tile again (into
+  // the slot read in the previous step, free after the barrier): with the
+  // same instructions on every path the compiler's own waits for the scale
   // registers count exactly and never fall back to waiting for everything.
-  constexpr int S = C::STAGES;
+  constexpr int SA = C::SA, SB = C::SB;
+  constexpr int PM = SB - 2;  // last prologue index (SB >= SA)
+  auto aslot = [&](int kt) { return lds + C::A_RING + (kt % SA) * C::A_STAGE; };
+  auto bslot = [&](int kt) { return lds + C::B_RING + (kt % SB) * C::B_BYTES; };
   issue_scales(0);
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s < KT ? s : KT - 1, lds + s * C::STAGE);
-  // vector-memory ops a step issues: the next group's scale copies (second
-  // k-tile of a group: every wave has read the buffer at the first, before
-  // this step's barrier), then the stage copies
-  auto ops_of_step = [&](int st) -> int { return ((st & 3) == 1 ? C::WSCP : 0) + C::CP; };
-  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+  for (int p = 0; p <= PM; ++p) {
+    issue_b(p < KT ? p : KT - 1, bslot(p));
+    if (p <= SA - 2) issue_a(p < KT ? p : KT - 1, aslot(p));
+  }
+  // vector-memory ops a step issues: the next group's scale copies (first
+  // k-tile of a group), then the weight and activation copies
+  auto ops_of_step = [&](int st) -> int { return C::ops_of_step(st); };
+  // one step; `after` = the vector-memory ops issued after k-tile kt's
+  // activation copies (vmcnt counts in issue order)
+  auto step = [&](int kt, int j, auto wait) {
+    wait();
+    __builtin_amdgcn_s_barrier();
+    // a new 4-k-tile group starts: its scale dwords were copied at the
+    // previous group's first k-tile (before, or with SA = 5 in the same step
+    // just before, the activation copies waited for), or in the prologue
+    if (j == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kt = kt0 + j;
-      if (kt >= KT) break;
-      // ops issued after slot kt's copies (vmcnt counts in issue order): the
-      // prologue's later stages (k-tile kt < S - 1) or the ops of the steps
-      // between the one that issued slot kt and this one
-      int after = 0;
-      if (kt < S - 1) {
-        after = (S - 2 - kt) * C::CP;
-#pragma unroll
-        for (int st = 0; st < S - 2; ++st)
-          if (st < kt) after += ops_of_step(st);
-      } else {
-#pragma unroll
-        for (int d = 1; d <= S - 2; ++d) after += ops_of_step(kt - d);
-      }
-      wait_vm_dyn<C::MAXWAIT>(after);
-      __builtin_amdgcn_s_barrier();
-      // a new 4-k-tile group starts: its scale dwords were copied at the
-      // previous group's second k-tile (before the stage copies waited for
-      // above), or in the prologue
-      if (j == 0) {
-#pragma unroll
-        for (int cb = 0; cb < WN; ++cb)
-          scur[cb] = *reinterpret_cast<const uint32_t*>(lds + C::WS_OFF + (wn * WN + cb) * 256 + lane * 4);
-      }
-      if (j == 1) issue_scales((kt >> 2) + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(kt + S - 1 < KT ? kt + S - 1 : KT - 1, lds + ((kt + S - 1) % S) * C::STAGE);
-      compute(kt, lds + (kt % S) * C::STAGE);
+      for (int cb = 0; cb < WN; ++cb)
+        scur[cb] = *reinterpret_cast<const uint32_t*>(
+            lds + C::WS_OFF + (((kt >> 2) & 1) * C::NRG + wn * WN + cb) * 256 + lane * 4);
+      // the next group's scale dwords, into the other buffer (last read at
+      // the previous group's first k-tile, before this step's barrier)
+      issue_scales((kt >> 2) + 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + SB - 1 < KT ? kt + SB - 1 : KT - 1, bslot(kt + SB - 1));
+    issue_a(kt + SA - 1 < KT ? kt + SA - 1 : KT - 1, aslot(kt + SA - 1));
+    compute(kt, aslot(kt), bslot(kt));
+  };
+  // waits: in the first group, the rest of the prologue and the steps before
+  // this one (k-tile kt <= SA - 2, issued in the prologue), or the steps
+  // between the one that issued its copies and this one; in later groups
+  // (every k-tile issued in a step, SA <= 5) a constant for each position
+  auto first_after = [&](int j) -> int {
+    int after = 0;
+    if (j <= SA - 2) {
+#pragma unroll
+      for (int p = 1; p <= PM; ++p)
+        if (p > j) after += C::B_CP + (p <= SA - 2 ? C::OPS_A : 0);
+#pragma unroll
+      for (int st = 0; st < SA - 2; ++st)
+        if (st < j) after += ops_of_step(st);
+    } else {
+#pragma unroll
+      for (int d = 1; d <= SA - 2; ++d) after += ops_of_step(j - d);
+    }
+    return after;
+  };
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+    const bool first = kt0 == 0;
+    step(kt0, 0, [&] { if (first) wait_vm_dyn<C::MAXWAIT>(first_after(0)); else wait_vm<C::steady_after(0)>(); });
+    if (kt0 + 1 < KT)
+      step(kt0 + 1, 1, [&] { if (first) wait_vm_dyn<C::MAXWAIT>(first_after(1)); else wait_vm<C::steady_after(1)>(); });
+    if (kt0 + 2 < KT)
+      step(kt0 + 2, 2, [&] { if (first) wait_vm_dyn<C::MAXWAIT>(first_after(2)); else wait_vm<C::steady_after(2)>(); });
+    if (kt0 + 3 < KT)
+      step(kt0 + 3, 3, [&] { if (first) wait_vm_dyn<C::MAXWAIT>(first_after(3)); else wait_vm<C::steady_after(3)>(); });
   }
 }
 
-// Tile width: NRG weight row groups (MXFP4_MOE_TILE_NRG, tests and benchmarks
-// only, selects 16; default 32).
-int tile_nrg() {
-  static const int v = [] {
-    const char* e = getenv("MXFP4_MOE_TILE_NRG");
-    return e && !strcmp(e, "16") ? 16 : 32;
-  }();
-  return v;
+// The k-loop of the PF configurations (MX activations): step kt waits for
+// k-tile kt + 1's copies, so that after the barrier the wave reads k-tile
+// kt + 1's operands from LDS into one register set while its MFMAs consume
+// k-tile kt's, read in the step before, from the other.  A slot's operands
+// are in registers one step before the k-tile is used, so step kt refills
+// slot kt with k-tile kt + S: S - 1 k-tiles stay in flight.  Before the
+// barrier each wave waits for its own LDS reads (those of the slot the next
+// copies overwrite have completed before any wave issues them).
+template <int AF, typename C>
+__device__ __forceinline__ void tile_mainloop_pf(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
+                                                 uint8_t* lds, f32x4_t (&acc)[C::RB][C::WN]) {
+  constexpr int WN = C::WN, RB = C::RB, S = C::SA;
+  const int lane = lane_id();
+  const int g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % C::WMW, wn = wave / C::WMW;
+  const int KT = (int)(K / kTileK);
+  const int32_t* rowidx = reinterpret_cast<const int32_t*>(lds + C::ROWS_OFF);
+
+  // ---- per-lane copy sources (k-tile 0); k-tile kt adds kt * row bytes
+  const uint8_t* a_src[C::A_CP];
+  const uint8_t* as_src;
+  {
+    const int64_t rb = K * act_row_bytes(AF) / kTileK;  // code bytes per activation row
+#pragma unroll
+    for (int jj = 0; jj < C::A_CP; ++jj) {
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);
+      int row, c;
+      if constexpr (AF == kActFp8) {
+        // copy j fills rows 8j .. 8j+7, lane i row 8j + i/8 at chunk i % 8,
+        // which holds the row's logical chunk (i % 8) ^ ((row >> 1) & 7)
+        row = 8 * j + (lane >> 3);
+        c = (lane & 7) ^ ((row >> 1) & 7);
+      } else {
+        // copy j fills rows 16j .. 16j+15, lane i row 16j + i/4 at block i % 4,
+        // which holds the row's logical block (i % 4) ^ ((row >> 2) & 3)
+        row = 16 * j + (lane >> 2);
+        c = (lane & 3) ^ ((row >> 2) & 3);
+      }
+      a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
+    }
+    const int row = 64 * (wave % C::AS_CHUNKS) + lane;
+    as_src = a.a_scales + (int64_t)rowidx[row] * (K / 32);
+  }
+  const int RSB = (int)(K / 32);  // activation scale bytes per row
+  uint8_t* rs = lds + C::RS_OFF;
+  // With rows of a multiple of 128 bytes the 16 rows of one MFMA operand
+  // would fall into two LDS banks; their 16-byte chunks are then XOR-swizzled
+  // by (row >> 1) & 7 (chosen through the copies' source addresses), which
+  // puts the 16 rows' bytes of one k-tile into 16 distinct banks.
+  const int rs_sw = RSB % 128 == 0 ? 7 : 0;
+  if constexpr (C::RS) {
+    // every scale byte of the tile's rows, row-major [MT][K/32]: a copy
+    // instruction covers 1 KiB (or 256 bytes) of that array, whole rows apart
+    // from its ends; issued before the prologue, so the first wait covers them
+    if (RSB % 16 == 0) {
+      const int n = C::MT * RSB / 1024;
+      for (int i = wave; i < n; i += kWaves) {
+        const int o = i * 1024 + lane * 16;
+        const int row = o / RSB, chunk = (o % RSB) / 16;
+        copy16(a.a_scales + (int64_t)rowidx[row] * RSB + (chunk ^ ((row >> 1) & rs_sw)) * 16, rs + i * 1024);
+      }
+    } else {
+      const int n = C::MT * RSB / 256;
+      for (int i = wave; i < n; i += kWaves) {
+        const int o = i * 256 + lane * 4;
+        copy4(a.a_scales + (int64_t)rowidx[o / RSB] * RSB + o % RSB, rs + i * 256);
+      }
+    }
+  }
+  const int64_t cpe = codes_per_expert(N, K), spe = scales_per_expert(N, K);
+  const uint8_t* b_lane = a.w_codes + (int64_t)it.e * cpe + lane * 16;
+  const uint8_t* s_lane = a.w_scales + (int64_t)it.e * spe + lane * 4;
+  const int nrg = (int)(N / 16);
+  auto clamp_rg = [&](int rg) { return rg < nrg ? rg : nrg - 1; };  // partial block: repeat (not stored)
+  const int64_t b_off = codes_tile_offset(clamp_rg(it.n0 / 16 + wave * C::B_CP), 0, K);
+  static_assert(C::B_CP == 1 && C::WSCP == 1, "one weight row group per wave");
+  const int NQ = (KT + 3) / 4;
+  auto issue_scales = [&](int q) {
+    q = q < NQ ? q : NQ - 1;
+    copy4(s_lane + scales_group_offset(clamp_rg(it.n0 / 16 + wave), q, K),
+          lds + C::WS_OFF + ((q & 1) * C::NRG + wave) * 256);
+  };
+  auto slot = [&](int kt) { return lds + (kt % S) * C::A_STAGE; };
+  auto bslot = [&](int kt) { return lds + C::B_RING + (kt % S) * C::B_BYTES; };
+  auto issue = [&](int kt) {
+    const int k = kt < KT ? kt : KT - 1;
+    copy16_nt(b_lane + b_off + (int64_t)k * 1024, bslot(kt) + wave * 1024);
+#pragma unroll
+    for (int jj = 0; jj < C::A_CP; ++jj) {
+      const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);
+      copy16(a_src[jj] + (int64_t)k * act_row_bytes(AF), slot(kt) + j * 1024);
+    }
+    if constexpr (!C::RS) copy4(as_src + (int64_t)k * 4, slot(kt) + C::A_BYTES + (wave % C::AS_CHUNKS) * 256);
+  };
+
+  struct Frag {
+    i32x8_t A[RB];
+    uint32_t as[RB];
+    u32x4_t B[WN];
+  };
+  auto load_frag = [&](Frag& f, int kt) {
+    if constexpr (C::RS) kt = kt < KT ? kt : KT - 1;  // (operands past K are not used)
+    const uint8_t* as_ = slot(kt);
+    const uint8_t* bs_ = bslot(kt);
+#pragma unroll
+    for (int cb = 0; cb < WN; ++cb) f.B[cb] = *reinterpret_cast<const u32x4_t*>(bs_ + (wn * WN + cb) * 1024 + lane * 16);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = C::rowblock(wm, rb) * 16 + (lane & 15);
+      if constexpr (AF == kActFp8) {
+        // 8-bit A elements: lane group g supplies K 16 g .. 16 g + 15 and
+        // 64 + 16 g .. 64 + 16 g + 15 (logical chunks g and 4 + g), with the
+        // scale of block g as for E2M1 (the MFMA reads block b's scale from
+        // lane group b)
+        const int sw = (row >> 1) & 7;
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(as_ + row * 128 + (g ^ sw) * 16);
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(as_ + row * 128 + ((4 + g) ^ sw) * 16);
+        f.A[rb] = (i32x8_t){(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                            (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+      } else {
+        const int phys = g ^ ((row >> 2) & 3);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(as_ + row * 64 + phys * 16);
+        f.A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+      }
+      if constexpr (C::RS)
+        f.as[rb] = rs[row * RSB + (((kt >> 2) ^ ((row >> 1) & rs_sw)) << 4) + 4 * (kt & 3) + g];
+      else
+        f.as[rb] = as_[C::A_BYTES + row * 4 + g];
+    }
+  };
+  uint32_t scur[WN];  // this wave's scale dwords of the current 4-k-tile group
+  auto mfma_frag = [&](const Frag& f, int kt) {
+#pragma unroll
+    for (int cb = 0; cb < WN; ++cb) {
+      const uint32_t sb = (scur[cb] >> (8 * (kt & 3))) & 0xFFu;
+      const i32x8_t B = {(int)f.B[cb][0], (int)f.B[cb][1], (int)f.B[cb][2], (int)f.B[cb][3], 0, 0, 0, 0};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f.A[rb], B, acc[rb][cb], AF == kActFp8 ? 0 : 4, 4, 0, (int)f.as[rb], 0, (int)sb);
+    }
+  };
+  // the wave's own LDS reads complete (lgkmcnt(0)), then the barrier; no
+  // memory fence: an LDS release fence would also wait for every
+  // global->LDS copy in flight (they write LDS), draining the ring each step
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: the first scale group, every slot's copies (k-tiles
+  // 0 .. S-1), then k-tile 0's operands
+  issue_scales(0);
+#pragma unroll
+  for (int p = 0; p < S; ++p) issue(p);
+  wait_vm<(S - 1) * (C::B_CP + C::OPS_A)>();
+  barrier();
+  Frag F[2];
+  load_frag(F[0], 0);
+  // ---- step kt: wait for k-tile kt + 1's copies, barrier, (group start)
+  // scale dwords and the next group's scale copies, refill slot kt with
+  // k-tile kt + S, read k-tile kt + 1's operands, MFMAs of k-tile kt
+  auto step = [&](int kt, int j, auto wait) {
+    wait();
+    barrier();
+    if (j == 0) {
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb)
+        scur[cb] = *reinterpret_cast<const uint32_t*>(
+            lds + C::WS_OFF + (((kt >> 2) & 1) * C::NRG + wn * WN + cb) * 256 + lane * 4);
+      issue_scales((kt >> 2) + 1);
+    }
+    issue(kt + S);
+    load_frag(F[(j + 1) & 1], kt + 1);
+    mfma_frag(F[j & 1], kt);
+  };
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+    const bool first = kt0 == 0;
+    step(kt0, 0, [&] { if (first) wait_vm_dyn<C::pf_max_after()>(C::pf_after(0)); else wait_vm<C::pf_after(4)>(); });
+    if (kt0 + 1 < KT)
+      step(kt0 + 1, 1, [&] { if (first) wait_vm_dyn<C::pf_max_after()>(C::pf_after(1)); else wait_vm<C::pf_after(5)>(); });
+    if (kt0 + 2 < KT)
+      step(kt0 + 2, 2, [&] { if (first) wait_vm_dyn<C::pf_max_after()>(C::pf_after(2)); else wait_vm<C::pf_after(6)>(); });
+    if (kt0 + 3 < KT)
+      step(kt0 + 3, 3, [&] { if (first) wait_vm_dyn<C::pf_max_after()>(C::pf_after(3)); else wait_vm<C::pf_after(7)>(); });
+  }
+  // the copies issued past K land before the workgroup ends
+  wait_vm<0>();
 }
 
 }  // namespace
 
 // gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
-template <int AF, int NRG>
+template <int AF, typename C>
 __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AF, NRG>;
-  constexpr int WN = C::WN;
+  constexpr int WN = C::WN, RB = C::RB;
   zero_duty(a);
   const int64_t H = a.K, I = a.N / 2;
   const int ntl = (int)((a.N + C::NT - 1) / C::NT);
   TileItem it;
   if (!tile_item(a, ntl, C::NT, &it)) return;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
-  for (int r = threadIdx.x; r < kMT; r += blockDim.x)
+  for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
     rowidx[r] = a.sorted[it.p0 + (r < it.rows ? r : 0)] / a.top_k;  // token of the tile row
   __syncthreads();
-  f32x4_t acc[4][WN];
+  f32x4_t acc[RB][WN];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AF, NRG>(a, it, H, a.N, lds, acc);
+  if constexpr (C::PF)
+    tile_mainloop_pf<AF, C>(a, it, H, a.N, lds, acc);
+  else
+    tile_mainloop<AF, C>(a, it, H, a.N, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::WMW, wn = wave / C::WMW;
   const int nrg = (int)(a.N / 16);
   // row groups (2f, 2f+1) of the wave hold gate and up of feature group
   // (n0/16 + WN wn + 2f) / 2
@@ -410,10 +699,10 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
     if (rg >= nrg) break;
     const int64_t n = (int64_t)(rg / 2) * 16 + (lane & 15);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + rb * 16 + 4 * (lane >> 4) + r;
+        const int row = C::rowblock(wm, rb) * 16 + 4 * (lane >> 4) + r;
         if (row < it.rows) {
           const float v = swiglu_clamped(acc[rb][2 * f][r], acc[rb][2 * f + 1][r], a.clamp_limit);
           a.act[(it.p0 + row) * I + n] = (uint16_t)f32_to_bf16_bits(v);
@@ -423,34 +712,36 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
 }
 
 // down + combine.
-template <int AF, bool ORDERED, int NRG>
+template <int AF, bool ORDERED, typename C>
 __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  using C = Cfg<AF, NRG>;
-  constexpr int WN = C::WN;
+  constexpr int WN = C::WN, RB = C::RB;
   const int64_t I = a.K, H = a.N;
   const int ntl = (int)((a.N + C::NT - 1) / C::NT);
   TileItem it;
   if (!tile_item(a, ntl, C::NT, &it)) return;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
-  for (int r = threadIdx.x; r < kMT; r += blockDim.x)
+  for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
     rowidx[r] = (int32_t)(it.p0 + (r < it.rows ? r : 0));  // sorted position of the tile row
   __syncthreads();
-  f32x4_t acc[4][WN];
+  f32x4_t acc[RB][WN];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  tile_mainloop<AF, NRG>(a, it, I, H, lds, acc);
+  if constexpr (C::PF)
+    tile_mainloop_pf<AF, C>(a, it, I, H, lds, acc);
+  else
+    tile_mainloop<AF, C>(a, it, I, H, lds, acc);
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::WMW, wn = wave / C::WMW;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wm * 64 + rb * 16 + 4 * (lane >> 4) + r;
+      const int row = C::rowblock(wm, rb) * 16 + 4 * (lane >> 4) + r;
       if (row >= it.rows) continue;
       const int64_t p = it.p0 + row;
       int64_t tok = 0;
@@ -474,6 +765,13 @@ __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------ launchers
 namespace {
+// 128 x 512 tiles (bf16 prefill and large MX calls) and 320 x 128 tiles (MX
+// calls whose experts hold up to 320 rows)
+template <int AF>
+using Cfg128 = Cfg<AF, 2, 4, 8, false, AF == kActFp4 ? 3 : 2, AF == kActFp4 ? 3 : 2>;
+template <int AF>
+using Cfg320 = Cfg<AF, 4, 5, 4, true, AF == kActFp8 ? 3 : 4, AF == kActFp8 ? 3 : 4, true, AF == kActFp4>;
+
 int64_t tile_grid(int64_t max_tiles, int64_t N, int nt) {
   const int64_t items = max_tiles * ((N + nt - 1) / nt);
   return 8 * ((items + 7) / 8);
@@ -487,49 +785,60 @@ hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
     attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds);
+                               (int)kTileLdsMax);
   });
   if (attr != hipSuccess) return attr;
+  if (lds > kTileLdsMax) return hipErrorInvalidValue;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int AF, int NRG>
-hipError_t gate_up_af(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
-  return launch_lds(tile_gate_up_kernel<AF, NRG>, grid, Cfg<AF, NRG>::LDS, a, s);
+template <int AF, typename C>
+hipError_t gate_up_c(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, C::NT);
+  return launch_lds(tile_gate_up_kernel<AF, C>, grid, C::lds_bytes(a.K), a, s);
 }
-template <int AF, int NRG>
-hipError_t down_af(const GemmArgs& a, int64_t max_tiles, bool ordered, hipStream_t s) {
-  const int64_t grid = tile_grid(max_tiles, a.N, 16 * NRG);
-  return ordered ? launch_lds(tile_down_kernel<AF, true, NRG>, grid, Cfg<AF, NRG>::LDS, a, s)
-                 : launch_lds(tile_down_kernel<AF, false, NRG>, grid, Cfg<AF, NRG>::LDS, a, s);
-}
-
-template <int NRG>
-hipError_t gate_up_nrg(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t s) {
-  if (af == kActFp8) return gate_up_af<kActFp8, NRG>(a, max_tiles, s);
-  return af == kActFp4 ? gate_up_af<kActFp4, NRG>(a, max_tiles, s) : gate_up_af<kActBf16, NRG>(a, max_tiles, s);
+template <int AF, typename C>
+hipError_t down_c(const GemmArgs& a, int64_t max_tiles, bool ordered, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, C::NT);
+  return ordered ? launch_lds(tile_down_kernel<AF, true, C>, grid, C::lds_bytes(a.K), a, s)
+                 : launch_lds(tile_down_kernel<AF, false, C>, grid, C::lds_bytes(a.K), a, s);
 }
 
-template <int NRG>
-hipError_t down_nrg(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
-  if (af == kActFp8) return down_af<kActFp8, NRG>(a, max_tiles, ordered, s);
-  return af == kActFp4 ? down_af<kActFp4, NRG>(a, max_tiles, ordered, s)
-                       : down_af<kActBf16, NRG>(a, max_tiles, ordered, s);
+template <int AF>
+hipError_t gate_up_af(const GemmArgs& a, int64_t max_tiles, int mt, hipStream_t s) {
+  if constexpr (AF != kActBf16)
+    if (mt == Cfg320<AF>::MT) return gate_up_c<AF, Cfg320<AF>>(a, max_tiles, s);
+  if (mt != Cfg128<AF>::MT) return hipErrorInvalidValue;
+  return gate_up_c<AF, Cfg128<AF>>(a, max_tiles, s);
+}
+template <int AF>
+hipError_t down_af(const GemmArgs& a, int64_t max_tiles, int mt, bool ordered, hipStream_t s) {
+  if constexpr (AF != kActBf16)
+    if (mt == Cfg320<AF>::MT) return down_c<AF, Cfg320<AF>>(a, max_tiles, ordered, s);
+  if (mt != Cfg128<AF>::MT) return hipErrorInvalidValue;
+  return down_c<AF, Cfg128<AF>>(a, max_tiles, ordered, s);
 }
 }  // namespace
 
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, hipStream_t s) {
-  if (max_tiles <= 0) return hipSuccess;
-  return tile_nrg() == 16 ? gate_up_nrg<16>(a, max_tiles, af, s) : gate_up_nrg<32>(a, max_tiles, af, s);
+bool tile_fits(int af, int mt, int64_t K) {
+  if (mt == 128) return true;
+  if (mt != 320 || af == kActBf16) return false;
+  return af == kActFp4 ? Cfg320<kActFp4>::lds_bytes(K) <= kTileLdsMax : Cfg320<kActFp8>::lds_bytes(K) <= kTileLdsMax;
 }
 
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  return tile_nrg() == 16 ? down_nrg<16>(a, max_tiles, af, ordered, s)
-                          : down_nrg<32>(a, max_tiles, af, ordered, s);
+  if (af == kActFp8) return gate_up_af<kActFp8>(a, max_tiles, mt, s);
+  return af == kActFp4 ? gate_up_af<kActFp4>(a, max_tiles, mt, s) : gate_up_af<kActBf16>(a, max_tiles, mt, s);
+}
+
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool ordered, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  if (af == kActFp8) return down_af<kActFp8>(a, max_tiles, mt, ordered, s);
+  return af == kActFp4 ? down_af<kActFp4>(a, max_tiles, mt, ordered, s)
+                       : down_af<kActBf16>(a, max_tiles, mt, ordered, s);
 }
 
 }  // namespace mxmoe

@@ -69,6 +69,10 @@ A4_CASES = {
     # 16-row kernels with 6 (gate_up, 48 k-tiles) and 7 (down, 56 k-tiles)
     # k-tiles per wave: a wave's scale bytes span up to three dwords
     "a4_wide": W.WORKLOADS["a4"].replace(T=4, H=6144, I=7168, E_global=4, E_local=4, top_k=2),
+    # 320-row tiles with skewed routing: the hottest experts take several
+    # tiles, a cold one a partial tile
+    "a4_skew": W.WORKLOADS["a4"].replace(T=1024, H=512, I=256, E_global=16, E_local=16, top_k=4,
+                                         logits_kind="zipf_bias"),
 }
 A8_CASES = {
     "a8_tiny": W.WORKLOADS["a8"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
@@ -79,6 +83,8 @@ A8_CASES = {
     "a8_decode": W.WORKLOADS["a8"].replace(T=16, H=2048, I=1536, E_global=64, E_local=64, top_k=8),
     # 16-row kernels with 7 (gate_up) and 5 (down) k-tiles per wave
     "a8_wide": W.WORKLOADS["a8"].replace(T=4, H=7168, I=5120, E_global=4, E_local=4, top_k=2),
+    "a8_skew": W.WORKLOADS["a8"].replace(T=1024, H=512, I=256, E_global=16, E_local=16, top_k=4,
+                                         logits_kind="zipf_bias"),
 }
 
 
