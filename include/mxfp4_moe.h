@@ -149,15 +149,37 @@ int mxfp4_moe_preshuffle(const mxfp4_moe_dims* d, const uint8_t* canon_w13,
                          const uint8_t* canon_w2s, uint8_t* w13, uint8_t* w13s, uint8_t* w2,
                          uint8_t* w2s, hipStream_t stream);
 
+/*
+ * Load-time weight conversion in one pass: unquantised expert weights ->
+ * the preshuffled MXFP4 tensors of mxfp4_moe_preshuffle, with no canonical
+ * intermediate.  The conversion packs 4-bit values with a shared block scale
+ * per expert tensor (campaign page "glm53-mxfp4-mi355x", section "The
+ * baseline is already one byte, and the exclusions are two") and is paid once,
+ * at load time, not per step (XFP blog, section "编码成本").
+ * Inputs (device, in_dtype MXFP4_MOE_DTYPE_F32 or _BF16; E_local + 1 experts
+ * with MXFP4_MOE_SHARED_EXPERT): w13 [E_local][2I][H] (rows 0..I-1 gate,
+ * I..2I-1 up), w2 [E_local][H][I].  Each 32-element block along K is quantised
+ * by the rule of mxfp4_moe_quantize.  Outputs: as mxfp4_moe_preshuffle's
+ * (sizes from mxfp4_moe_preshuffled_bytes; the scale padding to whole
+ * 512-element K groups is written as zeros).  Byte-identical to
+ * mxfp4_moe_quantize per expert followed by mxfp4_moe_preshuffle.
+ * Errors: as mxfp4_moe_preshuffle, BAD_ARGUMENT for another in_dtype.
+ */
+int mxfp4_moe_quantize_preshuffle(const mxfp4_moe_dims* d, const void* w13, const void* w2,
+                                  int32_t in_dtype, uint8_t* w13_out, uint8_t* w13s_out,
+                                  uint8_t* w2_out, uint8_t* w2s_out, hipStream_t stream);
+
 /* Workspace bytes mxfp4_moe_forward / mxfp4_moe_route need for these dims and top_k. */
 int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* bytes);
 
 /*
  * How mxfp4_moe_forward will run these dims and top_k (a pure host query):
- * *tile_rows = token rows per GEMM tile (16: K split across waves, for
- * decode-sized calls; 128: LDS-staged large tiles); *ordered_combine = 1 when
- * the combine gathers slot-ordered y rows (deterministic), 0 when it adds
- * into an fp32 buffer with atomics.  The large-tile plan always gathers.
+ * *tile_rows = token rows per gate_up tile (16: K split across waves, for
+ * decode-sized calls; 64; 128: LDS-staged large tiles; 320: with MXFP4
+ * activations, one tile per expert of up to 320 rows, down then on 128-row
+ * tiles); *ordered_combine = 1 when the combine gathers slot-ordered y rows
+ * (deterministic), 0 when it adds into an fp32 buffer with atomics.  The
+ * large-tile plans always gather.
  * Errors as mxfp4_moe_workspace_bytes; NULL outputs -> NULL_POINTER.
  */
 int mxfp4_moe_plan(const mxfp4_moe_dims* d, int32_t top_k, int32_t* tile_rows, int32_t* ordered_combine);

@@ -69,7 +69,8 @@ EXPORTED = ("mxfp4_moe_abi_version", "mxfp4_moe_status_string", "mxfp4_moe_last_
             "mxfp4_moe_preshuffled_bytes", "mxfp4_moe_preshuffle", "mxfp4_moe_workspace_bytes",
             "mxfp4_moe_forward", "mxfp4_moe_forward_debug", "mxfp4_moe_forward_timed",
             "mxfp4_moe_route", "mxfp4_moe_quantize", "mxfp4_moe_quantize8", "mxfp4_moe_plan",
-            "mxfp4_moe_preshuffle_fused", "mxfp4_moe_forward_mixed", "mxfp4_moe_forward_noalloc")
+            "mxfp4_moe_preshuffle_fused", "mxfp4_moe_forward_mixed", "mxfp4_moe_forward_noalloc",
+            "mxfp4_moe_quantize_preshuffle")
 
 
 def load_library(path: str = LIB_PATH):
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_moe_plan.argtypes = [D, I32, PI32, PI32]
     lib.mxfp4_moe_forward.restype = ctypes.c_int
     lib.mxfp4_moe_forward.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]
+    lib.mxfp4_moe_quantize_preshuffle.restype = ctypes.c_int
+    lib.mxfp4_moe_quantize_preshuffle.argtypes = [D, P, P, I32, P, P, P, P, P]
     lib.mxfp4_moe_forward_noalloc.restype = ctypes.c_int
     lib.mxfp4_moe_forward_noalloc.argtypes = [D, P, P, P, P, P, P, I32, ctypes.c_float, P, P]
     lib.mxfp4_moe_forward_debug.restype = ctypes.c_int
@@ -195,6 +198,21 @@ def mxfp4_moe_preshuffle(dims: Dims, w13, w13s, w2, w2s):
     _check("mxfp4_moe_preshuffle",
            _L().mxfp4_moe_preshuffle(ctypes.byref(dims), _p(w13), _p(w13s), _p(w2), _p(w2s),
                                      *[_p(o) for o in outs], _stream()))
+    return tuple(outs)
+
+
+def mxfp4_moe_quantize_preshuffle(dims: Dims, w13, w2):
+    """Unquantised expert weights (float32 or bf16 device tensors, w13 [E, 2I, H],
+    w2 [E, H, I]) -> preshuffled MXFP4 (w13, w13s, w2, w2s) in one pass."""
+    in_dtype = DTYPE_BF16 if w13.dtype == torch.bfloat16 else DTYPE_F32
+    want = torch.bfloat16 if in_dtype == DTYPE_BF16 else torch.float32
+    _dev_tensor(w13, want, "w13")
+    _dev_tensor(w2, want, "w2")
+    sizes = mxfp4_moe_preshuffled_bytes(dims)
+    outs = [torch.empty(n, dtype=torch.uint8, device=w13.device) for n in sizes]
+    _check("mxfp4_moe_quantize_preshuffle",
+           _L().mxfp4_moe_quantize_preshuffle(ctypes.byref(dims), _p(w13), _p(w2), int(in_dtype),
+                                              *[_p(o) for o in outs], _stream()))
     return tuple(outs)
 
 

@@ -610,6 +610,43 @@ int mxfp4_moe_preshuffle(const mxfp4_moe_dims* d, const uint8_t* canon_w13, cons
   return MXFP4_MOE_OK;
 }
 
+int mxfp4_moe_quantize_preshuffle(const mxfp4_moe_dims* d, const void* w13, const void* w2, int32_t in_dtype,
+                                  uint8_t* w13_out, uint8_t* w13s_out, uint8_t* w2_out, uint8_t* w2s_out,
+                                  hipStream_t stream) {
+  Shape s;
+  int st = check_dims(d, 1, false, &s);
+  if (st) return st;
+  if (in_dtype != MXFP4_MOE_DTYPE_BF16 && in_dtype != MXFP4_MOE_DTYPE_F32) return MXFP4_MOE_ERR_BAD_ARGUMENT;
+  int64_t n, bytes;
+  if (!mul_ok(2 * s.I, s.H, &n) || !mul_ok(n, s.El, &n) || !mul_ok(n, 4, &bytes)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
+  if (!w13 || !w2 || !w13_out || !w13s_out || !w2_out || !w2s_out) return MXFP4_MOE_ERR_NULL_POINTER;
+  if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_out, 16) || !aligned(w2_out, 16) ||
+      !aligned(w13s_out, 4) || !aligned(w2s_out, 4))
+    return MXFP4_MOE_ERR_MISALIGNED;
+  st = check_device();
+  if (st) return st;
+  QuantPreshuffleArgs q;
+  q.in = w13;
+  q.in_dtype = in_dtype;
+  q.codes = w13_out;
+  q.scales = w13s_out;
+  q.E = s.El;
+  q.N = 2 * s.I;
+  q.K = s.H;
+  q.interleave_gate_up = 1;
+  hipError_t e = launch_quantize_preshuffle(q, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  q.in = w2;
+  q.codes = w2_out;
+  q.scales = w2s_out;
+  q.N = s.H;
+  q.K = s.I;
+  q.interleave_gate_up = 0;
+  e = launch_quantize_preshuffle(q, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MXFP4_MOE_OK;
+}
+
 int mxfp4_moe_workspace_bytes(const mxfp4_moe_dims* d, int32_t top_k, size_t* bytes) {
   Shape s;
   int st = check_dims(d, top_k, true, &s);

@@ -128,6 +128,16 @@ struct QuantArgs {
   int32_t fp8;           // 1: E4M3 elements (MXFP8)
 };
 
+// fp32 / bf16 weights [E][N][K] -> preshuffled MXFP4 in one pass
+struct QuantPreshuffleArgs {
+  const void* in;
+  int32_t in_dtype;              // 0 bf16, 1 f32
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t E, N, K;
+  int32_t interleave_gate_up;    // 1 for w13
+};
+
 struct PreshuffleArgs {
   const uint8_t* canon_codes;   // [E][N][K/2]
   const uint8_t* canon_scales;  // [E][N][K/32]
@@ -189,6 +199,7 @@ hipError_t launch_bf16x_gate_up(const XArgs& a, hipStream_t stream);
 hipError_t launch_bf16x_down(const XArgs& a, bool ordered, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_preshuffle(const PreshuffleArgs& a, hipStream_t stream);
+hipError_t launch_quantize_preshuffle(const QuantPreshuffleArgs& a, hipStream_t stream);
 hipError_t launch_copy_rows(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 

@@ -108,6 +108,71 @@ __global__ __launch_bounds__(256) void preshuffle_scales_kernel(PreshuffleArgs a
   a.scales[o] = v;
 }
 
+// Load-time conversion in one pass: fp32 or bf16 expert weights [E][N][K]
+// (canonical row order; w13: gate rows then up rows) -> preshuffled MXFP4.
+// One thread per (expert, row group, K-block of the padded K, row in group):
+// it quantises the 32 elements of that block (the OCP rule of
+// quantize_kernel) and writes the 16 code bytes and the scale byte where
+// preshuffle_codes_kernel / preshuffle_scales_kernel put them; a block past K
+// (the scale groups' padding) only writes a zero scale byte.
+__global__ __launch_bounds__(256) void quantize_preshuffle_kernel(QuantPreshuffleArgs a) {
+  const int64_t nblk = a.K / 32;
+  const int64_t sg = scale_groups(a.K);
+  const int64_t pblk = sg * 16;                      // K-blocks incl. padding
+  const int64_t per_rg = pblk * 16;                  // threads per row group
+  const int64_t per_expert = (a.N / 16) * per_rg;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.E * per_expert) return;
+  const int64_t e = t / per_expert;
+  int64_t rem = t % per_expert;
+  const int64_t rg = rem / per_rg;
+  rem %= per_rg;
+  const int64_t b = rem / 16, r = rem % 16;          // K-block, row in group
+  const int64_t row = a.interleave_gate_up ? ((rg & 1) ? a.N / 2 : 0) + (rg >> 1) * 16 + r : rg * 16 + r;
+  // preshuffled scale byte: [rg][kt/4][lane = 16 (b % 4) + r][kt % 4], kt = b / 4
+  const int64_t kt = b / 4;
+  uint8_t* sdst = a.scales + e * scales_per_expert(a.N, a.K) + scales_group_offset(rg, kt / 4, a.K) +
+                  ((b % 4) * 16 + r) * 4 + kt % 4;
+  if (b >= nblk) {
+    *sdst = 0;
+    return;
+  }
+  float v[32];
+  if (a.in_dtype == 0) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.in) + (e * a.N + row) * a.K + b * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4_t w = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[q * 8 + 2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[q * 8 + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(a.in) + (e * a.N + row) * a.K + b * 32;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f32x4_t w = *reinterpret_cast<const f32x4_t*>(p + q * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[q * 4 + i] = w[i];
+    }
+  }
+  uint32_t packed[4], sc;
+  mx_quantize_block32(v, packed, &sc);
+  // preshuffled codes: [rg][b][r][16 bytes]
+  *reinterpret_cast<u32x4_t*>(a.codes + e * codes_per_expert(a.N, a.K) + rg * 16 * (a.K / 2) + (b * 16 + r) * 16) =
+      (u32x4_t){packed[0], packed[1], packed[2], packed[3]};
+  *sdst = (uint8_t)sc;
+}
+
+hipError_t launch_quantize_preshuffle(const QuantPreshuffleArgs& a, hipStream_t s) {
+  const int64_t n = a.E * (a.N / 16) * scale_groups(a.K) * 16 * 16;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_preshuffle_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int64_t nb = a.rows * (a.K / 32);
   if (nb == 0) return hipSuccess;

@@ -136,14 +136,20 @@ def test_plan_query(lib):
     # many rows per expert: large tiles, always the slot-ordered gather
     big = mx.mxfp4_moe_plan(dims(T=4096, E_global=8, E_local=8), 2)
     assert big == {"tile_rows": 128, "ordered_combine": True}
+    # MXFP4 activations: 320-row gate_up tiles while they hold a whole expert
+    # and its scale rows fit LDS (K <= 4352), else 128
+    assert mx.mxfp4_moe_plan(dims(T=1024, H=4352, flags=mx.MXFP4_MOE_A4), 2)["tile_rows"] == 320
+    assert mx.mxfp4_moe_plan(dims(T=1024, H=4480, flags=mx.MXFP4_MOE_A4), 2)["tile_rows"] == 128
+    assert mx.mxfp4_moe_plan(dims(T=4096, flags=mx.MXFP4_MOE_A4), 2)["tile_rows"] == 128
     # speculative-verify shapes of the decode layer (T = 6 per sequence): the
     # tile height follows the expected rows per expert T*k/E_global
     from mxfp4_block_scaled_router_amd import workloads as W
     want = {"verify_b1": 16, "verify_b8": 16, "verify_b16": 16, "verify_b32": 16, "verify_b48": 64,
-            "decode": 16, "ep_share": 16, "prefill": 128, "a4": 128}
+            "decode": 16, "ep_share": 16, "prefill": 128, "a4": 320, "a8": 128}
     for name, rows in want.items():
         wl = W.WORKLOADS[name]
-        d = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4)
+        d = mx.Dims.make(wl.T, wl.H, wl.I, wl.E_global, wl.E_local, wl.first_local, a4=wl.a4,
+                         a8=wl.a8)
         assert mx.mxfp4_moe_plan(d, wl.top_k)["tile_rows"] == rows, name
     out = ctypes.c_int32()
     assert lib.mxfp4_moe_plan(ctypes.byref(dims()), 2, None, ctypes.byref(out)) == NULL_POINTER
@@ -312,3 +318,15 @@ def test_noalloc_refusals(lib):
                   (dict(T=256, H=5120, I=1536, E_global=256, E_local=64, flags=0x2), 8)):
         st, n = ws_status(dims(**kw), k)
         assert st == OK and n <= 64 << 20, (kw, n)
+
+
+def test_quantize_preshuffle_refusals(lib):
+    f = lib.mxfp4_moe_quantize_preshuffle
+    P = 1 << 20
+    d = dims()
+    assert f(None, P, P, 1, P, P, P, P, None) == NULL_POINTER
+    assert f(ctypes.byref(d), P, P, 2, P, P, P, P, None) == BAD_ARGUMENT
+    assert f(ctypes.byref(d), None, P, 1, P, P, P, P, None) == NULL_POINTER
+    assert f(ctypes.byref(d), P + 4, P, 1, P, P, P, P, None) == MISALIGNED
+    assert f(ctypes.byref(dims(H=500)), P, P, 1, P, P, P, P, None) == UNSUPPORTED_SHAPE
+    assert f(ctypes.byref(d), P, P, 1, P, P, P, P, None) == UNSUPPORTED_DEVICE

@@ -353,6 +353,45 @@ def test_ep_shares_sum_to_full_layer():
     assert np.abs(acc - o.out32).max() <= 4 * 2e-2 * rms
 
 
+def test_ep_shares_sum_to_full_layer_full_shape():
+    """Expert parallelism at the expert-parallel share's real shape: the four
+    shares (first_local = 0, 64, 128, 192) of 256 global experts at T = 256,
+    H = 5120, I = 1536, each run through the C ABI on its own 64 experts,
+    summed; compared on sampled tokens with the oracle's whole 256-expert
+    layer.  The fp32 partial outputs sum to the layer within the bar; the sum
+    of the four bf16 partial outputs within four roundings more."""
+    base = W.WORKLOADS["ep_share"]
+    full_wl = base.replace(name="ep_full", E_local=256)
+    inp = W.make_inputs(full_wl)
+    mask = _sample_mask(full_wl.T, 12, 7)
+    log("oracle: whole layer, 256 experts, %d sampled tokens" % mask.sum())
+    o = oracle.moe_forward(inp["x"], inp["logits"], inp["w13"], inp["w13s"], inp["w2"], inp["w2s"],
+                           top_k=full_wl.top_k, clamp_limit=full_wl.clamp_limit, E_global=256,
+                           first_local=0, token_mask=mask, want_act=False)
+    acc32 = np.zeros((full_wl.T, full_wl.H), np.float64)
+    acc16 = np.zeros((full_wl.T, full_wl.H), np.float64)
+    for f in range(0, 256, 64):
+        sub = {"x": inp["x"], "logits": inp["logits"]}
+        for k in ("w13", "w13s", "w2", "w2s"):
+            sub[k] = inp[k][f:f + 64]
+        wl = base.replace(first_local=f)
+        log("share first_local=%d" % f)
+        c = Case(wl, inp=sub)
+        g = c.run_gpu(debug=True)
+        acc32 += g["out32"].cpu().numpy().astype(np.float64)
+        acc16 += g["out"].float().cpu().numpy().astype(np.float64)
+        del c, g
+        torch.cuda.empty_cache()
+    rows = np.nonzero(mask)[0]
+    ref = o.out32[rows].astype(np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err32 = np.abs(acc32[rows] - ref).max()
+    err16 = np.abs(acc16[rows] - ref).max()
+    log("  fp32 partials max err / rms %.3e, bf16 partials %.3e" % (err32 / rms, err16 / rms))
+    assert err32 <= 2e-2 * rms
+    assert err16 <= 4 * 2e-2 * rms
+
+
 def test_forward_prefill_full_sampled():
     case = Case(W.WORKLOADS["prefill"])
     _check_case(case, token_mask=_sample_mask(case.wl.T, 24, 2))
