@@ -330,6 +330,36 @@ __device__ __forceinline__ void share_of(int64_t U, int64_t* ub, int64_t* ue, in
   share_bounds(U, blockIdx.x, gridDim.x, cus, c, ub, ue);
 }
 
+// Units sliced by XCD.  Workgroup b runs on XCD b % 8 (round-robin
+// dispatch).  When the feature blocks per tile FB, the grid and the slot CU
+// count divide by 8, XCD x owns the feature blocks fb = x, x + 8, x + 16, ...
+// of every tile: its workgroups split the XCD's units v = tile * (FB / 8) +
+// fb / 8 into shares as above (b / 8 among G / 8, on cus / 8 CUs), and unit
+// v's feature block is 8 (v % (FB / 8)) + x.  An expert with several tiles
+// then streams each of its weight slices into one XCD's L2 once, where its
+// other tiles find it (with contiguous shares every XCD would stream the whole
+// expert, too much for its L2).
+constexpr int kXcds = 8;
+struct UnitMap {
+  int fbv;     // feature blocks per tile in this workgroup's numbering (FB or FB / 8)
+  int step;    // feature block of virtual block j: step * j + first
+  int first;
+  __device__ int fb(int j) const { return step * j + first; }
+};
+__device__ __forceinline__ bool xcd_sliced(int FB, unsigned G, int cus) {
+  return FB % kXcds == 0 && G % kXcds == 0 && (cus == 0 || cus % kXcds == 0);
+}
+// the share [ub, ue) of workgroup b (units in its numbering) and the numbering
+__device__ __forceinline__ UnitMap unit_share(int64_t ntiles, int FB, unsigned b, unsigned G, int cus, float c,
+                                              int64_t* ub, int64_t* ue) {
+  if (xcd_sliced(FB, G, cus)) {
+    share_bounds(ntiles * (FB / kXcds), b / kXcds, G / kXcds, cus / kXcds, c, ub, ue);
+    return UnitMap{FB / kXcds, kXcds, (int)(b % kXcds)};
+  }
+  share_bounds(ntiles * FB, b, G, cus, c, ub, ue);
+  return UnitMap{FB, 1, 0};
+}
+
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
 // up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
 // ROUTE: every workgroup first routes the tokens itself (route_block_masks, or
@@ -374,13 +404,12 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     ntiles = __builtin_amdgcn_readfirstlane(rl.t1[ra.E_local]);
     if (blockIdx.x == 0 && a.dn_desc) {
       // the down kernel's shares and first tiles (its tile table is this one)
-      const int64_t Ud = (int64_t)ntiles * a.dn_fb;
       for (int b = threadIdx.x; b < a.dn_grid; b += blockDim.x) {
         int64_t dub, due;
-        share_bounds(Ud, (unsigned)b, (unsigned)a.dn_grid, a.dn_cus, a.dn_c, &dub, &due);
+        const UnitMap dm = unit_share(ntiles, a.dn_fb, (unsigned)b, (unsigned)a.dn_grid, a.dn_cus, a.dn_c, &dub, &due);
         int4 d0 = make_int4((int)dub, (int)due, 0, 0), d1 = make_int4(0, 0, 0, 0);
         if (dub < due) {
-          const int t = (int)(dub / a.dn_fb);
+          const int t = (int)(dub / dm.fbv);
           const int4 ti = rl.tiles[t];
           d0.z = ti.x;
           d0.w = ti.y;
@@ -395,7 +424,8 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     ntiles = tile_count(a);
   }
   int64_t ub, ue;
-  share_of((int64_t)ntiles * FB, &ub, &ue, a.slot_cus, a.slot_c);
+  const UnitMap um = unit_share(ntiles, FB, blockIdx.x, gridDim.x, a.slot_cus, a.slot_c, &ub, &ue);
+  const int FBV = um.fbv;
   const uint32_t gbytes = (uint32_t)(16 * (H / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(H) * 256);
   const int64_t cpe = codes_per_expert(a.N, H), spe = scales_per_expert(a.N, H);
@@ -404,8 +434,8 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
   // wave 0's reads of it
   int phase = 0;
   for (int64_t sb = ub; sb < ue;) {
-    const int t = (int)(sb / FB);
-    const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
+    const int t = (int)(sb / FBV);
+    const int64_t se = ue < (int64_t)(t + 1) * FBV ? ue : (int64_t)(t + 1) * FBV;
     int4 ti;
     if constexpr (ROUTE) {
       const int4 v = rl.tiles[t];
@@ -418,10 +448,10 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
     const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
-    const int fb0 = (int)(sb - (int64_t)t * FB);
+    const int fb0 = (int)(sb - (int64_t)t * FBV);  // first unit of the segment, in the tile's numbering
     const int nu = (int)(se - sb);
     auto load_unit = [&](int i, WSlice<2, KPW>& w) {
-      const int fb = fb0 + i;
+      const int fb = um.fb(fb0 + i);
       const bool ok = i < nu;
       load_wslice(w, make_rsrc(ecodes + codes_tile_offset(2 * fb, 0, H), ok ? 2 * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(2 * fb, 0, H), ok ? 2 * gsbytes : 0u), gbytes, gsbytes,
@@ -463,7 +493,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
         // unit i sits in slot j; unit i + D refills it as it is consumed
-        const int fbn = fb0 + i + D;
+        const int fbn = um.fb(fb0 + i + D);
         const bool okn = i + D < nu;
         const __amdgpu_buffer_rsrc_t rcn = make_rsrc(ecodes + codes_tile_offset(2 * fbn, 0, H), okn ? 2 * gbytes : 0u);
         const __amdgpu_buffer_rsrc_t rsn =
@@ -477,7 +507,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
         });
         float* rb = red + (phase++ & 1) * (NW * 2 * 64 * 4);
         if (reduce_to_wave0<2>(acc, rb, NW) && i < nu) {
-          const int64_t nn = (int64_t)(fb0 + i) * 16 + r;
+          const int64_t nn = (int64_t)um.fb(fb0 + i) * 16 + r;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int row = 4 * (lane >> 4) + q;
@@ -511,14 +541,18 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   int64_t ub, ue;
   int4 first = make_int4(0, 0, 0, 0);  // with descriptors: the first segment's tile entry
   const bool desc = a.dn_desc && (int)gridDim.x == a.dn_grid;
+  UnitMap um;
   if (desc) {
     const_i32* dp = (const_i32*)a.dn_desc + 8 * (int64_t)blockIdx.x;
     ub = dp[0];
     ue = dp[1];
     first = make_int4(dp[2], dp[3], dp[4], 0);
+    um = xcd_sliced(FB, gridDim.x, a.slot_cus) ? UnitMap{FB / kXcds, kXcds, (int)(blockIdx.x % kXcds)}
+                                                : UnitMap{FB, 1, 0};
   } else {
-    share_of((int64_t)tile_count(a) * FB, &ub, &ue, a.slot_cus, a.slot_c);
+    um = unit_share(tile_count(a), FB, blockIdx.x, gridDim.x, a.slot_cus, a.slot_c, &ub, &ue);
   }
+  const int FBV = um.fbv;
   const uint32_t gbytes = (uint32_t)(16 * (I / 2));
   const uint32_t gsbytes = (uint32_t)(scale_groups(I) * 256);
   const int64_t cpe = codes_per_expert(H, I), spe = scales_per_expert(H, I);
@@ -527,17 +561,17 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   // wave 0's reads of it
   int phase = 0;
   for (int64_t sb = ub; sb < ue;) {
-    const int t = (int)(sb / FB);
-    const int64_t se = ue < (int64_t)(t + 1) * FB ? ue : (int64_t)(t + 1) * FB;
+    const int t = (int)(sb / FBV);
+    const int64_t se = ue < (int64_t)(t + 1) * FBV ? ue : (int64_t)(t + 1) * FBV;
     const int4 ti = desc && sb == ub ? first : tile_entry(a, t);
     const int rows = ti.y;
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
     const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
-    const int fb0 = (int)(sb - (int64_t)t * FB);
+    const int fb0 = (int)(sb - (int64_t)t * FBV);
     const int nu = (int)(se - sb);
     auto load_unit = [&](int i, WSlice<NG, KPW>& w) {
-      const int fb = fb0 + i;
+      const int fb = um.fb(fb0 + i);
       const bool ok = i < nu;
       load_wslice(w, make_rsrc(ecodes + codes_tile_offset(fb * NG, 0, I), ok ? NG * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(fb * NG, 0, I), ok ? NG * gsbytes : 0u), gbytes, gsbytes,
@@ -575,7 +609,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
-        const int fbn = fb0 + i + D;
+        const int fbn = um.fb(fb0 + i + D);
         const bool okn = i + D < nu;
         const __amdgpu_buffer_rsrc_t rcn =
             make_rsrc(ecodes + codes_tile_offset(fbn * NG, 0, I), okn ? NG * gbytes : 0u);
@@ -598,7 +632,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
             if (row < rows) {
 #pragma unroll
               for (int gi = 0; gi < NG; ++gi) {
-                const int64_t nn = ((int64_t)(fb0 + i) * NG + gi) * 16 + r;
+                const int64_t nn = ((int64_t)um.fb(fb0 + i) * NG + gi) * 16 + r;
                 if constexpr (ORDERED) {
                   a.ybuf[(p0 + row) * H + nn] = acc[gi][q];
                 } else {
