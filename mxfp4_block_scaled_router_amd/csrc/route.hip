@@ -121,7 +121,57 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a) {
   }
 }
 
+// (2 + 3) in one launch when the chunk table is small: every workgroup scans
+// the expert-major chunk counts into chunk bases in its own LDS (one wave per
+// expert), the first also writes counts, offsets and the tile tables, then
+// each places its slots.  The slot loads go out before the scan.
+__global__ __launch_bounds__(1024) void route_scan_scatter_kernel(RouteArgs a) {
+  extern __shared__ int32_t lds[];
+  const int E = a.E_local;
+  const int64_t S = a.T * (int64_t)a.top_k;
+  const int nchunk = (int)((S + 63) / 64);
+  int32_t* cnt = lds;                           // [E][nchunk]: counts, then bases
+  int32_t* counts = cnt + (int64_t)E * nchunk;  // [E]
+  int32_t* offs = counts + E;                   // [E + 1]
+  int32_t* t1 = offs + E + 1;                   // [E + 1]
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one slot per thread
+  const bool live = s < S;
+  const int e_s = live ? a.lexp[s] : -1;
+  const int32_t r_s = live ? a.rank[s] : 0;
+  const float w_s = live ? a.w[s] : 0.f;
+  for (int i = threadIdx.x; i < E * nchunk; i += blockDim.x) cnt[i] = a.chunk_cnt[i];
+  __syncthreads();
+  const int lane = lane_id(), nw = blockDim.x / 64;
+  for (int e = threadIdx.x / 64; e < E; e += nw) {
+    int32_t* row = cnt + (int64_t)e * nchunk;
+    int32_t carry = 0;
+    for (int c0 = 0; c0 < nchunk; c0 += 64) {
+      const int c = c0 + lane;
+      const int32_t v = c < nchunk ? row[c] : 0;
+      const int32_t incl = wave_incl_sum(v);
+      if (c < nchunk) row[c] = carry + incl - v;
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) {
+      counts[e] = carry;
+      if (blockIdx.x == 0) a.counts[e] = carry;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) wave_scan_experts(counts, E, a, blockIdx.x == 0, offs, t1);
+  __syncthreads();
+  if (live) {
+    if (e_s >= 0)
+      place_slot(a, s, offs[e_s] + cnt[(int64_t)e_s * nchunk + s / 64] + r_s, w_s, e_s, offs[e_s], t1[e_s]);
+    else
+      a.inv[s] = -1;
+  }
+}
+
 namespace {
+// chunk tables up to this many entries take route_scan_scatter_kernel
+constexpr int64_t kScanScatterMaxEntries = 8192;
+constexpr int64_t kScanScatterMaxSlots = 16 * 1024;
 size_t small_lds_bytes(int64_t S, int64_t E) { return (size_t)route_block_words(S, E, 0) * sizeof(int32_t); }
 int64_t gcd64(int64_t x, int64_t y) { return y ? gcd64(y, x % y) : x; }
 }  // namespace
@@ -145,19 +195,26 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), lds, stream, a);
     return hipGetLastError();
   }
-  // tokens per workgroup: a multiple of 64/gcd(64,k) (whole chunks), at least 16
-  int64_t unit = 64 / gcd64(64, a.top_k);
-  int64_t tpb = unit;
-  while (tpb < 16) tpb += unit;
-  const int64_t nblk = (a.T + tpb - 1) / tpb;
   // more than 64 experts and few tokens: one wave per token (up to 16 waves), a
   // shorter chain per token; with many tokens (the launch fills the GPU) the
   // 16-lane rows, which take fewer instructions per token (measured: prefill
   // routing 31 us with rows, 35 us with waves; ep_share 20.4 -> 17.6 us)
   const int wave_tok = a.E_global > 64 && a.T <= 2048 ? 1 : 0;
+  // tokens per workgroup: a multiple of 64/gcd(64,k) (whole chunks), at least
+  // 16 for the 16-lane rows (one workgroup of 16 rows) and 8 with a wave per token
+  int64_t unit = 64 / gcd64(64, a.top_k);
+  int64_t tpb = unit;
+  while (tpb < (wave_tok ? 8 : 16)) tpb += unit;
+  const int64_t nblk = (a.T + tpb - 1) / tpb;
   const int64_t threads = wave_tok ? (tpb < 16 ? tpb : 16) * 64 : 256;
   hipLaunchKernelGGL(route_topk_chunk_kernel, dim3((unsigned)nblk), dim3((unsigned)(threads < 256 ? 256 : threads)),
                      (size_t)(tpb * a.top_k) * sizeof(int32_t), stream, a, (int)tpb, wave_tok);
+  const int64_t entries = ((S + 63) / 64) * a.E_local;
+  if (entries <= kScanScatterMaxEntries && S <= kScanScatterMaxSlots) {
+    hipLaunchKernelGGL(route_scan_scatter_kernel, dim3((unsigned)((S + 1023) / 1024)), dim3(1024),
+                       (size_t)(entries + 3 * a.E_local + 2) * sizeof(int32_t), stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_chunk_scan_kernel, dim3((unsigned)((a.E_local + 3) / 4)), dim3(256), 0, stream, a);
   const int64_t nscatter = (S + 255) / 256 < 1024 ? (S + 255) / 256 : 1024;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)nscatter), dim3(256),
