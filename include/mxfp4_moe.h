@@ -36,8 +36,12 @@
  *     aligned.  The library allocates nothing.  Inputs are read-only; outputs are
  *     fully overwritten; the workspace's contents are undefined afterwards.
  *   - Execution: work is enqueued on `stream` (0 = the null stream) and the call
- *     returns without waiting.  No global mutable state: calls on different
- *     streams with different workspaces may run concurrently.
+ *     returns without waiting.  Calls on different streams with different
+ *     workspaces may run concurrently.  The only process-wide state is a set of
+ *     per-device caches filled once under a lock (the device check, the CU
+ *     count, resident-grid sizes, kernels' LDS limits) and the static scratch of
+ *     mxfp4_moe_forward_noalloc; results never depend on it.  The library reads
+ *     no environment variables.
  *   - Shapes: int64 counts, validated with checked arithmetic.  H and I must be
  *     multiples of 128; T may be 0 (nothing is enqueued).
  *   - Preconditions not checked (for cost): router logits are not NaN (a NaN
@@ -100,6 +104,10 @@ extern "C" {
                                         operand of the same scaled MFMA.  Excludes
                                         MXFP4_MOE_A4 (both: BAD_FLAGS).  Intermediates
                                         below then hold one code byte per element. */
+#define MXFP4_MOE_ROUTE_LAUNCH 0x10u /* route in a launch of its own even where the
+                                        gate_up kernel would route the tokens itself
+                                        (few tokens): same tables and results, one
+                                        launch more; lets a caller compare the forms */
 
 typedef struct mxfp4_moe_dims {
   int64_t T;           /* tokens */
@@ -109,7 +117,7 @@ typedef struct mxfp4_moe_dims {
   int64_t E_local;     /* experts held by this GPU */
   int64_t first_local; /* global id of local expert 0 */
   uint32_t flags;      /* MXFP4_MOE_A4 or MXFP4_MOE_A8, | MXFP4_MOE_DETERMINISTIC
-                          | MXFP4_MOE_SHARED_EXPERT */
+                          | MXFP4_MOE_SHARED_EXPERT | MXFP4_MOE_ROUTE_LAUNCH */
   uint32_t reserved;   /* must be 0 */
 } mxfp4_moe_dims;
 

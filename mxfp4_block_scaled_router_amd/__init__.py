@@ -22,6 +22,7 @@ MXFP4_MOE_A4 = 0x1
 MXFP4_MOE_DETERMINISTIC = 0x2
 MXFP4_MOE_SHARED_EXPERT = 0x4
 MXFP4_MOE_A8 = 0x8
+MXFP4_MOE_ROUTE_LAUNCH = 0x10
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
@@ -47,9 +48,10 @@ class Dims(ctypes.Structure):
 
     @classmethod
     def make(cls, T, H, I, E_global, E_local=None, first_local=0, a4=False,
-             deterministic=False, shared=False, a8=False) -> "Dims":
+             deterministic=False, shared=False, a8=False, route_launch=False) -> "Dims":
         flags = ((MXFP4_MOE_A4 if a4 else 0) | (MXFP4_MOE_DETERMINISTIC if deterministic else 0)
-                 | (MXFP4_MOE_SHARED_EXPERT if shared else 0) | (MXFP4_MOE_A8 if a8 else 0))
+                 | (MXFP4_MOE_SHARED_EXPERT if shared else 0) | (MXFP4_MOE_A8 if a8 else 0)
+                 | (MXFP4_MOE_ROUTE_LAUNCH if route_launch else 0))
         return cls(T, H, I, E_global, E_global if E_local is None else E_local, first_local,
                    flags, 0)
 

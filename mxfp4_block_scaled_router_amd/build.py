@@ -28,6 +28,13 @@ COMMON_FLAGS = [
 ]
 
 
+# MXFP4_MOE_TUNING=1 at build time compiles in the environment overrides of the
+# tuning parameters (tile plan, decode variant, ...) for parameter sweeps; the
+# regular library reads no environment.
+if os.environ.get("MXFP4_MOE_TUNING") == "1":
+    COMMON_FLAGS.append("-DMXFP4_MOE_TUNING")
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 

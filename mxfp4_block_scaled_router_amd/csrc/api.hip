@@ -41,6 +41,7 @@ struct Shape {
   int64_t Er, kp;  // routed local experts, routed picks per token
   int64_t sh;      // 1 with the shared expert
   bool a4, a8, ordered;
+  bool route_launch;  // route in its own launch even where gate_up could route
   // activation format of the GEMMs: 0 bf16, 1 MXFP4 (A4), 2 MXFP8 (A8)
   int af() const { return a4 ? 1 : a8 ? 2 : 0; }
   bool mx() const { return a4 || a8; }
@@ -52,7 +53,8 @@ GemmPlan choose_plan(const Shape& s);
 int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!d) return MXFP4_MOE_ERR_NULL_POINTER;
   if (d->reserved != 0) return MXFP4_MOE_ERR_BAD_ARGUMENT;
-  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT | MXFP4_MOE_A8))
+  if (d->flags & ~(MXFP4_MOE_A4 | MXFP4_MOE_DETERMINISTIC | MXFP4_MOE_SHARED_EXPERT | MXFP4_MOE_A8 |
+                   MXFP4_MOE_ROUTE_LAUNCH))
     return MXFP4_MOE_ERR_BAD_FLAGS;
   if ((d->flags & MXFP4_MOE_A4) && (d->flags & MXFP4_MOE_A8)) return MXFP4_MOE_ERR_BAD_FLAGS;
   if (d->T < 0 || d->H < 0 || d->I < 0 || d->E_global < 0 || d->E_local < 0 || d->first_local < 0)
@@ -81,6 +83,7 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   s->a4 = (d->flags & MXFP4_MOE_A4) != 0;
   s->a8 = (d->flags & MXFP4_MOE_A8) != 0;
   s->ordered = (d->flags & MXFP4_MOE_DETERMINISTIC) != 0;
+  s->route_launch = (d->flags & MXFP4_MOE_ROUTE_LAUNCH) != 0;
   // element counts that the kernels index with int64 and int32
   int64_t tmp;
   if (!mul_ok(s->T, s->k, &s->S)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
@@ -103,13 +106,6 @@ int check_clamp(float L) {
 }
 
 // ---------------------------------------------------------------- plans
-// MXFP4_MOE_ROUTE_KERNEL=1 (benchmarks only) keeps the separate routing kernel
-// where the decode gate_up kernel would route the tokens itself
-bool separate_route_kernel() {
-  const char* env = getenv("MXFP4_MOE_ROUTE_KERNEL");
-  return env && !strcmp(env, "1");
-}
-
 // Token-tile height by the expected rows per expert, r = T*k / E_global
 // (measured on MI355X with the decode and prefill layers' dims, T from 6 to
 // 8192): 16-row tiles, which stream an expert's weights once per 16 rows, win
@@ -128,16 +124,16 @@ GemmPlan choose_plan(const Shape& s) {
   // use one wave per 512 elements of K (at most 16 waves)
   const bool ksplit_ok = s.T * s.H * 2 < (int64_t(1) << 30) && s.S * s.I * 2 < (int64_t(1) << 30) &&
                          s.H <= 8192 && s.I <= 8192 && (s.I / 16) % 4 == 0 && (s.H / 32) % 4 == 0;
-  // MXFP4_MOE_PLAN=16|64|128 (benchmarks only) forces the token-tile height
+  // MXFP4_MOE_PLAN=16|64|128|320 (tuning builds only) forces the token-tile height
   int forced = 0;
-  if (const char* env = getenv("MXFP4_MOE_PLAN")) forced = atoi(env);
+  if (const char* env = tuning_env("MXFP4_MOE_PLAN")) forced = atoi(env);
   // (the 64-row kernels have no MXFP8 activations: A8 takes the 128-row tiles)
   const bool lds64 = !s.a8 && (forced == 64 || (forced == 0 && s.S <= kRowsPerExpert64 * s.Eg));
   if (ksplit_ok && (forced == 16 || (forced == 0 && s.S <= kRowsPerExpert16 * s.Eg))) {
-    p.ms = 1; p.fg = 1; p.nw = 4; p.direct_a = 1;
+    p.ms = 1; p.fg = 1; p.nw = 4;
   } else if (lds64) {
     // 64-token tiles with register-fed weights
-    p.ms = 4; p.fg = 2; p.nw = 4; p.direct_a = 0;
+    p.ms = 4; p.fg = 2; p.nw = 4;
   } else if (s.a4 && (forced == 0 || forced == 320) && s.S <= kRowsPerExpert320 * s.Eg &&
              tile_fits(s.af(), 320, s.H) && tile_fits(s.af(), 320, s.I)) {
     // MXFP4 activations, experts expected to hold at most 256 rows:
@@ -145,14 +141,14 @@ GemmPlan choose_plan(const Shape& s) {
     // stream once; 1.07x faster than 128 x 512 tiles at the A4 prefill shape
     // on MI355X).  MXFP8 activations stay on 128-row tiles (their 320-row
     // stages leave too few slots: 1.3x slower).
-    p.ms = 20; p.fg = 0; p.nw = 4; p.direct_a = 0;
+    p.ms = 20; p.fg = 0; p.nw = 4;
     // down (K = I, every activation row re-read by each 128-row weight block
     // of a 320-row tile) keeps the 128 x 512 tiles: 1.2x faster at the A4
     // prefill shape on MI355X
     p.ms_dn = 8;
   } else {
     // 128-token x 512-weight-row tiles staged through LDS
-    p.ms = 8; p.fg = 0; p.nw = 4; p.direct_a = 0;
+    p.ms = 8; p.fg = 0; p.nw = 4;
   }
   return p;
 }
@@ -345,7 +341,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   const bool has_x = bx && bx->n > 0;
   if (has_x) r.xmap = bx->expert_map;
   // few tokens on the 16-row plan: the gate_up kernel routes them itself
-  const bool fused_route = plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) && !separate_route_kernel();
+  const bool fused_route = plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) && !s.route_launch;
   hipError_t e = fused_route ? hipSuccess : launch_route(r, stream);
   if (e != hipSuccess) return hip_fail(e);
 

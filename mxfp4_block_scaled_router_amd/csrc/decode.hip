@@ -654,7 +654,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
 //
 // Variants: (KPW, D) = k-tiles per wave, ring slots (units ahead).  Default:
 // KPW 4 (5 or 8 when K needs it to fit 8 waves), D 1.
-// MXFP4_MOE_DECODE_VARIANT (tests and benchmarks only) picks another,
+// MXFP4_MOE_DECODE_VARIANT (tuning builds only) picks another,
 // "k<KPW>d<D>" with KPW 2 or 4 and D 1 or 2.  MXFP4_MOE_DECODE_WGS_PER_CU
 // caps the resident workgroups per CU.
 namespace {
@@ -666,7 +666,7 @@ Variant pick(int64_t K, bool defaults_only = false) {
   const int64_t KT = K / kTileK;
   Variant v{KT <= 32 ? 4 : KT <= 40 ? 5 : KT <= 48 ? 6 : KT <= 56 ? 7 : 8, 1};
   if (defaults_only) return v;
-  if (const char* env = getenv("MXFP4_MOE_DECODE_VARIANT")) {
+  if (const char* env = tuning_env("MXFP4_MOE_DECODE_VARIANT")) {
     int kpw = 0, d = 0;
     if (sscanf(env, "k%dd%d", &kpw, &d) == 2 && (kpw == 2 || kpw == 4) && (d == 1 || d == 2) &&
         (KT + kpw - 1) / kpw <= 8)
@@ -707,7 +707,7 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid, int c
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds)) != hipSuccess) return e;
   if (cap_per_cu > 0 && cap_per_cu < per_cu) per_cu = cap_per_cu;
-  if (const char* env = getenv("MXFP4_MOE_DECODE_WGS_PER_CU")) {
+  if (const char* env = tuning_env("MXFP4_MOE_DECODE_WGS_PER_CU")) {
     const int cap = atoi(env);
     if (cap > 0 && cap < per_cu) per_cu = cap;
   }
@@ -721,9 +721,9 @@ hipError_t resident_grid(const void* fn, int block, size_t lds, int* grid, int c
 // Slot weights c of the shares (measured on MI355X: with 3 workgroups per CU
 // the third streams ~1.35x slower than the first; c = 0.25 for gate_up and 0.1
 // for down took the kernels' last workgroups in by ~1 us).
-// MXFP4_MOE_SLOT_C_GU / MXFP4_MOE_SLOT_C_DN (benchmarks only) override them.
+// MXFP4_MOE_SLOT_C_GU / MXFP4_MOE_SLOT_C_DN (tuning builds only) override them.
 float slot_c(const char* name, float dflt) {
-  const char* v = getenv(name);
+  const char* v = tuning_env(name);
   return v ? (float)atof(v) : dflt;
 }
 std::mutex g_cus_mu;

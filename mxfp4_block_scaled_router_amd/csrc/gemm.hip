@@ -69,12 +69,11 @@ __device__ __forceinline__ f32x4_t mfma_fp4(u32x4_t a, uint32_t sa, u32x4_t b, u
 // ------------------------------------------------------------------------
 // W4A16 main loop: acc[ms][g] += A(tile rows) x W(row group g)^T over all K.
 //   NG weight row groups per wave, MS 16-row token subtiles per workgroup,
-//   CH k-tiles (of 128) per pipeline stage.
-//   DIRECT: MS == 1 and each lane loads its own A operand from global memory;
-//   else the workgroup stages A rows in LDS per stage.
-// row_ptr(row) gives the bf16 row of token-tile row `row` (< rows).
+//   CH k-tiles (of 128) per pipeline stage.  The workgroup stages its A rows
+//   in LDS per stage; row_off_lds[row] is the element offset of token-tile row
+//   `row` from abase (-1: a zero row).
 // ------------------------------------------------------------------------
-template <int MS, int NG, int NW, int CH, bool DIRECT>
+template <int MS, int NG, int NW, int CH>
 struct W4A16Loop {
   static constexpr int MT = 16 * MS;
   static constexpr int KC = CH * kTileK;          // K per stage
@@ -83,10 +82,9 @@ struct W4A16Loop {
   static constexpr int UNITS = MT * KC / 8;       // 16-byte units per stage
   static constexpr int UPT = (UNITS + NT - 1) / NT;
 
-  static constexpr size_t lds_bytes() { return DIRECT ? 0 : (size_t)MT * LDS_STRIDE * 2; }
+  static constexpr size_t lds_bytes() { return (size_t)MT * LDS_STRIDE * 2; }
 
-  __device__ static void run(const uint16_t* const* rowp_lane,      // DIRECT: this lane's row (or null)
-                             const int64_t* row_off_lds,            // LDS: row base offsets (elements), -1 = zero row
+  __device__ static void run(const int64_t* row_off_lds,            // LDS: row base offsets (elements), -1 = zero row
                              const uint16_t* abase, int64_t K,
                              const uint8_t* const* wc,              // [NG] codes base of row group
                              const uint8_t* const* wsb,             // [NG] scales base of row group
@@ -98,8 +96,7 @@ struct W4A16Loop {
 
     u32x4_t wcur[CH][NG], wnext[CH][NG];
     uint32_t scur[NG], snext[NG];
-    u32x4_t acur[DIRECT ? CH : 1][4], anext[DIRECT ? CH : 1][4];
-    u32x4_t stage_regs[DIRECT ? 1 : UPT];
+    u32x4_t stage_regs[UPT];
 
     auto load_w = [&](int st, u32x4_t (&wr)[CH][NG], uint32_t (&sr)[NG]) {
       const int kt0 = st * CH;
@@ -111,50 +108,31 @@ struct W4A16Loop {
           if (kt0 + c < KT) wr[c][gi] = ld16(wc[gi] + (int64_t)(kt0 + c) * 1024 + lane * 16);
       }
     };
-    auto load_a_direct = [&](int st, u32x4_t (&ar)[DIRECT ? CH : 1][4]) {
-      if constexpr (DIRECT) {
-        const int kt0 = st * CH;
-        const uint16_t* rp = *rowp_lane;
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (rp && kt0 + c < KT) v = ld16(rp + (int64_t)(kt0 + c) * kTileK + 32 * g + 8 * m);
-            ar[c][m] = v;
-          }
-      }
-    };
     auto load_stage_regs = [&](int st) {
-      if constexpr (!DIRECT) {
-        const int64_t k0 = (int64_t)st * KC;
+      const int64_t k0 = (int64_t)st * KC;
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-          int u = threadIdx.x + i * NT;
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (u < UNITS) {
-            int row = u / (KC / 8), col = (u % (KC / 8)) * 8;
-            int64_t off = row_off_lds[row];
-            if (off >= 0 && k0 + col < K) v = ld16(abase + off + k0 + col);
-          }
-          stage_regs[i] = v;
+      for (int i = 0; i < UPT; ++i) {
+        int u = threadIdx.x + i * NT;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (u < UNITS) {
+          int row = u / (KC / 8), col = (u % (KC / 8)) * 8;
+          int64_t off = row_off_lds[row];
+          if (off >= 0 && k0 + col < K) v = ld16(abase + off + k0 + col);
         }
+        stage_regs[i] = v;
       }
     };
     auto store_stage_lds = [&]() {
-      if constexpr (!DIRECT) {
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-          int u = threadIdx.x + i * NT;
-          if (u < UNITS) {
-            int row = u / (KC / 8), col = (u % (KC / 8)) * 8;
-            *reinterpret_cast<u32x4_t*>(lds + row * LDS_STRIDE + col) = stage_regs[i];
-          }
+      for (int i = 0; i < UPT; ++i) {
+        int u = threadIdx.x + i * NT;
+        if (u < UNITS) {
+          int row = u / (KC / 8), col = (u % (KC / 8)) * 8;
+          *reinterpret_cast<u32x4_t*>(lds + row * LDS_STRIDE + col) = stage_regs[i];
         }
       }
     };
-    auto compute = [&](int st, const u32x4_t (&wr)[CH][NG], const uint32_t (&sr)[NG],
-                       const u32x4_t (&ar)[DIRECT ? CH : 1][4]) {
+    auto compute = [&](int st, const u32x4_t (&wr)[CH][NG], const uint32_t (&sr)[NG]) {
       const int kt0 = st * CH;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
@@ -168,12 +146,8 @@ struct W4A16Loop {
           bf16x8_t av[MS];
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms) {
-            if constexpr (DIRECT) {
-              av[ms] = __builtin_bit_cast(bf16x8_t, ar[c][m]);
-            } else {
-              const uint16_t* p = lds + (ms * 16 + (lane & 15)) * LDS_STRIDE + c * kTileK + 32 * g + 8 * m;
-              av[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
-            }
+            const uint16_t* p = lds + (ms * 16 + (lane & 15)) * LDS_STRIDE + c * kTileK + 32 * g + 8 * m;
+            av[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
           }
 #pragma unroll
           for (int gi = 0; gi < NG; ++gi) {
@@ -186,21 +160,17 @@ struct W4A16Loop {
     };
 
     load_w(0, wcur, scur);
-    if constexpr (DIRECT) load_a_direct(0, acur);
-    else load_stage_regs(0);
+    load_stage_regs(0);
     for (int st = 0; st < nstage; ++st) {
-      if constexpr (!DIRECT) {
-        __syncthreads();
-        store_stage_lds();
-        __syncthreads();
-      }
+      __syncthreads();
+      store_stage_lds();
+      __syncthreads();
       const bool more = st + 1 < nstage;
       if (more) {
         load_w(st + 1, wnext, snext);
-        if constexpr (DIRECT) load_a_direct(st + 1, anext);
-        else load_stage_regs(st + 1);
+        load_stage_regs(st + 1);
       }
-      compute(st, wcur, scur, acur);
+      compute(st, wcur, scur);
       if (more) {
 #pragma unroll
         for (int c = 0; c < CH; ++c)
@@ -208,12 +178,6 @@ struct W4A16Loop {
           for (int gi = 0; gi < NG; ++gi) wcur[c][gi] = wnext[c][gi];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) scur[gi] = snext[gi];
-        if constexpr (DIRECT) {
-#pragma unroll
-          for (int c = 0; c < CH; ++c)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acur[c][m] = anext[c][m];
-        }
       }
     }
   }
@@ -262,7 +226,7 @@ __device__ __forceinline__ void a4_loop(const uint8_t* const (&arow)[MS], const 
 // gate_up + clamped SwiGLU
 // grid: x = token tiles (upper bound), y = feature blocks of NW*FG*16 features
 // ========================================================================
-template <int MS, int FG, int NW, int CH, bool DIRECT, bool A4>
+template <int MS, int FG, int NW, int CH, bool A4>
 __global__ __launch_bounds__(NW * 64) void gate_up_kernel(GemmArgs a) {
   extern __shared__ uint16_t lds_dyn[];
   zero_duty(a);
@@ -310,17 +274,12 @@ __global__ __launch_bounds__(NW * 64) void gate_up_kernel(GemmArgs a) {
       }
     }
     a4_loop<MS, NG>(arow, asrow, H, wc, wsb, acc);
-  } else if constexpr (DIRECT) {
-    int r = lane & 15;
-    const uint16_t* rp = nullptr;
-    if (r < tile.rows) rp = a.a_bf16 + (int64_t)(a.sorted[tile.p0 + r] / a.top_k) * H;
-    W4A16Loop<MS, NG, NW, CH, true>::run(&rp, nullptr, nullptr, H, wc, wsb, nullptr, acc);
   } else {
     __shared__ int64_t row_off[MT];
     for (int r = threadIdx.x; r < MT; r += NW * 64)
       row_off[r] = r < tile.rows ? (int64_t)(a.sorted[tile.p0 + r] / a.top_k) * H : -1;
     __syncthreads();
-    W4A16Loop<MS, NG, NW, CH, false>::run(nullptr, row_off, a.a_bf16, H, wc, wsb, lds_dyn, acc);
+    W4A16Loop<MS, NG, NW, CH>::run(row_off, a.a_bf16, H, wc, wsb, lds_dyn, acc);
   }
 
   // epilogue: act[p][n] = bf16(swiglu(g, u))
@@ -344,7 +303,7 @@ __global__ __launch_bounds__(NW * 64) void gate_up_kernel(GemmArgs a) {
 // down + combine
 // grid: x = token tiles (upper bound), y = feature blocks of NW*FG*16 of H
 // ========================================================================
-template <int MS, int FG, int NW, int CH, bool DIRECT, bool A4, bool ORDERED>
+template <int MS, int FG, int NW, int CH, bool A4, bool ORDERED>
 __global__ __launch_bounds__(NW * 64) void down_kernel(GemmArgs a) {
   extern __shared__ uint16_t lds_dyn[];
   constexpr int MT = 16 * MS;
@@ -386,16 +345,12 @@ __global__ __launch_bounds__(NW * 64) void down_kernel(GemmArgs a) {
       }
     }
     a4_loop<MS, NG>(arow, asrow, I, wc, wsb, acc);
-  } else if constexpr (DIRECT) {
-    int r = lane & 15;
-    const uint16_t* rp = r < tile.rows ? a.a_bf16 + (tile.p0 + r) * I : nullptr;
-    W4A16Loop<MS, NG, NW, CH, true>::run(&rp, nullptr, nullptr, I, wc, wsb, nullptr, acc);
   } else {
     __shared__ int64_t row_off[MT];
     for (int r = threadIdx.x; r < MT; r += NW * 64)
       row_off[r] = r < tile.rows ? (tile.p0 + r) * I : -1;
     __syncthreads();
-    W4A16Loop<MS, NG, NW, CH, false>::run(nullptr, row_off, a.a_bf16, I, wc, wsb, lds_dyn, acc);
+    W4A16Loop<MS, NG, NW, CH>::run(row_off, a.a_bf16, I, wc, wsb, lds_dyn, acc);
   }
 
   // epilogue
@@ -531,53 +486,46 @@ __global__ __launch_bounds__(256) void copy_bytes_kernel(const uint8_t* src, uin
 // ========================================================================
 namespace {
 
-template <int MS, int FG, int NW, int CH, bool DIRECT, bool A4>
+template <int MS, int FG, int NW, int CH, bool A4>
 hipError_t gate_up_variant(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  using L = W4A16Loop<MS, 2 * FG, NW, CH, DIRECT>;
+  using L = W4A16Loop<MS, 2 * FG, NW, CH>;
   size_t lds = A4 ? 0 : L::lds_bytes();
   dim3 grid((unsigned)max_tiles, (unsigned)(a.N / 2 / 16 / (NW * FG)));
-  hipLaunchKernelGGL((gate_up_kernel<MS, FG, NW, CH, DIRECT, A4>), grid, dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL((gate_up_kernel<MS, FG, NW, CH, A4>), grid, dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MS, int FG, int NW, int CH, bool DIRECT, bool A4>
+template <int MS, int FG, int NW, int CH, bool A4>
 hipError_t down_variant(const GemmArgs& a, int64_t max_tiles, bool ordered, hipStream_t s) {
-  using L = W4A16Loop<MS, FG, NW, CH, DIRECT>;
+  using L = W4A16Loop<MS, FG, NW, CH>;
   size_t lds = A4 ? 0 : L::lds_bytes();
   dim3 grid((unsigned)max_tiles, (unsigned)(a.N / 16 / (NW * FG)));
   if (ordered)
-    hipLaunchKernelGGL((down_kernel<MS, FG, NW, CH, DIRECT, A4, true>), grid, dim3(NW * 64), lds, s, a);
+    hipLaunchKernelGGL((down_kernel<MS, FG, NW, CH, A4, true>), grid, dim3(NW * 64), lds, s, a);
   else
-    hipLaunchKernelGGL((down_kernel<MS, FG, NW, CH, DIRECT, A4, false>), grid, dim3(NW * 64), lds, s, a);
+    hipLaunchKernelGGL((down_kernel<MS, FG, NW, CH, A4, false>), grid, dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Plans supported: (ms, fg, nw, direct) in
-//   (1, 1, 4, 1)  decode: 16-token tiles, A operands from global memory
-//   (4, 2, 4, 0)  64-token tiles, A staged in LDS
+// The one plan of these kernels: (ms, fg, nw) = (4, 2, 4), 64-token tiles with
+// the activation rows staged in LDS (16-row plans run the K-split kernels).
 hipError_t launch_gate_up(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4,
                           hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  if (p.ms == 1 && p.fg == 1 && p.nw == 4 && p.direct_a)
-    return a4 ? gate_up_variant<1, 1, 4, 2, true, true>(a, max_tiles, s)
-              : gate_up_variant<1, 1, 4, 2, true, false>(a, max_tiles, s);
-  if (p.ms == 4 && p.fg == 2 && p.nw == 4 && !p.direct_a)
-    return a4 ? gate_up_variant<4, 2, 4, 2, false, true>(a, max_tiles, s)
-              : gate_up_variant<4, 2, 4, 2, false, false>(a, max_tiles, s);
+  if (p.ms == 4 && p.fg == 2 && p.nw == 4)
+    return a4 ? gate_up_variant<4, 2, 4, 2, true>(a, max_tiles, s)
+              : gate_up_variant<4, 2, 4, 2, false>(a, max_tiles, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, bool a4, bool ordered,
                        hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  if (p.ms == 1 && p.fg == 1 && p.nw == 4 && p.direct_a)
-    return a4 ? down_variant<1, 1, 4, 2, true, true>(a, max_tiles, ordered, s)
-              : down_variant<1, 1, 4, 2, true, false>(a, max_tiles, ordered, s);
-  if (p.ms == 4 && p.fg == 2 && p.nw == 4 && !p.direct_a)
-    return a4 ? down_variant<4, 2, 4, 2, false, true>(a, max_tiles, ordered, s)
-              : down_variant<4, 2, 4, 2, false, false>(a, max_tiles, ordered, s);
+  if (p.ms == 4 && p.fg == 2 && p.nw == 4)
+    return a4 ? down_variant<4, 2, 4, 2, true>(a, max_tiles, ordered, s)
+              : down_variant<4, 2, 4, 2, false>(a, max_tiles, ordered, s);
   return hipErrorInvalidValue;
 }
 

@@ -4,8 +4,21 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace mxmoe {
+
+// Tuning overrides (MXFP4_MOE_PLAN, MXFP4_MOE_DECODE_VARIANT, ...) exist only in
+// a library built with -DMXFP4_MOE_TUNING, for parameter sweeps; the regular
+// build reads no environment and always uses the measured defaults.
+inline const char* tuning_env(const char* name) {
+#ifdef MXFP4_MOE_TUNING
+  return getenv(name);
+#else
+  (void)name;
+  return nullptr;
+#endif
+}
 
 constexpr size_t kRouteFusedMaxLds = 48 * 1024;
 // the decode gate_up kernel routes tokens itself only for E_global <= 16 x this
@@ -152,7 +165,6 @@ struct GemmPlan {
   int ms;        // 16-row token subtiles per workgroup (token tile = 16 * ms)
   int fg;        // 16-feature groups per wave
   int nw;        // waves per workgroup
-  int direct_a;  // 1: activation operands loaded straight from global memory
   int ms_dn = 0; // down's token tile in 16-row subtiles when it differs from gate_up's (0: ms)
   int down_ms() const { return ms_dn ? ms_dn : ms; }
 };

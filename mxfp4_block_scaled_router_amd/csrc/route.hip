@@ -190,7 +190,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const size_t lds = small_lds_bytes(S, a.E_local);
   // one workgroup wins up to ~48 tokens of 64 experts, top-8 (measured)
   int64_t small_work = 2048;
-  if (const char* env = getenv("MXFP4_MOE_ROUTE_SMALL_WORK")) small_work = atoll(env);  // benchmarks only
+  if (const char* env = tuning_env("MXFP4_MOE_ROUTE_SMALL_WORK")) small_work = atoll(env);  // tuning builds only
   if (lds <= kRouteFusedMaxLds && work <= small_work) {
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), lds, stream, a);
     return hipGetLastError();

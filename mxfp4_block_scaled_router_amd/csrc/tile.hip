@@ -777,17 +777,21 @@ int64_t tile_grid(int64_t max_tiles, int64_t N, int nt) {
   return 8 * ((items + 7) / 8);
 }
 
-// Launch with `lds` bytes of dynamic LDS; the first launch of each kernel
-// raises its dynamic-LDS limit to that size.
+// Launch with `lds` bytes of dynamic LDS; the first launch of each kernel on a
+// device raises its dynamic-LDS limit there to kTileLdsMax.
 template <typename Kernel>
 hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a, hipStream_t s) {
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)kTileLdsMax);
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t attr[kMaxDevices];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    attr[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTileLdsMax);
   });
-  if (attr != hipSuccess) return attr;
+  if (attr[dev] != hipSuccess) return attr[dev];
   if (lds > kTileLdsMax) return hipErrorInvalidValue;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, s, a);

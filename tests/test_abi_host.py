@@ -75,7 +75,7 @@ def ws_status(d, k=2):
     ({}, -1, BAD_TOP_K), ({}, 9, BAD_TOP_K), ({"E_global": 64, "E_local": 64}, 33, BAD_TOP_K),
     ({"T": 1 << 40}, 8, SHAPE_OVERFLOW), ({"T": 1 << 60, "H": 1 << 10}, 2, SHAPE_OVERFLOW),
     ({"first_local": (1 << 63) - 4}, 2, SHAPE_OVERFLOW),
-    ({"flags": 0x10}, 2, BAD_FLAGS),
+    ({"flags": 0x20}, 2, BAD_FLAGS),
     ({"flags": 0x1 | 0x8}, 2, BAD_FLAGS),     # A4 and A8 exclude each other
 ])
 def test_dims_refusals(lib, kw, k, expect):
