@@ -117,6 +117,10 @@ constexpr int64_t kRowsPerExpert64 = 48;
 // tiles hold every expert of a routing whole (the rows an expert gets spread
 // by about the square root of the mean; above 320 an expert takes two tiles).
 constexpr int64_t kRowsPerExpert320 = 256;
+// K-split plans take 32-row tiles from this many tokens on, where the
+// activations of two row blocks fit the registers (measured: verify_b32 on
+// the decode layer 143 -> 104 us; verify_b16 90 either way)
+constexpr int64_t kKsplit32MinT = 64;
 
 GemmPlan choose_plan(const Shape& s) {
   GemmPlan p;
@@ -129,8 +133,14 @@ GemmPlan choose_plan(const Shape& s) {
   if (const char* env = tuning_env("MXFP4_MOE_PLAN")) forced = atoi(env);
   // (the 64-row kernels have no MXFP8 activations: A8 takes the 128-row tiles)
   const bool lds64 = !s.a8 && (forced == 64 || (forced == 0 && s.S <= kRowsPerExpert64 * s.Eg));
-  if (ksplit_ok && (forced == 16 || (forced == 0 && s.S <= kRowsPerExpert16 * s.Eg))) {
-    p.ms = 1; p.fg = 1; p.nw = 4;
+  if (ksplit_ok && (forced == 16 || forced == 32 || (forced == 0 && s.S <= kRowsPerExpert16 * s.Eg))) {
+    // K-split kernels; with many tokens an expert may fill several 16-row
+    // tiles, each of which would stream the expert's weights: 32-row tiles
+    // (two row blocks per weight slice) halve that
+    p.ksplit = 1;
+    const bool fit = ksplit_two_blocks_fit(s.H, s.af()) && ksplit_two_blocks_fit(s.I, s.af());
+    p.ms = forced == 32 || (forced == 0 && s.T >= kKsplit32MinT && fit) ? 2 : 1;
+    p.fg = 1; p.nw = 4;
   } else if (lds64) {
     // 64-token tiles with register-fed weights
     p.ms = 4; p.fg = 2; p.nw = 4;
@@ -194,8 +204,8 @@ Layout layout_of(const Shape& s) {
                                    ? max_tiles(s, 16 * p.ms) : max_tiles(s, 16 * p.down_ms()));
     L.tiles1 = take(nt * 16);
     L.tiles2 = take(nt * 16);
-    L.tile_tok = p.ms == 1 ? take(nt * 16 * 4) : 0;
-    L.dn_desc = p.ms == 1 ? take((size_t)kMaxDownDesc * 32) : 0;
+    L.tile_tok = p.ksplit ? take(nt * 16 * p.ms * 4) : 0;
+    L.dn_desc = p.ksplit ? take((size_t)kMaxDownDesc * 32) : 0;
   }
   L.pos_tok = take(S * 4);
   L.pos_w = take(S * 4);
@@ -341,7 +351,8 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   const bool has_x = bx && bx->n > 0;
   if (has_x) r.xmap = bx->expert_map;
   // few tokens on the 16-row plan: the gate_up kernel routes them itself
-  const bool fused_route = plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) && !s.route_launch;
+  const bool fused_route = plan.ksplit && plan.ms == 1 && max_tiles(s, mt) > 0 && route_fusable(r) &&
+                           !s.route_launch;
   hipError_t e = fused_route ? hipSuccess : launch_route(r, stream);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -372,6 +383,12 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.top_k = (int32_t)s.k;
   g.E_local = (int32_t)s.El;
   g.clamp_limit = clamp_limit;
+  g.tile_ms = plan.ksplit ? plan.ms : 0;
+  // 16-row tiles with many tokens: hot experts span several tiles, whose
+  // units find the expert's weight slices in L2 when they are loaded cached
+  // (measured, ep_share: gate_up 61.4 -> 52.3 us; decode, one tile per
+  // expert, keeps the non-temporal loads: 58.5 vs 65.3 us cached)
+  g.wcache = plan.ksplit && plan.ms == 1 && s.T >= kKsplit32MinT ? 1 : 0;
   // gate_up
   g.a_bf16 = reinterpret_cast<const uint16_t*>(x);
   g.a_rows = s.T;
@@ -403,7 +420,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
       g.dn_c = c;
     }
   }
-  e = plan.ms == 1   ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.af(), stream)
+  e = plan.ksplit    ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.af(), stream)
       : plan.ms >= 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), mt, stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -448,7 +465,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.zero_n = 0;
   g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
-  e = plan.ms == 1   ? launch_down_ksplit(g, max_tiles(s, mt), s.af(), s.ordered, stream)
+  e = plan.ksplit    ? launch_down_ksplit(g, max_tiles(s, mt), s.af(), s.ordered, stream)
       : plan.ms >= 8 ? launch_down_tile(g, max_tiles(s, mt_dn), s.af(), mt_dn, s.ordered, stream)
                      : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);

@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -98,11 +99,13 @@ struct ASlice<KPW, kActFp8> {
 
 // Weight slices are buffer loads against a descriptor that spans the unit's NG
 // adjacent row groups; a unit past the workgroup's share gets an empty
-// descriptor, whose loads return zeros without touching memory.  Loads carry
-// the non-temporal hint (the stream is read once per step).  k-tiles past KT
-// are clamped to KT-1 and contribute zero in compute_refill.
-constexpr int kNonTemporal = 2;
-template <int NG, int KPW>
+// descriptor, whose loads return zeros without touching memory.  NT: the
+// loads carry the non-temporal hint (each slice is read once per step);
+// without it an expert spread over several tiles can find the slices in L2.
+// k-tiles past KT are clamped to KT-1 and contribute zero in compute_refill.
+template <bool NT>
+constexpr int kWeightCpol = NT ? 2 : 0;
+template <bool NT, int NG, int KPW>
 __device__ __forceinline__ void load_wcodes(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, uint32_t group_bytes,
                                             int c, int kt0, int KT) {
   const int kt = kt0 + c < KT ? kt0 + c : KT - 1;
@@ -110,9 +113,9 @@ __device__ __forceinline__ void load_wcodes(WSlice<NG, KPW>& t, __amdgpu_buffer_
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi)
     t.w[c][gi] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, gi * group_bytes + off, 0, kNonTemporal));
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, gi * group_bytes + off, 0, kWeightCpol<NT>));
 }
-template <int NG, int KPW>
+template <bool NT, int NG, int KPW>
 __device__ __forceinline__ void load_wscales(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rs, uint32_t group_sbytes,
                                              int kt0, int KT) {
   const int q0 = kt0 >> 2;
@@ -124,16 +127,16 @@ __device__ __forceinline__ void load_wscales(WSlice<NG, KPW>& t, __amdgpu_buffer
 #pragma unroll
     for (int j = 0; j < kScaleWords<KPW>; ++j) {
       const int q = q0 + j < qmax ? q0 + j : qmax;
-      t.sd[gi][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q * 256u, 0, kNonTemporal);
+      t.sd[gi][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + (uint32_t)q * 256u, 0, kWeightCpol<NT>);
     }
   }
 }
-template <int NG, int KPW>
+template <bool NT, int NG, int KPW>
 __device__ __forceinline__ void load_wslice(WSlice<NG, KPW>& t, __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
                                             uint32_t group_bytes, uint32_t group_sbytes, int kt0, int KT) {
 #pragma unroll
-  for (int c = 0; c < KPW; ++c) load_wcodes(t, rc, group_bytes, c, kt0, KT);
-  load_wscales(t, rs, group_sbytes, kt0, KT);
+  for (int c = 0; c < KPW; ++c) load_wcodes<NT>(t, rc, group_bytes, c, kt0, KT);
+  load_wscales<NT>(t, rs, group_sbytes, kt0, KT);
 }
 
 // Activation operands are buffer loads: a lane whose tile row is past the
@@ -197,10 +200,11 @@ __device__ __forceinline__ void load_aslice(ASlice<KPW, kActFp8>& t, __amdgpu_bu
 // are decoded into per-k-tile operands first).  The weight stream thus keeps
 // a steady amount in flight without a second register copy of the slice.
 // Slots past K contribute zero through both operands; FULL (every wave's
-// k-tiles inside K) drops the zeroing selects.
-template <bool FULL, int NG, int KPW, typename Refill>
-__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, kActBf16>& at, int kt0, int KT,
-                                               f32x4_t (&acc)[NG], Refill&& refill) {
+// k-tiles inside K) drops the zeroing selects.  MS 16-row blocks of the tile
+// share each unpacked weight operand: acc[ms * NG + g].
+template <bool FULL, int MS, int NG, int KPW, typename Refill>
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, kActBf16> (&at)[MS], int kt0,
+                                               int KT, f32x4_t (&acc)[MS * NG], Refill&& refill) {
   float sc[KPW][NG];
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
@@ -219,8 +223,11 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
       for (int m = 0; m < 4; ++m) {
         u32x4_t b = __builtin_bit_cast(u32x4_t, unpack8_e2m1(wt.w[c][gi][m], sc[c][gi]));
         if constexpr (!FULL) b = kin ? b : (u32x4_t){0u, 0u, 0u, 0u};
-        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, at.av[c][m]),
-                                                          __builtin_bit_cast(bf16x8_t, b), acc[gi], 0, 0, 0);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+          acc[ms * NG + gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, at[ms].av[c][m]), __builtin_bit_cast(bf16x8_t, b), acc[ms * NG + gi], 0,
+              0, 0);
       }
     }
     refill(c);
@@ -229,9 +236,9 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
 }
 // MX activations (AF = A4 or A8): the scaled MFMA takes the raw blocks and
 // both scale bytes; A's format code is FP4 (4) or FP8 E4M3 (0), W's FP4.
-template <bool FULL, int NG, int KPW, int AF, typename Refill>
-__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, AF>& at, int kt0, int KT,
-                                               f32x4_t (&acc)[NG], Refill&& refill) {
+template <bool FULL, int MS, int NG, int KPW, int AF, typename Refill>
+__device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice<KPW, AF> (&at)[MS], int kt0, int KT,
+                                               f32x4_t (&acc)[MS * NG], Refill&& refill) {
   uint32_t sbyte[KPW][NG];
 #pragma unroll
   for (int c = 0; c < KPW; ++c) {
@@ -249,17 +256,21 @@ __device__ __forceinline__ void compute_refill(WSlice<NG, KPW>& wt, const ASlice
     const bool kin = FULL || kt0 + c < KT;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      i32x8_t A;
-      if constexpr (AF == kActFp8)
-        A = (i32x8_t){(int)at.av[c][0][0], (int)at.av[c][0][1], (int)at.av[c][0][2], (int)at.av[c][0][3],
-                      (int)at.av[c][1][0], (int)at.av[c][1][1], (int)at.av[c][1][2], (int)at.av[c][1][3]};
-      else
-        A = (i32x8_t){(int)at.av[c][0], (int)at.av[c][1], (int)at.av[c][2], (int)at.av[c][3], 0, 0, 0, 0};
       u32x4_t wb = wt.w[c][gi];
       if constexpr (!FULL) wb = kin ? wb : (u32x4_t){0u, 0u, 0u, 0u};
       const i32x8_t B = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], 0, 0, 0, 0};
-      acc[gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[gi], AF == kActFp8 ? 0 : 4, 4, 0,
-                                                                 (int)at.as[c], 0, (int)sbyte[c][gi]);
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const ASlice<KPW, AF>& t = at[ms];
+        i32x8_t A;
+        if constexpr (AF == kActFp8)
+          A = (i32x8_t){(int)t.av[c][0][0], (int)t.av[c][0][1], (int)t.av[c][0][2], (int)t.av[c][0][3],
+                        (int)t.av[c][1][0], (int)t.av[c][1][1], (int)t.av[c][1][2], (int)t.av[c][1][3]};
+        else
+          A = (i32x8_t){(int)t.av[c][0], (int)t.av[c][1], (int)t.av[c][2], (int)t.av[c][3], 0, 0, 0, 0};
+        acc[ms * NG + gi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            A, B, acc[ms * NG + gi], AF == kActFp8 ? 0 : 4, 4, 0, (int)t.as[c], 0, (int)sbyte[c][gi]);
+      }
     }
     refill(c);
     __builtin_amdgcn_sched_barrier(0);
@@ -366,10 +377,13 @@ __device__ __forceinline__ UnitMap unit_share(int64_t ntiles, int FB, unsigned b
 // route_block past 32 tokens or 64 local experts; tables in LDS after the
 // partial buffers; workgroup 0 also writes the global tables that the down and
 // combine kernels read, and with dn_desc the down shares), so no routing kernel
-// runs before this one.
-template <int KPW, int D, int AF, bool FULL, bool ROUTE>
+// runs before this one.  MS: 16-row blocks per tile (tiles of 16 MS rows),
+// all multiplied by each weight slice.
+template <int KPW, int D, int AF, bool FULL, bool ROUTE, int MS, bool NT>
 __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteArgs ra) {
-  extern __shared__ float red[];  // [2][waves][2][64][4], then (ROUTE) the routing tables
+  static_assert(MS == 1 || !ROUTE, "the fused routing builds 16-row tiles");
+  constexpr int NA = 2 * MS;      // accumulators: gate and up of each row block
+  extern __shared__ float red[];  // [2][waves][NA][64][4], then (ROUTE) the routing tables
   // The routing runs at a raised wave priority: the workgroups dispatched
   // last onto a CU route while the first ones already stream, and at equal
   // priority the older waves' instructions go first and hold them back.
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
   if constexpr (ROUTE) {
     const int64_t S = ra.T * (int64_t)ra.top_k;
     const int64_t bound = (ra.E_local < S ? ra.E_local : S) + S / 16;
-    rl = route_lds(reinterpret_cast<int32_t*>(red + 2 * NW * 2 * 64 * 4), S, ra.E_local, bound);
+    rl = route_lds(reinterpret_cast<int32_t*>(red + 2 * NW * NA * 64 * 4), S, ra.E_local, bound);
     tmask = reinterpret_cast<uint32_t*>(rl.cnt);  // [E_local] (the chunk counts' space)
     if (masks_route_ok(ra))
       route_block_masks<kFusedRouteMaxVpl>(ra, rl, tmask, blockIdx.x == 0);
@@ -453,37 +467,42 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     auto load_unit = [&](int i, WSlice<2, KPW>& w) {
       const int fb = um.fb(fb0 + i);
       const bool ok = i < nu;
-      load_wslice(w, make_rsrc(ecodes + codes_tile_offset(2 * fb, 0, H), ok ? 2 * gbytes : 0u),
+      load_wslice<NT>(w, make_rsrc(ecodes + codes_tile_offset(2 * fb, 0, H), ok ? 2 * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(2 * fb, 0, H), ok ? 2 * gsbytes : 0u), gbytes, gsbytes,
                   kt0, KT);
     };
     WSlice<2, KPW> wt[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
-    // this lane's tile row and its token (garbage past the tile's rows: unused)
-    const bool valid = r < rows;
-    int32_t tok_raw;
-    if constexpr (ROUTE) {
-      if (masks_route_ok(ra)) {
-        // row r of the tile: token bit (p0 - offs[e]) + r of the expert's mask
-        const int e = ti.x;
-        tok_raw = valid ? nth_set_bit32(tmask[e], (int)(p0 - rl.offs[e]) + r) : 0;
+    // this lane's row of each row block and its token (garbage past the
+    // tile's rows: unused)
+    ASlice<KPW, AF> at[MS];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int row = 16 * ms + r;
+      const bool valid = row < rows;
+      int32_t tok_raw;
+      if constexpr (ROUTE) {
+        if (masks_route_ok(ra)) {
+          // row r of the tile: token bit (p0 - offs[e]) + r of the expert's mask
+          const int e = ti.x;
+          tok_raw = valid ? nth_set_bit32(tmask[e], (int)(p0 - rl.offs[e]) + r) : 0;
+        } else {
+          tok_raw = rl.ptok[p0 + (valid ? r : 0)];
+        }
+      } else
+        tok_raw = a.tile_tok[(int64_t)t * (16 * MS) + row];
+      const int64_t tok = valid ? tok_raw : 0;
+      if constexpr (AF != kActBf16) {
+        const int64_t rb = AF == kActFp8 ? H : H / 2;  // code bytes per row
+        const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (H / 32));
+        load_aslice(at[ms], make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * rb) : nb, nb,
+                    make_rsrc(a.a_scales, ns), valid ? (uint32_t)(tok * (H / 32)) : ns, ns, kt0, KT);
       } else {
-        tok_raw = rl.ptok[p0 + (valid ? r : 0)];
+        const uint32_t nb = (uint32_t)(a.a_rows * H * 2);
+        __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
+        load_aslice(at[ms], rs, valid ? (uint32_t)(tok * H * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
       }
-    } else
-      tok_raw = a.tile_tok[(int64_t)t * 16 + r];
-    const int64_t tok = valid ? tok_raw : 0;
-    ASlice<KPW, AF> at;
-    if constexpr (AF != kActBf16) {
-      const int64_t rb = AF == kActFp8 ? H : H / 2;  // code bytes per row
-      const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (H / 32));
-      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(tok * rb) : nb, nb,
-                  make_rsrc(a.a_scales, ns), valid ? (uint32_t)(tok * (H / 32)) : ns, ns, kt0, KT);
-    } else {
-      const uint32_t nb = (uint32_t)(a.a_rows * H * 2);
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
-      load_aslice(at, rs, valid ? (uint32_t)(tok * H * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
     }
     // one rotation of the ring: units i0 .. i0+D-1.  The first rotation is
     // peeled so that the loop is entered with the same loads in flight as at
@@ -498,24 +517,28 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
         const __amdgpu_buffer_rsrc_t rcn = make_rsrc(ecodes + codes_tile_offset(2 * fbn, 0, H), okn ? 2 * gbytes : 0u);
         const __amdgpu_buffer_rsrc_t rsn =
             make_rsrc(escales + scales_group_offset(2 * fbn, 0, H), okn ? 2 * gsbytes : 0u);
-        f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        compute_refill<FULL>(wt[j], at, kt0, KT, acc, [&](int part) {
+        f32x4_t acc[NA];
+#pragma unroll
+        for (int q = 0; q < NA; ++q) acc[q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        compute_refill<FULL, MS>(wt[j], at, kt0, KT, acc, [&](int part) {
           if (part < 0)
-            load_wscales(wt[j], rsn, gsbytes, kt0, KT);
+            load_wscales<NT>(wt[j], rsn, gsbytes, kt0, KT);
           else
-            load_wcodes(wt[j], rcn, gbytes, part, kt0, KT);
+            load_wcodes<NT>(wt[j], rcn, gbytes, part, kt0, KT);
         });
-        float* rb = red + (phase++ & 1) * (NW * 2 * 64 * 4);
-        if (reduce_to_wave0<2>(acc, rb, NW) && i < nu) {
+        float* rb = red + (phase++ & 1) * (NW * NA * 64 * 4);
+        if (reduce_to_wave0<NA>(acc, rb, NW) && i < nu) {
           const int64_t nn = (int64_t)um.fb(fb0 + i) * 16 + r;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = 4 * (lane >> 4) + q;
-            if (row < rows) {
-              const float v = swiglu_clamped(acc[0][q], acc[1][q], a.clamp_limit);
-              a.act[(p0 + row) * I + nn] = (uint16_t)f32_to_bf16_bits(v);
+          for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = 16 * ms + 4 * (lane >> 4) + q;
+              if (row < rows) {
+                const float v = swiglu_clamped(acc[2 * ms][q], acc[2 * ms + 1][q], a.clamp_limit);
+                a.act[(p0 + row) * I + nn] = (uint16_t)f32_to_bf16_bits(v);
+              }
             }
-          }
         }
       }
     };
@@ -527,9 +550,10 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
 
 // down + combine: unit = (tile, 16*NG output features).  Atomic combine adds
 // weight * y into out32[token]; ORDERED writes y per sorted position to ybuf.
-template <int KPW, int NG, int D, int AF, bool ORDERED, bool FULL>
+template <int KPW, int NG, int D, int AF, bool ORDERED, bool FULL, int MS, bool NT>
 __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
-  extern __shared__ float red[];  // [2][waves][NG][64][4]
+  constexpr int NA = NG * MS;     // accumulators: NG row groups of each row block
+  extern __shared__ float red[];  // [2][waves][NA][64][4]
   const int lane = lane_id();
   const int r = lane & 15;
   const int wave = threadIdx.x >> 6;
@@ -573,36 +597,39 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
     auto load_unit = [&](int i, WSlice<NG, KPW>& w) {
       const int fb = um.fb(fb0 + i);
       const bool ok = i < nu;
-      load_wslice(w, make_rsrc(ecodes + codes_tile_offset(fb * NG, 0, I), ok ? NG * gbytes : 0u),
+      load_wslice<NT>(w, make_rsrc(ecodes + codes_tile_offset(fb * NG, 0, I), ok ? NG * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(fb * NG, 0, I), ok ? NG * gsbytes : 0u), gbytes, gsbytes,
                   kt0, KT);
     };
     WSlice<NG, KPW> wt[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) load_unit(j, wt[j]);
-    const bool valid = r < rows;
-    const int64_t pr = p0 + r;
-    ASlice<KPW, AF> at;
-    if constexpr (AF != kActBf16) {
-      const int64_t rb = AF == kActFp8 ? I : I / 2;  // code bytes per row
-      const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (I / 32));
-      load_aslice(at, make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * rb) : nb, nb,
-                  make_rsrc(a.a_scales, ns), valid ? (uint32_t)(pr * (I / 32)) : ns, ns, kt0, KT);
-    } else {
-      const uint32_t nb = (uint32_t)(a.a_rows * I * 2);
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
-      load_aslice(at, rs, valid ? (uint32_t)(pr * I * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
-    }
-    // token and router weight of this lane's four output rows
-    int64_t tok[4];
-    float wgt[4];
-    if constexpr (!ORDERED) {
+    ASlice<KPW, AF> at[MS];
+    // token and router weight of this lane's four output rows of each block
+    int64_t tok[MS][4];
+    float wgt[MS][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 4 * (lane >> 4) + q;
-        const int64_t pp = p0 + (row < rows ? row : 0);
-        tok[q] = a.pos_tok[pp];
-        wgt[q] = a.pos_w[pp];
+    for (int ms = 0; ms < MS; ++ms) {
+      const bool valid = 16 * ms + r < rows;
+      const int64_t pr = p0 + 16 * ms + r;
+      if constexpr (AF != kActBf16) {
+        const int64_t rb = AF == kActFp8 ? I : I / 2;  // code bytes per row
+        const uint32_t nb = (uint32_t)(a.a_rows * rb), ns = (uint32_t)(a.a_rows * (I / 32));
+        load_aslice(at[ms], make_rsrc(a.a_codes, nb), valid ? (uint32_t)(pr * rb) : nb, nb,
+                    make_rsrc(a.a_scales, ns), valid ? (uint32_t)(pr * (I / 32)) : ns, ns, kt0, KT);
+      } else {
+        const uint32_t nb = (uint32_t)(a.a_rows * I * 2);
+        __amdgpu_buffer_rsrc_t rs = make_rsrc(a.a_bf16, nb);
+        load_aslice(at[ms], rs, valid ? (uint32_t)(pr * I * 2) : nb, nb, rs, 0u, 0u, kt0, KT);
+      }
+      if constexpr (!ORDERED) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 16 * ms + 4 * (lane >> 4) + q;
+          const int64_t pp = p0 + (row < rows ? row : 0);
+          tok[ms][q] = a.pos_tok[pp];
+          wgt[ms][q] = a.pos_w[pp];
+        }
       }
     }
     auto rotation = [&](int i0) {
@@ -615,32 +642,34 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
             make_rsrc(ecodes + codes_tile_offset(fbn * NG, 0, I), okn ? NG * gbytes : 0u);
         const __amdgpu_buffer_rsrc_t rsn =
             make_rsrc(escales + scales_group_offset(fbn * NG, 0, I), okn ? NG * gsbytes : 0u);
-        f32x4_t acc[NG];
+        f32x4_t acc[NA];
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) acc[gi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        compute_refill<FULL>(wt[j], at, kt0, KT, acc, [&](int part) {
+        for (int q = 0; q < NA; ++q) acc[q] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        compute_refill<FULL, MS>(wt[j], at, kt0, KT, acc, [&](int part) {
           if (part < 0)
-            load_wscales(wt[j], rsn, gsbytes, kt0, KT);
+            load_wscales<NT>(wt[j], rsn, gsbytes, kt0, KT);
           else
-            load_wcodes(wt[j], rcn, gbytes, part, kt0, KT);
+            load_wcodes<NT>(wt[j], rcn, gbytes, part, kt0, KT);
         });
-        float* rb = red + (phase++ & 1) * (NW * NG * 64 * 4);
-        if (reduce_to_wave0<NG>(acc, rb, NW) && i < nu) {
+        float* rb = red + (phase++ & 1) * (NW * NA * 64 * 4);
+        if (reduce_to_wave0<NA>(acc, rb, NW) && i < nu) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = 4 * (lane >> 4) + q;
-            if (row < rows) {
+          for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-              for (int gi = 0; gi < NG; ++gi) {
-                const int64_t nn = ((int64_t)um.fb(fb0 + i) * NG + gi) * 16 + r;
-                if constexpr (ORDERED) {
-                  a.ybuf[(p0 + row) * H + nn] = acc[gi][q];
-                } else {
-                  unsafeAtomicAdd(a.out32 + tok[q] * H + nn, wgt[q] * acc[gi][q]);
+            for (int q = 0; q < 4; ++q) {
+              const int row = 16 * ms + 4 * (lane >> 4) + q;
+              if (row < rows) {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                  const int64_t nn = ((int64_t)um.fb(fb0 + i) * NG + gi) * 16 + r;
+                  if constexpr (ORDERED) {
+                    a.ybuf[(p0 + row) * H + nn] = acc[ms * NG + gi][q];
+                  } else {
+                    unsafeAtomicAdd(a.out32 + tok[ms][q] * H + nn, wgt[ms][q] * acc[ms * NG + gi][q]);
+                  }
                 }
               }
             }
-          }
         }
       }
     };
@@ -775,18 +804,41 @@ hipError_t gate_up_v(const GemmArgs& a0, const RouteArgs* r, int64_t max_tiles, 
   const int nw = (KT + KPW - 1) / KPW;
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 2 / 16);
-  size_t lds = (size_t)2 * nw * 2 * 64 * 4 * sizeof(float);
+  const int ms = a.tile_ms == 2 ? 2 : 1;
+  size_t lds = (size_t)2 * nw * 2 * ms * 64 * 4 * sizeof(float);
   if (r) {
+    if (ms != 1) return hipErrorInvalidValue;
     const int64_t S = r->T * (int64_t)r->top_k;
     const int64_t bound = (r->E_local < S ? r->E_local : S) + S / 16;
     lds += (size_t)route_block_words(S, r->E_local, bound) * sizeof(int32_t);
     if (lds > kRouteFusedMaxLds) return hipErrorInvalidValue;
-    return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, true, true>, nw, lds, mu, s, a, *r)
-                         : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, true>, nw, lds, mu, s, a, *r);
+    return KT % KPW == 0
+               ? launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, true, true, 1, true>, nw, lds, mu, s, a, *r)
+               : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, true, 1, true>, nw, lds, mu, s, a, *r);
   }
   const RouteArgs none{};
-  return KT % KPW == 0 ? launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, true, false>, nw, lds, mu, s, a, none)
-                       : launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, false, false>, nw, lds, mu, s, a, none);
+  auto go = [&](auto full, auto kms, auto nt) -> hipError_t {
+    return launch_persistent(gate_up_ksplit_kernel<KPW, D, AF, decltype(full)::value, false, decltype(kms)::value,
+                                                   decltype(nt)::value>,
+                             nw, lds, mu, s, a, none);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  if (ms == 2 || a.wcache) {
+    // 32-row tiles and cached weight loads come only in the default variants
+    // (one unit ahead); cached loads only with 16-row tiles
+    if constexpr (D == 1) {
+      if (ms == 2) {
+        if constexpr (KPW == 4) return KT % KPW == 0 ? go(T_{}, M2{}, T_{}) : go(F_{}, M2{}, T_{});
+        return hipErrorInvalidValue;
+      }
+      return KT % KPW == 0 ? go(T_{}, M1{}, F_{}) : go(F_{}, M1{}, F_{});
+    }
+    return hipErrorInvalidValue;
+  }
+  return KT % KPW == 0 ? go(T_{}, M1{}, T_{}) : go(F_{}, M1{}, T_{});
 }
 
 // Share parameters of a down launch (down_ksplit_shares).
@@ -806,7 +858,8 @@ hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s, DownShar
   const int nw = (KT + KPW - 1) / KPW;
   if (nw > 8) return hipErrorInvalidValue;
   const int64_t mu = max_tiles * (a.N / 16 / NG);
-  const size_t lds = (size_t)2 * nw * NG * 64 * 4 * sizeof(float);
+  const int ms = a.tile_ms == 2 ? 2 : 1;
+  const size_t lds = (size_t)2 * nw * NG * ms * 64 * 4 * sizeof(float);
   auto go = [&](auto kernel) -> hipError_t {
     if (!q) return launch_persistent_capped(kernel, nw, lds, mu, kDownWgsPerCu, s, a);
     // the grid launch_persistent_capped takes
@@ -819,8 +872,21 @@ hipError_t down_v(const GemmArgs& a0, int64_t max_tiles, hipStream_t s, DownShar
     q->c = a.slot_c;
     return hipSuccess;
   };
-  return KT % KPW == 0 ? go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true>)
-                       : go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false>);
+  if (ms == 2 || a.wcache) {
+    if constexpr (D == 1) {
+      if (ms == 2) {
+        if constexpr (KPW == 4)
+          return KT % KPW == 0 ? go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true, 2, true>)
+                               : go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false, 2, true>);
+        return hipErrorInvalidValue;
+      }
+      return KT % KPW == 0 ? go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true, 1, false>)
+                           : go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false, 1, false>);
+    }
+    return hipErrorInvalidValue;
+  }
+  return KT % KPW == 0 ? go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, true, 1, true>)
+                       : go(down_ksplit_kernel<KPW, NG, D, AF, ORDERED, false, 1, true>);
 }
 
 template <int KPW, int D>
@@ -879,6 +945,14 @@ hipError_t down_dispatch(const GemmArgs& a, int64_t max_tiles, int af, bool orde
   return down_kd<8, 1>(a, max_tiles, af, ordered, s, q);
 }
 }  // namespace
+
+bool ksplit_two_blocks_fit(int64_t K, int af) {
+  // with 4 k-tiles per wave (K up to 4096) the second row block's activation
+  // registers fit beside the first in every activation format (at most 256
+  // VGPRs, two waves per SIMD); wider waves would spill
+  (void)af;
+  return pick(K, true).kpw <= 4;
+}
 
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;

@@ -51,7 +51,7 @@ struct RouteArgs {
   int32_t* pos_tok;     // [S]
   float* pos_w;         // [S]
   // per tile of height mt1 (== mt2 when set): the token of each of its rows
-  int32_t* tile_tok;    // [tile bound][16], or null
+  int32_t* tile_tok;    // [tile bound][mt1] (K-split tiles of 16 or 32 rows), or null
   // experts kept in bf16: xmap[e] >= 0 for such an expert (null: none).  They
   // keep their counts, offsets and sorted positions but get no tiles, so the
   // MXFP4 GEMMs never see them; the bf16 expert kernels cover their rows.
@@ -76,7 +76,7 @@ struct GemmArgs {
   const float* route_w;     // [S] (down: combine weights)
   const int32_t* pos_tok;   // [S] token of sorted position p
   const float* pos_w;       // [S] router weight of sorted position p
-  const int32_t* tile_tok;  // [tile bound][16] token of each row of a 16-row tile
+  const int32_t* tile_tok;  // [tile bound][16 tile_ms] token of each row of a K-split tile
   int32_t top_k, E_local;
   int64_t K, N;             // contraction length and weight rows (gate_up: N = 2I)
   float clamp_limit;
@@ -90,6 +90,11 @@ struct GemmArgs {
   // 16-row kernels: shares weighted by dispatch slot (set by the launcher)
   int32_t slot_cus;
   float slot_c;
+  // K-split kernels: 16-row blocks per tile (1: 16-row tiles, 2: 32-row tiles)
+  int32_t tile_ms;
+  // K-split kernels: 1 = weight loads without the non-temporal hint (an
+  // expert may span several tiles, whose units then find its slices in L2)
+  int32_t wcache;
   // 16-row kernels with the routing inside gate_up: per down workgroup b,
   // desc[2b] = {first unit, end unit, expert, rows} and desc[2b+1] = {first
   // sorted position, tile, 0, 0} of its share, written by gate_up's first
@@ -162,6 +167,7 @@ struct PreshuffleArgs {
 
 // variant of the grouped GEMMs chosen by the host
 struct GemmPlan {
+  int ksplit = 0; // 1: the K-split kernels (decode.hip), tiles of 16 ms rows, ms 1 or 2
   int ms;        // 16-row token subtiles per workgroup (token tile = 16 * ms)
   int fg;        // 16-feature groups per wave
   int nw;        // waves per workgroup
@@ -194,6 +200,9 @@ bool tile_fits(int af, int mt, int64_t K);
 // arguments (for the gate_up side of dn_desc).
 hipError_t down_ksplit_shares(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, int* grid, int* fb,
                               int* cus, float* c);
+// whether the K-split kernels hold the activations of two 16-row blocks
+// (32-row tiles) in registers for contraction length K and activation format af
+bool ksplit_two_blocks_fit(int64_t K, int af);
 hipError_t launch_down_ksplit(const GemmArgs& a, int64_t max_tiles, int af, bool ordered,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool ordered, hipStream_t stream);

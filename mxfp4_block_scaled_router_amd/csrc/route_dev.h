@@ -409,9 +409,10 @@ __device__ void wave_scan_experts(const int32_t* v, int n, const RouteArgs& a, b
 }
 
 // Sorted position pos of slot s: the permutation both ways, the side tables
-// (token and router weight w of pos) and -- for 16-row tiles -- the token of
-// that tile row.  e, off_e, tile_e: the slot's expert, its offset and first
-// 16-row tile (an expert kept in bf16 has no tiles).
+// (token and router weight w of pos) and -- for the K-split kernels' tiles
+// of mt1 (16 or 32) rows -- the token of that tile row.  e, off_e, tile_e:
+// the slot's expert, its offset and first mt1-row tile (an expert kept in
+// bf16 has no tiles).
 __device__ __forceinline__ void place_slot(const RouteArgs& a, int64_t s, int32_t pos, float w, int e,
                                            int32_t off_e, int32_t tile_e) {
   const int32_t t = (int32_t)(s / a.top_k);
@@ -421,7 +422,7 @@ __device__ __forceinline__ void place_slot(const RouteArgs& a, int64_t s, int32_
   a.pos_w[pos] = w;
   if (a.tile_tok && !bf16_expert(a, e)) {
     const int32_t rel = pos - off_e;
-    a.tile_tok[(int64_t)(tile_e + rel / 16) * 16 + rel % 16] = t;
+    a.tile_tok[(int64_t)(tile_e + rel / a.mt1) * a.mt1 + rel % a.mt1] = t;
   }
 }
 

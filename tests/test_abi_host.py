@@ -142,9 +142,11 @@ def test_plan_query(lib):
     assert mx.mxfp4_moe_plan(dims(T=1024, H=4480, flags=mx.MXFP4_MOE_A4), 2)["tile_rows"] == 128
     assert mx.mxfp4_moe_plan(dims(T=4096, flags=mx.MXFP4_MOE_A4), 2)["tile_rows"] == 128
     # speculative-verify shapes of the decode layer (T = 6 per sequence): the
-    # tile height follows the expected rows per expert T*k/E_global
+    # tile height follows the expected rows per expert T*k/E_global (K-split
+    # tiles of 32 rows from 64 tokens on where two row blocks fit the registers:
+    # not with the bf16 rows of the 5120-wide EP share)
     from mxfp4_block_scaled_router_amd import workloads as W
-    want = {"verify_b1": 16, "verify_b8": 16, "verify_b16": 16, "verify_b32": 16, "verify_b48": 64,
+    want = {"verify_b1": 16, "verify_b8": 16, "verify_b16": 32, "verify_b32": 32, "verify_b48": 64,
             "decode": 16, "ep_share": 16, "prefill": 128, "a4": 320, "a8": 128}
     for name, rows in want.items():
         wl = W.WORKLOADS[name]

@@ -60,6 +60,12 @@ SMALL_CASES = {
     "masks_T32": W.Workload("masks_T32", 32, 256, 128, 64, 64, 0, 8, seed=11),
     "masks_ep_T24": W.Workload("masks_ep_T24", 24, 256, 128, 128, 64, 32, 4, seed=12),
     "T33": W.Workload("T33", 33, 256, 128, 64, 64, 0, 8, seed=13),
+    # 32-row K-split tiles (64 tokens or more) under a skewed routing: hot
+    # experts span several tiles, the last ones partial
+    "skew_rows32": scaled("ep_share", T=128, H=512, I=256, E_global=64, E_local=64, first_local=0),
+    # 64 tokens whose bf16 rows are too wide for two row blocks (K of 36
+    # k-tiles): 16-row tiles with cached weight loads
+    "wide_h_t64": W.Workload("wide_h_t64", 64, 4608, 256, 32, 32, 0, 4, seed=14),
 }
 A4_CASES = {
     "a4_tiny": W.WORKLOADS["a4"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
@@ -174,7 +180,7 @@ def test_forward_small(name):
     _check_case(Case(SMALL_CASES[name]))
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_T5_H256", "mid_lds", "prefill_small"])
+@pytest.mark.parametrize("name", ["tiny", "decode_T5_H256", "mid_lds", "prefill_small", "skew_rows32"])
 def test_forward_deterministic(name):
     case = Case(SMALL_CASES[name], deterministic=True)
     g1, o = _check_case(case)
