@@ -223,6 +223,39 @@ def cpu_baseline(wl, inp, target_s, shared=False):
 
 # ---------------------------------------------------------------- timing
 
+# dense MFMA flops per CU per clock on CDNA4 (one 16x16x32 bf16 MFMA per SIMD
+# every 16 cycles; FP8 twice, FP4 four times that)
+MFMA_FLOP_PER_CU_CLK = {"bf16": 4096, "fp8": 8192, "fp4": 16384}
+
+
+def device_peaks():
+    """Peaks from the device's own attributes (hipDeviceGetAttribute): MFMA =
+    compute units x peak engine clock x the per-CU dense rate; for HBM the
+    bytes per reported memory clock over the bus (the attributes do not give
+    the transfers per clock of the memory).  Reported beside the nominal
+    figures the roofline fractions use."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    dev = ctypes.c_int(0)
+    hip.hipGetDevice(ctypes.byref(dev))
+
+    def attr(code):
+        v = ctypes.c_int(0)
+        return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev.value) == 0 else None
+    # hipDeviceAttributeClockRate, MultiprocessorCount, MemoryClockRate, MemoryBusWidth
+    clk, cus, mclk, bus = attr(5), attr(63), attr(60), attr(59)
+    out = {"compute_units": cus, "clock_khz": clk, "memory_clock_khz": mclk, "memory_bus_bits": bus}
+    if cus and clk:
+        out["mfma_tflops"] = {k: cus * clk * 1e3 * v / 1e12 for k, v in MFMA_FLOP_PER_CU_CLK.items()}
+    if mclk and bus:
+        # bytes per reported memory clock over the whole bus; the nominal HBM
+        # figure divided by it is the transfers per reported clock it assumes
+        out["hbm_gbps_per_transfer_per_clock"] = mclk * 1e3 * bus / 8 / 1e9
+        out["nominal_hbm_transfers_per_clock"] = HBM_PEAK_GBS / out["hbm_gbps_per_transfer_per_clock"]
+    out["nominal"] = {"mfma_tflops": MFMA_PEAK_TFLOPS, "hbm_gbps": HBM_PEAK_GBS}
+    return out
+
+
 def time_loop(step, n):
     import torch
     torch.cuda.synchronize()
@@ -469,8 +502,12 @@ def main():
                  "mfma_frac": (flops["gate_up"] + flops["down"]) / (ms_per_step * 1e-3) / 1e12 /
                  MFMA_PEAK_TFLOPS[mfma_dtype]},
         "phase_ms": phase_ms,
+        "device_peaks": device_peaks(),
         "source_digest": source_digest(),
     }
+    if wl.E_local < wl.E_global:
+        # an expert-parallel share: the local assignments it computes per second
+        rec["local_assignments_per_s"] = n_assign / (ms_per_step * 1e-3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.shared)
     print(json.dumps(rec), flush=True)

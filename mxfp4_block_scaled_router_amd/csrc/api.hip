@@ -96,7 +96,9 @@ int check_dims(const mxfp4_moe_dims* d, int64_t top_k, bool need_k, Shape* s) {
   if (!mul_ok(2 * s->I, s->H, &per) || !mul_ok(per, s->El, &tmp)) return MXFP4_MOE_ERR_SHAPE_OVERFLOW;
   // the large-tile GEMMs always use the slot-ordered combine: with many rows
   // per call, writing y and gathering it beats fp32 atomics into out32
-  if (choose_plan(*s).ms >= 8) s->ordered = true;
+  // (MXFP4_MOE_LARGE_ATOMIC=1, tuning builds only: keep the atomic combine)
+  const char* la = tuning_env("MXFP4_MOE_LARGE_ATOMIC");
+  if (choose_plan(*s).ms >= 8 && !(la && la[0] == '1')) s->ordered = true;
   return MXFP4_MOE_OK;
 }
 
