@@ -371,6 +371,40 @@ __device__ __forceinline__ UnitMap unit_share(int64_t ntiles, int FB, unsigned b
   return UnitMap{FB, 1, 0};
 }
 
+// Segments of a share [ub, ub + n) of tile-major units (FBV per tile), one per
+// tile, in walk order.  Plain: in order.  Aligned (an expert may span several
+// tiles, whose units are then processed by several workgroups of one XCD):
+// the share's last tile first, then the others in order, and inside each
+// segment the feature blocks rotated so that, where the segment holds it,
+// block (k mod FBV) is walked at the workgroup's k-th unit.  Every workgroup
+// then tends to read feature block j of an expert's tiles at the same time,
+// so the slice is fetched once and found in L2 by the others.
+struct Segment {
+  int t;     // tile
+  int fb0;   // first unit's feature block (in the workgroup's numbering)
+  int nu;    // units
+  int rot;   // unit i is feature block fb0 + (i + rot) mod nu
+  __device__ int fb(int i) const {
+    const int v = i + rot;
+    return fb0 + (v < nu ? v : v - nu);
+  }
+};
+__device__ __forceinline__ Segment share_segment(int64_t ub, int64_t ue, int FBV, int si, bool aligned, int k) {
+  const int t_first = (int)(ub / FBV), t_last = (int)((ue - 1) / FBV);
+  Segment g;
+  g.t = aligned && t_last > t_first ? (si == 0 ? t_last : t_first + si - 1) : t_first + si;
+  const int64_t tb = (int64_t)g.t * FBV;
+  const int64_t sb = ub > tb ? ub : tb, se = ue < tb + FBV ? ue : tb + FBV;
+  g.fb0 = (int)(sb - tb);
+  g.nu = (int)(se - sb);
+  g.rot = 0;
+  if (aligned) {
+    const int r = ((k - g.fb0) % FBV + FBV) % FBV;
+    g.rot = r < g.nu ? r : 0;
+  }
+  return g;
+}
+
 // gate_up: unit = (tile, 16 gate + 16 up features); writes act = SwiGLU(gate,
 // up) in bf16 at the tile's sorted positions.  Side duty: zero zero_buf.
 // ROUTE: every workgroup first routes the tokens itself (route_block_masks, or
@@ -447,9 +481,12 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
   // included), so a buffer is rewritten only after the barrier that follows
   // wave 0's reads of it
   int phase = 0;
-  for (int64_t sb = ub; sb < ue;) {
-    const int t = (int)(sb / FBV);
-    const int64_t se = ue < (int64_t)(t + 1) * FBV ? ue : (int64_t)(t + 1) * FBV;
+  const int nseg = ue > ub ? (int)((ue - 1) / FBV - ub / FBV) + 1 : 0;
+  const bool aligned = !ROUTE && a.wcache;
+  for (int si = 0, k = 0; si < nseg; ++si) {
+    const Segment sg = share_segment(ub, ue, FBV, si, aligned, k);
+    const int t = sg.t;
+    k += sg.nu;
     int4 ti;
     if constexpr (ROUTE) {
       const int4 v = rl.tiles[t];
@@ -462,10 +499,9 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
     const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
-    const int fb0 = (int)(sb - (int64_t)t * FBV);  // first unit of the segment, in the tile's numbering
-    const int nu = (int)(se - sb);
+    const int nu = sg.nu;
     auto load_unit = [&](int i, WSlice<2, KPW>& w) {
-      const int fb = um.fb(fb0 + i);
+      const int fb = um.fb(sg.fb(i));
       const bool ok = i < nu;
       load_wslice<NT>(w, make_rsrc(ecodes + codes_tile_offset(2 * fb, 0, H), ok ? 2 * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(2 * fb, 0, H), ok ? 2 * gsbytes : 0u), gbytes, gsbytes,
@@ -512,7 +548,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
         // unit i sits in slot j; unit i + D refills it as it is consumed
-        const int fbn = um.fb(fb0 + i + D);
+        const int fbn = um.fb(sg.fb(i + D));
         const bool okn = i + D < nu;
         const __amdgpu_buffer_rsrc_t rcn = make_rsrc(ecodes + codes_tile_offset(2 * fbn, 0, H), okn ? 2 * gbytes : 0u);
         const __amdgpu_buffer_rsrc_t rsn =
@@ -528,7 +564,7 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
         });
         float* rb = red + (phase++ & 1) * (NW * NA * 64 * 4);
         if (reduce_to_wave0<NA>(acc, rb, NW) && i < nu) {
-          const int64_t nn = (int64_t)um.fb(fb0 + i) * 16 + r;
+          const int64_t nn = (int64_t)um.fb(sg.fb(i)) * 16 + r;
 #pragma unroll
           for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -544,7 +580,6 @@ __global__ __launch_bounds__(512) void gate_up_ksplit_kernel(GemmArgs a, RouteAr
     };
     rotation(0);
     for (int i0 = D; i0 < nu; i0 += D) rotation(i0);
-    sb = se;
   }
 }
 
@@ -584,18 +619,20 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
   // included), so a buffer is rewritten only after the barrier that follows
   // wave 0's reads of it
   int phase = 0;
-  for (int64_t sb = ub; sb < ue;) {
-    const int t = (int)(sb / FBV);
-    const int64_t se = ue < (int64_t)(t + 1) * FBV ? ue : (int64_t)(t + 1) * FBV;
-    const int4 ti = desc && sb == ub ? first : tile_entry(a, t);
+  const int nseg = ue > ub ? (int)((ue - 1) / FBV - ub / FBV) + 1 : 0;
+  const bool aligned = !desc && a.wcache;
+  for (int si = 0, k = 0; si < nseg; ++si) {
+    const Segment sg = share_segment(ub, ue, FBV, si, aligned, k);
+    const int t = sg.t;
+    k += sg.nu;
+    const int4 ti = desc && si == 0 ? first : tile_entry(a, t);
     const int rows = ti.y;
     const int64_t p0 = ti.z;
     const uint8_t* ecodes = a.w_codes + (int64_t)ti.x * cpe;
     const uint8_t* escales = a.w_scales + (int64_t)ti.x * spe;
-    const int fb0 = (int)(sb - (int64_t)t * FBV);
-    const int nu = (int)(se - sb);
+    const int nu = sg.nu;
     auto load_unit = [&](int i, WSlice<NG, KPW>& w) {
-      const int fb = um.fb(fb0 + i);
+      const int fb = um.fb(sg.fb(i));
       const bool ok = i < nu;
       load_wslice<NT>(w, make_rsrc(ecodes + codes_tile_offset(fb * NG, 0, I), ok ? NG * gbytes : 0u),
                   make_rsrc(escales + scales_group_offset(fb * NG, 0, I), ok ? NG * gsbytes : 0u), gbytes, gsbytes,
@@ -636,7 +673,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         const int i = i0 + j;
-        const int fbn = um.fb(fb0 + i + D);
+        const int fbn = um.fb(sg.fb(i + D));
         const bool okn = i + D < nu;
         const __amdgpu_buffer_rsrc_t rcn =
             make_rsrc(ecodes + codes_tile_offset(fbn * NG, 0, I), okn ? NG * gbytes : 0u);
@@ -661,7 +698,7 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
               if (row < rows) {
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                  const int64_t nn = ((int64_t)um.fb(fb0 + i) * NG + gi) * 16 + r;
+                  const int64_t nn = ((int64_t)um.fb(sg.fb(i)) * NG + gi) * 16 + r;
                   if constexpr (ORDERED) {
                     a.ybuf[(p0 + row) * H + nn] = acc[ms * NG + gi][q];
                   } else {
@@ -675,7 +712,6 @@ __global__ __launch_bounds__(512) void down_ksplit_kernel(GemmArgs a) {
     };
     rotation(0);
     for (int i0 = D; i0 < nu; i0 += D) rotation(i0);
-    sb = se;
   }
 }
 
