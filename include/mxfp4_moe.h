@@ -41,7 +41,9 @@
  *     per-device caches filled once under a lock (the device check, the CU
  *     count, resident-grid sizes, kernels' LDS limits) and the static scratch of
  *     mxfp4_moe_forward_noalloc; results never depend on it.  The library reads
- *     no environment variables.
+ *     no environment variables.  A forward enqueues kernels only (no memset or
+ *     copy nodes, no host synchronisation), so it can be recorded into a HIP
+ *     graph and replayed.
  *   - Shapes: int64 counts, validated with checked arithmetic.  H and I must be
  *     multiples of 128; T may be 0 (nothing is enqueued).
  *   - Preconditions not checked (for cost): router logits are not NaN (a NaN
