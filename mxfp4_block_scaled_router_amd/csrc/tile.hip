@@ -24,10 +24,14 @@
 // issue order, so such a wait would also wait for every copy issued before.
 //
 // Bank conflicts.  The activation rows are stored with their 16-byte chunks
-// XOR-swizzled by the row (bf16: chunk c of row r at c ^ (r & 15); MXFP4:
-// block c at c ^ ((r >> 2) & 3)), chosen through the per-lane source address
-// of the copy, so the 16 lanes that read one MFMA operand hit 16 distinct
-// 16-byte bank groups.  Weight codes are read lane-contiguously.
+// XOR-swizzled by the row, chosen through the per-lane source address of the
+// copy: bf16 (256-byte rows) chunk c of row r at c ^ bf16_swz(r), MXFP4
+// (64-byte rows) block c at c ^ ((r >> 1) & 3), MXFP8 (128-byte rows) chunk c
+// at c ^ ((r >> 1) & 7).  These are the patterns a probe of the operand reads
+// (ds_read_b128, lane l reading row l % 16) measured free of LDS bank
+// conflicts on gfx950 (an XOR by r & 15 for bf16, or by (r >> 2) & 3 for
+// MXFP4, measures twice the LDS cycles).  Weight codes are read
+// lane-contiguously.
 //
 // MFMA layout: as in the other GEMMs (lane l: row l%16, MX block l/16 of the
 // k-tile; K element 8m+e of the block feeds bf16 MFMA m).  Eight waves form a
@@ -54,6 +58,10 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// bf16 activation rows: the physical 16-byte chunk of logical chunk c of row
+// r is c ^ bf16_swz(r & 15) (for each row a permutation of its 16 chunks)
+__device__ __forceinline__ int bf16_swz(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -251,7 +259,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     for (int jj = 0; jj < C::A_CP; ++jj) {
       const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);  // rows 4j .. 4j+3
       const int row = 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 15);
+      const int c = (lane & 15) ^ bf16_swz(row & 15);
       a_src[jj] = reinterpret_cast<const uint8_t*>(a.a_bf16) + (int64_t)rowidx[row] * rb + c * 16;
     }
   } else if constexpr (AF == kActFp8) {
@@ -273,7 +281,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
     for (int jj = 0; jj < C::A_CP; ++jj) {
       const int j = min(wave * C::A_CP + jj, C::A_COPIES - 1);  // rows 16j .. 16j+15
       const int row = 16 * j + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
       a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
     }
     const int row = 64 * (wave % C::AS_CHUNKS) + lane;
@@ -346,7 +354,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int row = C::rowblock(wm, rb) * 16 + (lane & 15);
-          const int phys = (4 * g + m) ^ (lane & 15);
+          const int phys = (4 * g + m) ^ bf16_swz(lane & 15);
           av[rb] = __builtin_bit_cast(
               bf16x8_t, *reinterpret_cast<const u32x4_t*>(aslot + row * 256 + phys * 16));
         }
@@ -375,7 +383,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
           A[rb] = (i32x8_t){(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
                             (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
         } else {
-          const int phys = g ^ ((row >> 2) & 3);
+          const int phys = g ^ ((row >> 1) & 3);
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(aslot + row * 64 + phys * 16);
           A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
         }
@@ -503,9 +511,9 @@ __device__ __forceinline__ void tile_mainloop_pf(const GemmArgs& a, const TileIt
         c = (lane & 7) ^ ((row >> 1) & 7);
       } else {
         // copy j fills rows 16j .. 16j+15, lane i row 16j + i/4 at block i % 4,
-        // which holds the row's logical block (i % 4) ^ ((row >> 2) & 3)
+        // which holds the row's logical block (i % 4) ^ ((row >> 1) & 3)
         row = 16 * j + (lane >> 2);
-        c = (lane & 3) ^ ((row >> 2) & 3);
+        c = (lane & 3) ^ ((row >> 1) & 3);
       }
       a_src[jj] = a.a_codes + (int64_t)rowidx[row] * rb + c * 16;
     }
@@ -589,7 +597,7 @@ __device__ __forceinline__ void tile_mainloop_pf(const GemmArgs& a, const TileIt
         f.A[rb] = (i32x8_t){(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
                             (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
       } else {
-        const int phys = g ^ ((row >> 2) & 3);
+        const int phys = g ^ ((row >> 1) & 3);
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(as_ + row * 64 + phys * 16);
         f.A[rb] = (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
       }
