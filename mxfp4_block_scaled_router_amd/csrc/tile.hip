@@ -348,23 +348,49 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, const TileItem&
       float sc[WN];
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) sc[cb] = e8m0_scale_operand(sbyte[cb]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        bf16x8_t av[RB];
+      // Sub-step m (K 32 m .. 32 m + 31).  Each weight row group's E2M1 codes
+      // are unpacked while the previous row group's MFMAs issue (one unpack
+      // between two MFMAs, into the other of two operand registers), and the
+      // A operands of sub-step m + 1 are read after the first row group's
+      // MFMAs, so their LDS latency hides behind the rest of the sub-step.
+      // The scheduling-group barriers fix that interleave; 12 LDS reads at
+      // most are in flight, within lgkmcnt's range.
+      bf16x8_t av[2][RB];
+      auto read_a = [&](int m, bf16x8_t (&dst)[RB]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int row = C::rowblock(wm, rb) * 16 + (lane & 15);
           const int phys = (4 * g + m) ^ bf16_swz(lane & 15);
-          av[rb] = __builtin_bit_cast(
+          dst[rb] = __builtin_bit_cast(
               bf16x8_t, *reinterpret_cast<const u32x4_t*>(aslot + row * 256 + phys * 16));
         }
+      };
+      read_a(0, av[0]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t bv[2];
+        bv[0] = unpack8_e2m1(bw[0][m], sc[0]);
 #pragma unroll
         for (int cb = 0; cb < WN; ++cb) {
-          const bf16x8_t bv = unpack8_e2m1(bw[cb][m], sc[cb]);
+          if (cb + 1 < WN) bv[(cb + 1) & 1] = unpack8_e2m1(bw[cb + 1][m], sc[cb + 1]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rb], bv, acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m & 1][rb], bv[cb & 1], acc[rb][cb], 0, 0, 0);
+          if (cb == 0 && m < 3) read_a(m + 1, av[(m + 1) & 1]);
         }
+        // schedule: the first row group's unpack, then MFMA / unpack pairs
+        // (the A reads of the next sub-step after the first row group), then
+        // the last row group's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+#pragma unroll
+        for (int i = 0; i < 4 * (WN - 1); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+          if (i == RB - 1 && m < 3) __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       i32x8_t A[RB];

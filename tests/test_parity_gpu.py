@@ -79,6 +79,9 @@ A4_CASES = {
     # tiles, a cold one a partial tile
     "a4_skew": W.WORKLOADS["a4"].replace(T=1024, H=512, I=256, E_global=16, E_local=16, top_k=4,
                                          logits_kind="zipf_bias"),
+    # 320-row tiles at the widest K whose scale rows fit LDS: gate_up's rows of
+    # 136 scale bytes (not a multiple of 16) take the 4-byte copies
+    "a4_k4352": W.WORKLOADS["a4"].replace(T=128, H=4352, I=256, E_global=8, E_local=8, top_k=4),
 }
 A8_CASES = {
     "a8_tiny": W.WORKLOADS["a8"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
