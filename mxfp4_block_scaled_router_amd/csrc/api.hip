@@ -148,16 +148,26 @@ GemmPlan choose_plan(const Shape& s) {
     p.ms = 4; p.fg = 2; p.nw = 4;
   } else if (s.a4 && (forced == 0 || forced == 320) && s.S <= kRowsPerExpert320 * s.Eg &&
              tile_fits(s.af(), 320, s.H) && tile_fits(s.af(), 320, s.I)) {
-    // MXFP4 activations, experts expected to hold at most 256 rows:
-    // gate_up on 320-token x 128-weight-row tiles, one per expert (its weights
-    // stream once; 1.07x faster than 128 x 512 tiles at the A4 prefill shape
-    // on MI355X).  MXFP8 activations stay on 128-row tiles (their 320-row
-    // stages leave too few slots: 1.3x slower).
+    // MXFP4 activations, experts expected to hold at most 256 rows: 320-row
+    // tiles, one per expert, so each expert's weights stream once.  Where
+    // their LDS fits (K a multiple of 512, K/32 <= 128), the direct-weight
+    // 320 x 256 tiles for both GEMMs (weights straight into registers; A4
+    // prefill shape on MI355X: gate_up 455 -> 390 us, down 283 -> 246 us,
+    // step 0.83 -> 0.72 ms); otherwise gate_up on 320 x 128 tiles through the
+    // LDS ring and down on 128 x 512 tiles (every activation row of a 320-row
+    // tile re-read by each 128-row weight block: 1.2x slower there).  MXFP8
+    // activations stay on 128-row tiles (their 320-row stages leave too few
+    // slots: 1.3x slower).  MXFP4_MOE_DW (tuning builds only) = 0: no
+    // direct-weight tiles, 1: gate_up only, 2: both.
     p.ms = 20; p.fg = 0; p.nw = 4;
-    // down (K = I, every activation row re-read by each 128-row weight block
-    // of a 320-row tile) keeps the 128 x 512 tiles: 1.2x faster at the A4
-    // prefill shape on MI355X
     p.ms_dn = 8;
+    int dw = 2;
+    if (const char* env = tuning_env("MXFP4_MOE_DW")) dw = atoi(env);
+    if (dw >= 1 && tile_fits(s.af(), 320, s.H, true)) p.dw = 1;
+    if (dw >= 2 && tile_fits(s.af(), 320, s.I, true)) {
+      p.ms_dn = 20;
+      p.dw_dn = 1;
+    }
   } else {
     // 128-token x 512-weight-row tiles staged through LDS
     p.ms = 8; p.fg = 0; p.nw = 4;
@@ -423,7 +433,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
     }
   }
   e = plan.ksplit    ? launch_gate_up_ksplit(g, fused_route ? &r : nullptr, max_tiles(s, mt), s.af(), stream)
-      : plan.ms >= 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), mt, stream)
+      : plan.ms >= 8 ? launch_gate_up_tile(g, max_tiles(s, mt), s.af(), mt, plan.dw, stream)
                      : launch_gate_up(g, plan, max_tiles(s, mt), s.a4, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (has_x) {
@@ -468,7 +478,7 @@ int run_forward(const Shape& s, const Layout& L, const void* x, const float* log
   g.out32 = s.ordered ? nullptr : at<float>(ws, L.out32);
   g.ybuf = s.ordered ? at<float>(ws, L.ybuf) : nullptr;
   e = plan.ksplit    ? launch_down_ksplit(g, max_tiles(s, mt), s.af(), s.ordered, stream)
-      : plan.ms >= 8 ? launch_down_tile(g, max_tiles(s, mt_dn), s.af(), mt_dn, s.ordered, stream)
+      : plan.ms >= 8 ? launch_down_tile(g, max_tiles(s, mt_dn), s.af(), mt_dn, plan.dw_dn, s.ordered, stream)
                      : launch_down(g, plan, max_tiles(s, mt), s.a4, s.ordered, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (has_x) {

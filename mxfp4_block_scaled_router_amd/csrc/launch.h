@@ -172,6 +172,8 @@ struct GemmPlan {
   int fg;        // 16-feature groups per wave
   int nw;        // waves per workgroup
   int ms_dn = 0; // down's token tile in 16-row subtiles when it differs from gate_up's (0: ms)
+  int dw = 0;    // 320-row tiles: gate_up on the direct-weight tiles
+  int dw_dn = 0; // 320-row tiles: down on the direct-weight tiles
   int down_ms() const { return ms_dn ? ms_dn : ms; }
 };
 
@@ -189,13 +191,17 @@ hipError_t launch_down(const GemmArgs& a, const GemmPlan& p, int64_t max_tiles, 
 hipError_t launch_gate_up_ksplit(const GemmArgs& a, const RouteArgs* route, int64_t max_tiles, int af,
                                  hipStream_t stream);
 // Large token tiles through an LDS ring fed by global->LDS copies (tile.hip):
-// mt = 128 (128 x 512 tiles) or, with MX activations, 320 (320 x 128 tiles)
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, hipStream_t stream);
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool ordered,
+// mt = 128 (128 x 512 tiles) or, with MX activations, 320 (320 x 128 tiles);
+// dw: with MXFP4 activations and mt = 320, the direct-weight 320 x 256 tiles
+// (weights loaded into registers, activations through LDS)
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool dw,
+                               hipStream_t stream);
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool dw, bool ordered,
                             hipStream_t stream);
-// whether the tile kernels of height mt take a contraction of length K with
-// activation format af (the 320-row tiles hold their rows' scale bytes in LDS)
-bool tile_fits(int af, int mt, int64_t K);
+// whether the tile kernels of height mt (dw: the direct-weight tiles) take a
+// contraction of length K with activation format af (the 320-row tiles hold
+// their rows' scale bytes in LDS)
+bool tile_fits(int af, int mt, int64_t K, bool dw = false);
 // The grid and share parameters launch_down_ksplit will use for these
 // arguments (for the gate_up side of dn_desc).
 hipError_t down_ksplit_shares(const GemmArgs& a, int64_t max_tiles, int af, bool ordered, int* grid, int* fb,

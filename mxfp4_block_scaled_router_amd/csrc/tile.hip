@@ -48,6 +48,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -94,6 +95,7 @@ struct Cfg {
   // reads the next k-tile's operands from LDS into a second register set
   // while its MFMAs run on the current one (tile_mainloop_pf)
   static constexpr bool PF = PF_;
+  static constexpr bool DW = false;
   static constexpr int WMW = WMW_, WNW = kWaves / WMW_, RB = RB_, WN = WN_;
   static constexpr bool IL = IL_;
   static constexpr int MT = 16 * RB * WMW;                      // token rows per tile
@@ -695,28 +697,252 @@ __device__ __forceinline__ void tile_mainloop_pf(const GemmArgs& a, const TileIt
   wait_vm<0>();
 }
 
+// Direct-weight tiles (MXFP4 activations): a workgroup owns a 320-token x
+// 256-weight-row tile of one expert.  Only the activation rows go through
+// LDS; every wave loads its own four weight row groups' codes straight into
+// registers (the preshuffled 1 KiB of a row group and k-tile is exactly one
+// MFMA B operand), two k-tiles ahead.  With the weights in LDS every weight
+// byte crossed LDS twice (the copy, then each of the four waves that read its
+// row group) and the LDS traffic and per-k-tile waits set the pace; here LDS
+// carries the activations only, and the two M halves of the workgroup read
+// each weight slice from HBM and then L2.
+//
+// The activation rows of a k-tile are loaded into registers (8 bytes per lane
+// and load, five loads per wave) one step before their k-tile and written to
+// one of two LDS slots just before the step's barrier.  Every global load of
+// the loop thus writes registers, so the compiler's own vmcnt waits count
+// them exactly (loads that write LDS directly would make it wait for all).
+// The tile's activation scale bytes (rows of kRsStride bytes: K/32 <= 128)
+// and the weight scale dwords of its 16 row groups ([16][K/512][256 B]) are
+// copied into LDS once, before the loop.
+//   waves: 2 x 4 grid, wave (wm, wn) owns row blocks wm, wm + 2, ... (10) and
+//   row groups 4 wn .. 4 wn + 3 (gate / up pairs); 160 accumulator VGPRs.
+constexpr int kRsStride = 128;
+template <int AF>
+struct CfgDW {
+  static constexpr bool DW = true, PF = false, RS = true, IL = true;
+  static constexpr int WMW = 2, WNW = kWaves / WMW, RB = 10, WN = 4;
+  static constexpr int MT = 16 * RB * WMW;  // 320 token rows
+  static constexpr int NRG = WN * WNW;      // 16 weight row groups
+  static constexpr int NT = 16 * NRG;       // 256 weight rows
+  static constexpr int ARB = act_row_bytes(AF);
+  static constexpr int A_BYTES = MT * ARB;
+  static constexpr int A_LD = A_BYTES / (kThreads * 8);  // 8-byte activation loads per lane and k-tile
+  static constexpr int ROWS_OFF = 2 * A_BYTES;
+  static constexpr int RS_OFF = ROWS_OFF + MT * 4;
+  static constexpr int WSC_OFF = RS_OFF + MT * kRsStride;
+  static constexpr size_t lds_bytes(int64_t K) {
+    return (size_t)WSC_OFF + (size_t)NRG * (size_t)(K / 512) * 256;
+  }
+  // K a multiple of 512 (whole scale groups, 16-byte scale chunks) and at
+  // most kRsStride scale bytes per row
+  static constexpr bool fits(int64_t K) {
+    return K > 0 && K % 512 == 0 && K / 32 <= kRsStride && lds_bytes(K) <= kTileLdsMax;
+  }
+  static_assert(AF == kActFp4 && A_BYTES % (kThreads * 8) == 0 && (kThreads * 8) % 512 == 0, "direct-weight tile");
+  __device__ static constexpr int rowblock(int wm, int rb) { return wm + WMW * rb; }
+};
+
+template <int AF, typename C, typename FillRows>
+__device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
+                                                 uint8_t* lds, f32x4_t (&acc)[C::RB][C::WN], FillRows fill_rows) {
+  constexpr int WN = C::WN, RB = C::RB;
+  const int lane = lane_id();
+  const int g = lane >> 4, l15 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % C::WMW, wn = wave / C::WMW;
+  const int KT = (int)(K / kTileK);
+  const int NQ = KT / 4;
+  const int RSB = (int)(K / 32);  // activation scale bytes per row
+  const int32_t* rowidx = reinterpret_cast<const int32_t*>(lds + C::ROWS_OFF);
+  uint8_t* rs = lds + C::RS_OFF;
+  uint8_t* wsc = lds + C::WSC_OFF;
+
+  const int nrg = (int)(N / 16);
+  const int rg0 = it.n0 / 16;
+  const int nrgt = nrg - rg0 < C::NRG ? nrg - rg0 : C::NRG;  // row groups of this tile
+  {
+    // weight scale dwords: the tile's row groups are contiguous
+    const uint8_t* src = a.w_scales + (int64_t)it.e * scales_per_expert(N, K) + scales_group_offset(rg0, 0, K);
+    const int n = nrgt * NQ / 4;  // whole KiB
+#pragma unroll 1
+    for (int i = wave; i < n; i += kWaves) copy16(src + i * 1024 + lane * 16, wsc + i * 1024);
+#pragma unroll 1
+    for (int i = wave; i < (nrgt * NQ) % 4; i += kWaves)
+      copy4(src + n * 1024 + i * 256 + lane * 4, wsc + n * 1024 + i * 256);
+  }
+  // weight codes: one buffer descriptor over the expert; the row group and
+  // k-tile as the scalar offset, the lane's 16 bytes as the vector offset, a
+  // k-tile past K an out-of-range vector offset (zeros, no memory traffic)
+  const int64_t cpe = codes_per_expert(N, K);
+  const __amdgpu_buffer_rsrc_t wrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w_codes + (int64_t)it.e * cpe), (short)0, (int)cpe, 0x00020000);
+  uint32_t brg[WN];    // byte offset of the row group (wave-uniform)
+  uint32_t wsoff[WN];  // LDS offset of the row group's scale dwords (group 0)
+#pragma unroll
+  for (int cb = 0; cb < WN; ++cb) {
+    const int rgl = min(wn * WN + cb, nrgt - 1);  // a partial tile repeats its last row group
+    brg[cb] = __builtin_amdgcn_readfirstlane((uint32_t)codes_tile_offset(rg0 + rgl, 0, K));
+    wsoff[cb] = (uint32_t)(rgl * NQ * 256 + lane * 4);
+  }
+  u32x4_t B[2][WN];
+  auto load_b = [&](int kt, u32x4_t (&dst)[WN]) {
+    const uint32_t vo = (uint32_t)lane * 16u + (kt < KT ? 0u : 0x80000000u);
+    const uint32_t ko = (uint32_t)(kt < KT ? kt : 0) * 1024u;
+#pragma unroll
+    for (int cb = 0; cb < WN; ++cb)
+      dst[cb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrc, vo, brg[cb] + ko, kCpolNT));
+  };
+  // prologue.  The weight scale copies and the weights of k-tiles 0 and 1
+  // depend on the item only and go out first; then the tile's rows (their
+  // tokens or sorted positions) are filled in, the row scale copies and the
+  // activations of k-tiles 0 and 1 follow, and everything lands before the
+  // loop, whose waits then count register loads only.
+  __builtin_amdgcn_sched_barrier(0);
+  load_b(0, B[0]);
+  load_b(1, B[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  fill_rows();
+  // one-time copies.  Row scale bytes: row r at rs + r * kRsStride, its
+  // 16-byte chunk c at c ^ ((r >> 1) & 7) (a copy covers 8 rows; lanes past
+  // a row's K / 32 bytes copy its chunk 0 again into an unread chunk)
+  {
+    const int nch = RSB / 16;
+#pragma unroll 1
+    for (int i = wave; i < C::MT / 8; i += kWaves) {
+      const int row = 8 * i + (lane >> 3);
+      const int cp = lane & 7;               // physical chunk
+      const int cl = cp ^ ((row >> 1) & 7);  // logical chunk it holds
+      copy16(a.a_scales + (int64_t)rowidx[row] * RSB + (cl < nch ? cl : 0) * 16, rs + i * 1024);
+    }
+  }
+  // activation loads of one k-tile: 8-byte piece P = 320 w + 64 j + lane of
+  // the tile's 2560 (row P / 8, piece P % 8 of its 64 bytes), stored at its
+  // chunk's swizzled place: logical chunk c of row r at c ^ ((r >> 1) & 3);
+  // (r >> 1) & 3 does not depend on j, so piece j is an immediate 512 j away
+  uint32_t a_off[C::A_LD];
+  uint32_t a_dst;
+  {
+    const int p8 = lane & 7;
+#pragma unroll
+    for (int j = 0; j < C::A_LD; ++j) {
+      const int row = (C::MT / kWaves) * wave + 8 * j + (lane >> 3);
+      a_off[j] = (uint32_t)rowidx[row] * (uint32_t)(K / 2) + (uint32_t)p8 * 8u;
+    }
+    const int row = (C::MT / kWaves) * wave + (lane >> 3);
+    a_dst = (uint32_t)(row * 64 + (((p8 >> 1) ^ ((row >> 1) & 3)) << 4) + (p8 & 1) * 8);
+  }
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+  u32x2_t areg[2][C::A_LD];
+  auto load_a = [&](int kt, u32x2_t (&dst)[C::A_LD]) {
+    const int k = kt < KT ? kt : KT - 1;
+    const uint8_t* base = a.a_codes + (int64_t)k * 64;
+#pragma unroll
+    for (int j = 0; j < C::A_LD; ++j) dst[j] = *reinterpret_cast<const u32x2_t*>(base + a_off[j]);
+  };
+  auto store_a = [&](int kt, const u32x2_t (&src)[C::A_LD]) {
+    uint8_t* dst = lds + (kt & 1) * C::A_BYTES + a_dst;
+#pragma unroll
+    for (int j = 0; j < C::A_LD; ++j) *reinterpret_cast<u32x2_t*>(dst + 512 * j) = src[j];
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(0, areg[0]);
+  load_a(1, areg[1]);
+  wait_vm<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  // operand reads: row block rb of the wave is tile row 32 rb + 16 wm + l15;
+  // the MXFP4 swizzle (row >> 1) & 3 and the scale swizzle (row >> 1) & 7
+  // depend on l15 only, so every row block is an immediate offset from one
+  // per-lane address
+  const int row0 = 16 * wm + l15;
+  const uint32_t a_lane = (uint32_t)(row0 * 64 + ((g ^ ((row0 >> 1) & 3)) * 16));
+  const int ssw = (row0 >> 1) & 7;
+  const uint32_t s_lane = (uint32_t)(row0 * kRsStride + g);
+
+  uint32_t scur[WN];
+
+  // step kt (J = kt % 4): store k-tile kt's activation rows (loaded in the
+  // previous step) into slot kt & 1 -- the compiler waits for those loads,
+  // and so for the earlier weight loads of k-tile kt -- then a barrier
+  // publishes the slot (every wave's reads of slot kt & 1 from step kt - 2
+  // ended before its barrier in step kt - 1); load k-tile kt + 1's
+  // activation rows, MFMAs of k-tile kt, weight loads of k-tile kt + 2 into
+  // the registers just consumed.
+  auto step = [&](int kt, auto Jc, u32x4_t (&bset)[WN], u32x2_t (&aset)[C::A_LD]) {
+    constexpr int J = decltype(Jc)::value;
+    store_a(kt, aset);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stores are in LDS, this wave's reads of slot kt - 1 done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (J == 0) {
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb)
+        scur[cb] = *reinterpret_cast<const uint32_t*>(wsc + wsoff[cb] + (kt >> 2) * 256);
+    }
+    load_a(kt + 2, aset);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* ab = lds + (kt & 1) * C::A_BYTES + a_lane;
+    const uint8_t* sbp = rs + s_lane + (((kt >> 2) ^ ssw) << 4) + 4 * J;
+    u32x4_t av[RB];
+    uint32_t as[RB];
+    auto read_a = [&](int rb) {
+      av[rb] = *reinterpret_cast<const u32x4_t*>(ab + rb * 32 * 64);
+      as[rb] = sbp[rb * 32 * kRsStride];
+    };
+    read_a(0);
+    read_a(1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb + 2 < RB) read_a(rb + 2);
+      const i32x8_t A = {(int)av[rb][0], (int)av[rb][1], (int)av[rb][2], (int)av[rb][3], 0, 0, 0, 0};
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb) {
+        const i32x8_t Bv = {(int)bset[cb][0], (int)bset[cb][1], (int)bset[cb][2], (int)bset[cb][3], 0, 0, 0, 0};
+        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, acc[rb][cb], 4, 4, 0, (int)as[rb], J,
+                                                                       (int)scur[cb]);
+      }
+    }
+    // two operand reads, then four MFMAs, per row block (reads two blocks ahead)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb + 2 < RB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(kt + 2, bset);
+  };
+  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
+    step(kt0, std::integral_constant<int, 0>{}, B[0], areg[0]);
+    step(kt0 + 1, std::integral_constant<int, 1>{}, B[1], areg[1]);
+    step(kt0 + 2, std::integral_constant<int, 2>{}, B[0], areg[0]);
+    step(kt0 + 3, std::integral_constant<int, 3>{}, B[1], areg[1]);
+  }
+}
+
 }  // namespace
 
 // gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
 template <int AF, typename C>
-__global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
+__device__ __forceinline__ void tile_gate_up_item(const GemmArgs& a, const TileItem& it, uint8_t* lds) {
   constexpr int WN = C::WN, RB = C::RB;
-  zero_duty(a);
   const int64_t H = a.K, I = a.N / 2;
-  const int ntl = (int)((a.N + C::NT - 1) / C::NT);
-  TileItem it;
-  if (!tile_item(a, ntl, C::NT, &it)) return;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
-  for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
-    rowidx[r] = a.sorted[it.p0 + (r < it.rows ? r : 0)] / a.top_k;  // token of the tile row
-  __syncthreads();
+  auto fill_rows = [&] {
+    for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
+      rowidx[r] = a.sorted[it.p0 + (r < it.rows ? r : 0)] / a.top_k;  // token of the tile row
+    __syncthreads();
+  };
+  if constexpr (!C::DW) fill_rows();
   f32x4_t acc[RB][WN];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  if constexpr (C::PF)
+  if constexpr (C::DW)
+    tile_mainloop_dw<AF, C>(a, it, H, a.N, lds, acc, fill_rows);
+  else if constexpr (C::PF)
     tile_mainloop_pf<AF, C>(a, it, H, a.N, lds, acc);
   else
     tile_mainloop<AF, C>(a, it, H, a.N, lds, acc);
@@ -745,25 +971,37 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   }
 }
 
-// down + combine.
-template <int AF, bool ORDERED, typename C>
-__global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
+// gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
+template <int AF, typename C>
+__global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  constexpr int WN = C::WN, RB = C::RB;
-  const int64_t I = a.K, H = a.N;
+  zero_duty(a);
   const int ntl = (int)((a.N + C::NT - 1) / C::NT);
   TileItem it;
   if (!tile_item(a, ntl, C::NT, &it)) return;
+  tile_gate_up_item<AF, C>(a, it, lds);
+}
+
+// down + combine.
+template <int AF, bool ORDERED, typename C>
+__device__ __forceinline__ void tile_down_item(const GemmArgs& a, const TileItem& it, uint8_t* lds) {
+  constexpr int WN = C::WN, RB = C::RB;
+  const int64_t I = a.K, H = a.N;
   int32_t* rowidx = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
-  for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
-    rowidx[r] = (int32_t)(it.p0 + (r < it.rows ? r : 0));  // sorted position of the tile row
-  __syncthreads();
+  auto fill_rows = [&] {
+    for (int r = threadIdx.x; r < C::MT; r += blockDim.x)
+      rowidx[r] = (int32_t)(it.p0 + (r < it.rows ? r : 0));  // sorted position of the tile row
+    __syncthreads();
+  };
+  if constexpr (!C::DW) fill_rows();
   f32x4_t acc[RB][WN];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  if constexpr (C::PF)
+  if constexpr (C::DW)
+    tile_mainloop_dw<AF, C>(a, it, I, H, lds, acc, fill_rows);
+  else if constexpr (C::PF)
     tile_mainloop_pf<AF, C>(a, it, I, H, lds, acc);
   else
     tile_mainloop<AF, C>(a, it, I, H, lds, acc);
@@ -797,6 +1035,15 @@ __global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
     }
 }
 
+template <int AF, bool ORDERED, typename C>
+__global__ __launch_bounds__(kThreads) void tile_down_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int ntl = (int)((a.N + C::NT - 1) / C::NT);
+  TileItem it;
+  if (!tile_item(a, ntl, C::NT, &it)) return;
+  tile_down_item<AF, ORDERED, C>(a, it, lds);
+}
+
 // ------------------------------------------------------------------ launchers
 namespace {
 // 128 x 512 tiles (bf16 prefill and large MX calls) and 320 x 128 tiles (MX
@@ -806,15 +1053,18 @@ using Cfg128 = Cfg<AF, 2, 4, 8, false, AF == kActFp4 ? 3 : 2, AF == kActFp4 ? 3 
 template <int AF>
 using Cfg320 = Cfg<AF, 4, 5, 4, true, AF == kActFp8 ? 3 : 4, AF == kActFp8 ? 3 : 4, true, AF == kActFp4>;
 
+template <int AF>
+using Cfg320DW = CfgDW<AF>;
+
 int64_t tile_grid(int64_t max_tiles, int64_t N, int nt) {
   const int64_t items = max_tiles * ((N + nt - 1) / nt);
   return 8 * ((items + 7) / 8);
 }
 
-// Launch with `lds` bytes of dynamic LDS; the first launch of each kernel on a
-// device raises its dynamic-LDS limit there to kTileLdsMax.
+// The first use of each kernel on a device raises its dynamic-LDS limit there
+// to kTileLdsMax.
 template <typename Kernel>
-hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a, hipStream_t s) {
+hipError_t lds_limit(Kernel kernel) {
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   static hipError_t attr[kMaxDevices];
@@ -825,7 +1075,13 @@ hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a
     attr[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTileLdsMax);
   });
-  if (attr[dev] != hipSuccess) return attr[dev];
+  return attr[dev];
+}
+
+// Launch with `lds` bytes of dynamic LDS.
+template <typename Kernel>
+hipError_t launch_lds(Kernel kernel, int64_t grid, size_t lds, const GemmArgs& a, hipStream_t s) {
+  if (hipError_t e = lds_limit(kernel); e != hipSuccess) return e;
   if (lds > kTileLdsMax) return hipErrorInvalidValue;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
@@ -837,22 +1093,31 @@ hipError_t gate_up_c(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   const int64_t grid = tile_grid(max_tiles, a.N, C::NT);
   return launch_lds(tile_gate_up_kernel<AF, C>, grid, C::lds_bytes(a.K), a, s);
 }
+template <int AF, bool ORDERED, typename C>
+hipError_t down_co(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  const int64_t grid = tile_grid(max_tiles, a.N, C::NT);
+  return launch_lds(tile_down_kernel<AF, ORDERED, C>, grid, C::lds_bytes(a.K), a, s);
+}
 template <int AF, typename C>
 hipError_t down_c(const GemmArgs& a, int64_t max_tiles, bool ordered, hipStream_t s) {
-  const int64_t grid = tile_grid(max_tiles, a.N, C::NT);
-  return ordered ? launch_lds(tile_down_kernel<AF, true, C>, grid, C::lds_bytes(a.K), a, s)
-                 : launch_lds(tile_down_kernel<AF, false, C>, grid, C::lds_bytes(a.K), a, s);
+  return ordered ? down_co<AF, true, C>(a, max_tiles, s) : down_co<AF, false, C>(a, max_tiles, s);
 }
 
 template <int AF>
-hipError_t gate_up_af(const GemmArgs& a, int64_t max_tiles, int mt, hipStream_t s) {
+hipError_t gate_up_af(const GemmArgs& a, int64_t max_tiles, int mt, bool dw, hipStream_t s) {
+  if constexpr (AF == kActFp4)
+    if (dw && mt == Cfg320DW<AF>::MT) return gate_up_c<AF, Cfg320DW<AF>>(a, max_tiles, s);
+  if (dw) return hipErrorInvalidValue;
   if constexpr (AF != kActBf16)
     if (mt == Cfg320<AF>::MT) return gate_up_c<AF, Cfg320<AF>>(a, max_tiles, s);
   if (mt != Cfg128<AF>::MT) return hipErrorInvalidValue;
   return gate_up_c<AF, Cfg128<AF>>(a, max_tiles, s);
 }
 template <int AF>
-hipError_t down_af(const GemmArgs& a, int64_t max_tiles, int mt, bool ordered, hipStream_t s) {
+hipError_t down_af(const GemmArgs& a, int64_t max_tiles, int mt, bool dw, bool ordered, hipStream_t s) {
+  if constexpr (AF == kActFp4)
+    if (dw && mt == Cfg320DW<AF>::MT) return down_c<AF, Cfg320DW<AF>>(a, max_tiles, ordered, s);
+  if (dw) return hipErrorInvalidValue;
   if constexpr (AF != kActBf16)
     if (mt == Cfg320<AF>::MT) return down_c<AF, Cfg320<AF>>(a, max_tiles, ordered, s);
   if (mt != Cfg128<AF>::MT) return hipErrorInvalidValue;
@@ -860,23 +1125,26 @@ hipError_t down_af(const GemmArgs& a, int64_t max_tiles, int mt, bool ordered, h
 }
 }  // namespace
 
-bool tile_fits(int af, int mt, int64_t K) {
+bool tile_fits(int af, int mt, int64_t K, bool dw) {
+  if (dw) return af == kActFp4 && mt == 320 && Cfg320DW<kActFp4>::fits(K);
   if (mt == 128) return true;
   if (mt != 320 || af == kActBf16) return false;
   return af == kActFp4 ? Cfg320<kActFp4>::lds_bytes(K) <= kTileLdsMax : Cfg320<kActFp8>::lds_bytes(K) <= kTileLdsMax;
 }
 
-hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, hipStream_t s) {
+hipError_t launch_gate_up_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool dw, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  if (af == kActFp8) return gate_up_af<kActFp8>(a, max_tiles, mt, s);
-  return af == kActFp4 ? gate_up_af<kActFp4>(a, max_tiles, mt, s) : gate_up_af<kActBf16>(a, max_tiles, mt, s);
+  if (af == kActFp8) return gate_up_af<kActFp8>(a, max_tiles, mt, dw, s);
+  return af == kActFp4 ? gate_up_af<kActFp4>(a, max_tiles, mt, dw, s)
+                       : gate_up_af<kActBf16>(a, max_tiles, mt, dw, s);
 }
 
-hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool ordered, hipStream_t s) {
+hipError_t launch_down_tile(const GemmArgs& a, int64_t max_tiles, int af, int mt, bool dw, bool ordered,
+                            hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  if (af == kActFp8) return down_af<kActFp8>(a, max_tiles, mt, ordered, s);
-  return af == kActFp4 ? down_af<kActFp4>(a, max_tiles, mt, ordered, s)
-                       : down_af<kActBf16>(a, max_tiles, mt, ordered, s);
+  if (af == kActFp8) return down_af<kActFp8>(a, max_tiles, mt, dw, ordered, s);
+  return af == kActFp4 ? down_af<kActFp4>(a, max_tiles, mt, dw, ordered, s)
+                       : down_af<kActBf16>(a, max_tiles, mt, dw, ordered, s);
 }
 
 }  // namespace mxmoe
