@@ -743,9 +743,12 @@ struct CfgDW {
   __device__ static constexpr int rowblock(int wm, int rb) { return wm + WMW * rb; }
 };
 
-template <int AF, typename C, typename FillRows>
+// load_row(r): what row r of the tile is read from (a global load at most);
+// row_value(v): its A-matrix row index.
+template <int AF, typename C, typename LoadRow, typename RowValue>
 __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileItem& it, int64_t K, int64_t N,
-                                                 uint8_t* lds, f32x4_t (&acc)[C::RB][C::WN], FillRows fill_rows) {
+                                                 uint8_t* lds, f32x4_t (&acc)[C::RB][C::WN], LoadRow load_row,
+                                                 RowValue row_value) {
   constexpr int WN = C::WN, RB = C::RB;
   const int lane = lane_id();
   const int g = lane >> 4, l15 = lane & 15;
@@ -761,16 +764,6 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
   const int nrg = (int)(N / 16);
   const int rg0 = it.n0 / 16;
   const int nrgt = nrg - rg0 < C::NRG ? nrg - rg0 : C::NRG;  // row groups of this tile
-  {
-    // weight scale dwords: the tile's row groups are contiguous
-    const uint8_t* src = a.w_scales + (int64_t)it.e * scales_per_expert(N, K) + scales_group_offset(rg0, 0, K);
-    const int n = nrgt * NQ / 4;  // whole KiB
-#pragma unroll 1
-    for (int i = wave; i < n; i += kWaves) copy16(src + i * 1024 + lane * 16, wsc + i * 1024);
-#pragma unroll 1
-    for (int i = wave; i < (nrgt * NQ) % 4; i += kWaves)
-      copy4(src + n * 1024 + i * 256 + lane * 4, wsc + n * 1024 + i * 256);
-  }
   // weight codes: one buffer descriptor over the expert; the row group and
   // k-tile as the scalar offset, the lane's 16 bytes as the vector offset, a
   // k-tile past K an out-of-range vector offset (zeros, no memory traffic)
@@ -793,29 +786,36 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
     for (int cb = 0; cb < WN; ++cb)
       dst[cb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrc, vo, brg[cb] + ko, kCpolNT));
   };
-  // prologue.  The weight scale copies and the weights of k-tiles 0 and 1
-  // depend on the item only and go out first; then the tile's rows (their
-  // tokens or sorted positions) are filled in, the row scale copies and the
-  // activations of k-tiles 0 and 1 follow, and everything lands before the
-  // loop, whose waits then count register loads only.
+  // prologue.  Each thread's tile row is looked up, the weights of k-tiles 0
+  // and 1 (they depend on the item only) go out behind it, the rows go into
+  // LDS (waiting for the lookups only) and a barrier that waits for LDS
+  // traffic only publishes them; then the weight scale copies, the row scale
+  // copies and the activations of k-tiles 0 and 1, and everything lands
+  // before the loop, whose waits then count register loads only.
+  static_assert(C::MT <= kThreads, "one tile row per thread");
+  int32_t* rowidx_w = reinterpret_cast<int32_t*>(lds + C::ROWS_OFF);
+  const bool has_row = (int)threadIdx.x < C::MT;
+  int row_raw = 0;
+  if (has_row) row_raw = load_row((int)threadIdx.x);
   __builtin_amdgcn_sched_barrier(0);
   load_b(0, B[0]);
   load_b(1, B[1]);
   __builtin_amdgcn_sched_barrier(0);
-  fill_rows();
+  if (has_row) rowidx_w[threadIdx.x] = row_value(row_raw);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   // one-time copies.  Row scale bytes: row r at rs + r * kRsStride, its
   // 16-byte chunk c at c ^ ((r >> 1) & 7) (a copy covers 8 rows; lanes past
   // a row's K / 32 bytes copy its chunk 0 again into an unread chunk)
-  {
-    const int nch = RSB / 16;
-#pragma unroll 1
-    for (int i = wave; i < C::MT / 8; i += kWaves) {
-      const int row = 8 * i + (lane >> 3);
-      const int cp = lane & 7;               // physical chunk
-      const int cl = cp ^ ((row >> 1) & 7);  // logical chunk it holds
-      copy16(a.a_scales + (int64_t)rowidx[row] * RSB + (cl < nch ? cl : 0) * 16, rs + i * 1024);
-    }
-  }
+  // (every LDS read of the tile rows comes before the first copy into LDS: a
+  // read behind such a copy makes the compiler wait for all loads)
+  static_assert((C::MT / 8) % kWaves == 0, "row scale copies");
+  constexpr int RS_CP = C::MT / 8 / kWaves;
+  int rs_row[RS_CP];
+#pragma unroll
+  for (int ii = 0; ii < RS_CP; ++ii) rs_row[ii] = rowidx[8 * (wave + kWaves * ii) + (lane >> 3)];
   // activation loads of one k-tile: 8-byte piece P = 320 w + 64 j + lane of
   // the tile's 2560 (row P / 8, piece P % 8 of its 64 bytes), stored at its
   // chunk's swizzled place: logical chunk c of row r at c ^ ((r >> 1) & 3);
@@ -846,8 +846,36 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
     for (int j = 0; j < C::A_LD; ++j) *reinterpret_cast<u32x2_t*>(dst + 512 * j) = src[j];
   };
   __builtin_amdgcn_sched_barrier(0);
+  {
+    const int nch = RSB / 16;
+#pragma unroll
+    for (int ii = 0; ii < RS_CP; ++ii) {
+      const int i = wave + kWaves * ii;
+      const int row = 8 * i + (lane >> 3);
+      const int cp = lane & 7;               // physical chunk
+      const int cl = cp ^ ((row >> 1) & 7);  // logical chunk it holds
+      copy16(a.a_scales + (int64_t)rs_row[ii] * RSB + (cl < nch ? cl : 0) * 16, rs + i * 1024);
+    }
+  }
   load_a(0, areg[0]);
   load_a(1, areg[1]);
+  // weight scale dwords: the tile's row groups are contiguous; whole KiB by
+  // every wave (NRG * K/512 / 4 <= 32 KiB: at most four each, a short share
+  // repeating the last KiB), a last partial KiB (256-byte pieces) at the end
+  const uint8_t* ws_src = a.w_scales + (int64_t)it.e * scales_per_expert(N, K) + scales_group_offset(rg0, 0, K);
+  const int ws_kib = nrgt * NQ / 4, ws_rem = (nrgt * NQ) % 4;
+  static_assert(C::NRG * (kRsStride * 32 / 512) / 4 <= 4 * kWaves, "weight scale copies");
+  if (ws_kib > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = min(wave + kWaves * i, ws_kib - 1);
+      copy16(ws_src + u * 1024 + lane * 16, wsc + u * 1024);
+    }
+  }
+  if (ws_rem > 0) {
+    const int u = min(wave, ws_rem - 1);
+    copy4(ws_src + ws_kib * 1024 + u * 256 + lane * 4, wsc + ws_kib * 1024 + u * 256);
+  }
   wait_vm<0>();
   __builtin_amdgcn_sched_barrier(0);
   // operand reads: row block rb of the wave is tile row 32 rb + 16 wm + l15;
@@ -861,18 +889,19 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
 
   uint32_t scur[WN];
 
-  // step kt (J = kt % 4): store k-tile kt's activation rows (loaded in the
-  // previous step) into slot kt & 1 -- the compiler waits for those loads,
-  // and so for the earlier weight loads of k-tile kt -- then a barrier
-  // publishes the slot (every wave's reads of slot kt & 1 from step kt - 2
-  // ended before its barrier in step kt - 1); load k-tile kt + 1's
-  // activation rows, MFMAs of k-tile kt, weight loads of k-tile kt + 2 into
-  // the registers just consumed.
-  auto step = [&](int kt, auto Jc, u32x4_t (&bset)[WN], u32x2_t (&aset)[C::A_LD]) {
+  // step kt (J = kt % 4): a barrier publishes slot kt & 1 (k-tile kt's rows,
+  // stored in the middle of step kt - 1) and frees the registers that held
+  // them; k-tile kt + 2's rows are loaded into those registers; then the
+  // MFMAs of k-tile kt, with k-tile kt + 1's rows (loaded in step kt - 1)
+  // stored into slot (kt + 1) & 1 halfway through them -- that slot was last
+  // read in step kt - 1, before every wave's barrier of this step -- so the
+  // wait for those loads and the stores overlap the MFMAs already issued;
+  // last the weight loads of k-tile kt + 2 into the registers just consumed.
+  // The compiler's vmcnt waits (register loads only) order everything else.
+  auto step = [&](int kt, auto Jc, u32x4_t (&bset)[WN], u32x2_t (&aload)[C::A_LD], u32x2_t (&astore)[C::A_LD]) {
     constexpr int J = decltype(Jc)::value;
-    store_a(kt, aset);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stores are in LDS, this wave's reads of slot kt - 1 done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's stores and reads of the previous step are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (J == 0) {
@@ -880,7 +909,7 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
       for (int cb = 0; cb < WN; ++cb)
         scur[cb] = *reinterpret_cast<const uint32_t*>(wsc + wsoff[cb] + (kt >> 2) * 256);
     }
-    load_a(kt + 2, aset);
+    load_a(kt + 2, aload);
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* ab = lds + (kt & 1) * C::A_BYTES + a_lane;
     const uint8_t* sbp = rs + s_lane + (((kt >> 2) ^ ssw) << 4) + 4 * J;
@@ -890,11 +919,7 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
       av[rb] = *reinterpret_cast<const u32x4_t*>(ab + rb * 32 * 64);
       as[rb] = sbp[rb * 32 * kRsStride];
     };
-    read_a(0);
-    read_a(1);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (rb + 2 < RB) read_a(rb + 2);
+    auto mfma_rb = [&](int rb) {
       const i32x8_t A = {(int)av[rb][0], (int)av[rb][1], (int)av[rb][2], (int)av[rb][3], 0, 0, 0, 0};
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) {
@@ -902,28 +927,53 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
         acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, acc[rb][cb], 4, 4, 0, (int)as[rb], J,
                                                                        (int)scur[cb]);
       }
+    };
+    constexpr int RH = RB / 2;
+    // first half: two operand reads, then four MFMAs, per row block (reads
+    // two blocks ahead)
+    read_a(0);
+    read_a(1);
+#pragma unroll
+    for (int rb = 0; rb < RH; ++rb) {
+      read_a(rb + 2);
+      mfma_rb(rb);
     }
-    // two operand reads, then four MFMAs, per row block (reads two blocks ahead)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RH; ++rb) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(kt + 1, astore);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = RH; rb < RB; ++rb) {
+      if (rb + 2 < RB) read_a(rb + 2);
+      mfma_rb(rb);
+    }
+#pragma unroll
+    for (int rb = RH; rb < RB; ++rb) {
       if (rb + 2 < RB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_b(kt + 2, bset);
   };
+  // k-tile 0's rows into slot 0 before the first barrier
+  store_a(0, areg[0]);
   for (int kt0 = 0; kt0 < KT; kt0 += 4) {
-    step(kt0, std::integral_constant<int, 0>{}, B[0], areg[0]);
-    step(kt0 + 1, std::integral_constant<int, 1>{}, B[1], areg[1]);
-    step(kt0 + 2, std::integral_constant<int, 2>{}, B[0], areg[0]);
-    step(kt0 + 3, std::integral_constant<int, 3>{}, B[1], areg[1]);
+    step(kt0, std::integral_constant<int, 0>{}, B[0], areg[0], areg[1]);
+    step(kt0 + 1, std::integral_constant<int, 1>{}, B[1], areg[1], areg[0]);
+    step(kt0 + 2, std::integral_constant<int, 2>{}, B[0], areg[0], areg[1]);
+    step(kt0 + 3, std::integral_constant<int, 3>{}, B[1], areg[1], areg[0]);
   }
 }
 
 }  // namespace
 
-// gate_up + clamped SwiGLU.  grid: 8 * ceil(item bound / 8) workgroups of 512.
+// One item of gate_up + clamped SwiGLU: the GEMM of the item's tile, then
+// the SwiGLU of its gate / up pairs into act.
 template <int AF, typename C>
 __device__ __forceinline__ void tile_gate_up_item(const GemmArgs& a, const TileItem& it, uint8_t* lds) {
   constexpr int WN = C::WN, RB = C::RB;
@@ -941,7 +991,9 @@ __device__ __forceinline__ void tile_gate_up_item(const GemmArgs& a, const TileI
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   if constexpr (C::DW)
-    tile_mainloop_dw<AF, C>(a, it, H, a.N, lds, acc, fill_rows);
+    tile_mainloop_dw<AF, C>(
+        a, it, H, a.N, lds, acc, [&](int r) { return a.sorted[it.p0 + (r < it.rows ? r : 0)]; },
+        [&](int v) { return v / a.top_k; });  // token of the tile row
   else if constexpr (C::PF)
     tile_mainloop_pf<AF, C>(a, it, H, a.N, lds, acc);
   else
@@ -951,6 +1003,45 @@ __device__ __forceinline__ void tile_gate_up_item(const GemmArgs& a, const TileI
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WMW, wn = wave / C::WMW;
   const int nrg = (int)(a.N / 16);
+  if constexpr (C::DW) {
+    // The tile's act (MT rows x NT/2 features, bf16) is assembled in LDS
+    // (the activation slots and row scales are free once every wave is past
+    // the k-loop) and written out as 16-byte row pieces.  LDS row r holds
+    // 16-byte chunk c at c ^ (r & 15), so the four row quads of a wave's
+    // MFMA block land in different banks.  Lane (g, l15) of wave (wm, wn)
+    // holds rows 32 rb + 16 wm + 4 g + r and features 32 wn + 16 f + l15.
+    constexpr int FT = C::NT / 2;         // features of the tile
+    constexpr int RBYTES = FT * 2;        // LDS row bytes
+    static_assert(C::MT * RBYTES <= C::RS_OFF + C::MT * kRsStride && RBYTES == 256, "act staging");
+    __syncthreads();
+    const int g = lane >> 4, l15 = lane & 15;
+#pragma unroll
+    for (int f = 0; f < WN / 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rq = 4 * g + r;                    // row & 15
+        const int feat = 32 * wn + 16 * f + l15;
+        uint8_t* base = lds + (16 * wm + rq) * RBYTES + (((feat >> 3) ^ rq) << 4) + (feat & 7) * 2;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float v = swiglu_clamped(acc[rb][2 * f][r], acc[rb][2 * f + 1][r], a.clamp_limit);
+          *reinterpret_cast<__bf16*>(base + rb * 32 * RBYTES) = (__bf16)v;
+        }
+      }
+    __syncthreads();
+    // 16-byte pieces: piece q of the tile is row q / 16, chunk q % 16
+    const int nfeat = (int)(I - it.n0 / 2) < FT ? (int)(I - it.n0 / 2) : FT;  // features of a partial tile
+#pragma unroll
+    for (int i = 0; i < C::MT * RBYTES / 16 / kThreads; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      const int row = q >> 4, c = q & 15;
+      if (row < it.rows && c * 8 < nfeat) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * RBYTES + ((c ^ (row & 15)) << 4));
+        *reinterpret_cast<u32x4_t*>(a.act + (it.p0 + row) * I + it.n0 / 2 + c * 8) = v;
+      }
+    }
+    return;
+  }
   // row groups (2f, 2f+1) of the wave hold gate and up of feature group
   // (n0/16 + WN wn + 2f) / 2
 #pragma unroll
@@ -982,7 +1073,8 @@ __global__ __launch_bounds__(kThreads) void tile_gate_up_kernel(GemmArgs a) {
   tile_gate_up_item<AF, C>(a, it, lds);
 }
 
-// down + combine.
+// One item of down + combine: the GEMM of the item's tile, then its rows
+// into y (ordered combine) or w * y into out32 (fp32 atomics).
 template <int AF, bool ORDERED, typename C>
 __device__ __forceinline__ void tile_down_item(const GemmArgs& a, const TileItem& it, uint8_t* lds) {
   constexpr int WN = C::WN, RB = C::RB;
@@ -1000,7 +1092,9 @@ __device__ __forceinline__ void tile_down_item(const GemmArgs& a, const TileItem
 #pragma unroll
     for (int cb = 0; cb < WN; ++cb) acc[rb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   if constexpr (C::DW)
-    tile_mainloop_dw<AF, C>(a, it, I, H, lds, acc, fill_rows);
+    tile_mainloop_dw<AF, C>(
+        a, it, I, H, lds, acc, [&](int r) { return (int32_t)(it.p0 + (r < it.rows ? r : 0)); },
+        [](int v) { return v; });  // sorted position of the tile row
   else if constexpr (C::PF)
     tile_mainloop_pf<AF, C>(a, it, I, H, lds, acc);
   else
