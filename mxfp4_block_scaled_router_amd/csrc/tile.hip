@@ -129,6 +129,7 @@ struct Cfg {
   static constexpr int ROWS_OFF = WS_OFF + WS_BYTES;
   static constexpr int RS_OFF = ROWS_OFF + ROWS_BYTES;  // RS: [MT][K/32] activation scale bytes
   static constexpr int LDS = RS_OFF;                     // without the row scales
+  static constexpr int STAGE_MAX = WS_OFF;  // LDS free for the epilogue (the rings)
   static constexpr size_t lds_bytes(int64_t K) { return (size_t)LDS + (RS ? (size_t)MT * (size_t)(K / 32) : 0); }
   static_assert(SA >= 2 && SA <= 5 && SB >= SA && LDS <= 160 * 1024, "LDS budget");
   static_assert(!RS || PF, "row scales need the PF pipeline");
@@ -731,6 +732,7 @@ struct CfgDW {
   static constexpr int ROWS_OFF = 2 * A_BYTES;
   static constexpr int RS_OFF = ROWS_OFF + MT * 4;
   static constexpr int WSC_OFF = RS_OFF + MT * kRsStride;
+  static constexpr int STAGE_MAX = WSC_OFF;  // LDS free for the epilogue (slots, rows, row scales)
   static constexpr size_t lds_bytes(int64_t K) {
     return (size_t)WSC_OFF + (size_t)NRG * (size_t)(K / 512) * 256;
   }
@@ -1003,62 +1005,49 @@ __device__ __forceinline__ void tile_gate_up_item(const GemmArgs& a, const TileI
   const int wave = threadIdx.x >> 6;
   const int wm = wave % C::WMW, wn = wave / C::WMW;
   const int nrg = (int)(a.N / 16);
-  if constexpr (C::DW) {
-    // The tile's act (MT rows x NT/2 features, bf16) is assembled in LDS
-    // (the activation slots and row scales are free once every wave is past
-    // the k-loop) and written out as 16-byte row pieces.  LDS row r holds
-    // 16-byte chunk c at c ^ (r & 15), so the four row quads of a wave's
-    // MFMA block land in different banks.  Lane (g, l15) of wave (wm, wn)
-    // holds rows 32 rb + 16 wm + 4 g + r and features 32 wn + 16 f + l15.
-    constexpr int FT = C::NT / 2;         // features of the tile
-    constexpr int RBYTES = FT * 2;        // LDS row bytes
-    static_assert(C::MT * RBYTES <= C::RS_OFF + C::MT * kRsStride && RBYTES == 256, "act staging");
-    __syncthreads();
+  // The tile's act (MT rows x NT/2 features, bf16) is assembled in LDS (the
+  // rings are free once every wave is past the k-loop and the copies issued
+  // past K have landed) and written out as 16-byte row pieces: one store per
+  // 16 bytes instead of a 2-byte store per element.  LDS row r holds 16-byte
+  // chunk c at c ^ (r & SW), so the four row quads of an MFMA block land in
+  // different banks.  Lane (g, l15) of wave (wm, wn) holds rows
+  // 16 rowblock(wm, rb) + 4 g + r and features 16 (WN wn / 2 + f) + l15.
+  constexpr int FT = C::NT / 2;      // features of the tile
+  constexpr int RBYTES = FT * 2;     // LDS row bytes
+  constexpr int CH = RBYTES / 16;    // 16-byte chunks per row (a power of two)
+  constexpr int SW = CH < 16 ? CH - 1 : 15;
+  static_assert(C::MT * RBYTES <= C::STAGE_MAX && (CH & (CH - 1)) == 0, "act staging");
+  static_assert((C::MT * RBYTES / 16) % kThreads == 0, "act pieces");
+  wait_vm<0>();
+  __syncthreads();
+  (void)nrg;
+  {
     const int g = lane >> 4, l15 = lane & 15;
 #pragma unroll
     for (int f = 0; f < WN / 2; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rq = 4 * g + r;                    // row & 15
-        const int feat = 32 * wn + 16 * f + l15;
-        uint8_t* base = lds + (16 * wm + rq) * RBYTES + (((feat >> 3) ^ rq) << 4) + (feat & 7) * 2;
+        const int feat = 16 * (wn * WN / 2 + f) + l15;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+          const int row = C::rowblock(wm, rb) * 16 + 4 * g + r;
           const float v = swiglu_clamped(acc[rb][2 * f][r], acc[rb][2 * f + 1][r], a.clamp_limit);
-          *reinterpret_cast<__bf16*>(base + rb * 32 * RBYTES) = (__bf16)v;
+          *reinterpret_cast<__bf16*>(lds + row * RBYTES + (((feat >> 3) ^ (row & SW)) << 4) + (feat & 7) * 2) =
+              (__bf16)v;
         }
       }
-    __syncthreads();
-    // 16-byte pieces: piece q of the tile is row q / 16, chunk q % 16
-    const int nfeat = (int)(I - it.n0 / 2) < FT ? (int)(I - it.n0 / 2) : FT;  // features of a partial tile
-#pragma unroll
-    for (int i = 0; i < C::MT * RBYTES / 16 / kThreads; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q >> 4, c = q & 15;
-      if (row < it.rows && c * 8 < nfeat) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * RBYTES + ((c ^ (row & 15)) << 4));
-        *reinterpret_cast<u32x4_t*>(a.act + (it.p0 + row) * I + it.n0 / 2 + c * 8) = v;
-      }
-    }
-    return;
   }
-  // row groups (2f, 2f+1) of the wave hold gate and up of feature group
-  // (n0/16 + WN wn + 2f) / 2
+  __syncthreads();
+  // 16-byte pieces: piece q of the tile is row q / CH, chunk q % CH
+  const int nfeat = (int)(I - it.n0 / 2) < FT ? (int)(I - it.n0 / 2) : FT;  // features of a partial tile
 #pragma unroll
-  for (int f = 0; f < WN / 2; ++f) {
-    const int rg = it.n0 / 16 + wn * WN + 2 * f;
-    if (rg >= nrg) break;
-    const int64_t n = (int64_t)(rg / 2) * 16 + (lane & 15);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = C::rowblock(wm, rb) * 16 + 4 * (lane >> 4) + r;
-        if (row < it.rows) {
-          const float v = swiglu_clamped(acc[rb][2 * f][r], acc[rb][2 * f + 1][r], a.clamp_limit);
-          a.act[(it.p0 + row) * I + n] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
+  for (int i = 0; i < C::MT * RBYTES / 16 / kThreads; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    const int row = q / CH, c = q % CH;
+    if (row < it.rows && c * 8 < nfeat) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * RBYTES + ((c ^ (row & SW)) << 4));
+      *reinterpret_cast<u32x4_t*>(a.act + (it.p0 + row) * I + it.n0 / 2 + c * 8) = v;
+    }
   }
 }
 
