@@ -82,6 +82,10 @@ A4_CASES = {
     # 320-row tiles at the widest K whose scale rows fit LDS: gate_up's rows of
     # 136 scale bytes (not a multiple of 16) take the 4-byte copies
     "a4_k4352": W.WORKLOADS["a4"].replace(T=128, H=4352, I=256, E_global=8, E_local=8, top_k=4),
+    # down on the direct-weight 320 x 256 tiles (I a multiple of 512) with a
+    # half last tile (H = 640: 2.5 tiles of 256 weight rows); gate_up (K = 640)
+    # on the 320 x 128 tiles
+    "a4_dw_partial": W.WORKLOADS["a4"].replace(T=512, H=640, I=512, E_global=16, E_local=16, top_k=4),
 }
 A8_CASES = {
     "a8_tiny": W.WORKLOADS["a8"].replace(T=64, H=512, I=256, E_global=8, E_local=8, top_k=2),
