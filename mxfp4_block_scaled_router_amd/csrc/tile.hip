@@ -836,11 +836,16 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
   }
   typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
   u32x2_t areg[2][C::A_LD];
+  // buffer loads: the k-tile as the scalar offset, the row piece as a 32-bit
+  // vector offset (no 64-bit address registers per load)
+  const int64_t a_bytes = a.a_rows * (K / 2);
+  const __amdgpu_buffer_rsrc_t arc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.a_codes), (short)0, (int)(a_bytes < INT32_MAX ? a_bytes : INT32_MAX), 0x00020000);
   auto load_a = [&](int kt, u32x2_t (&dst)[C::A_LD]) {
-    const int k = kt < KT ? kt : KT - 1;
-    const uint8_t* base = a.a_codes + (int64_t)k * 64;
+    const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * 64u;
 #pragma unroll
-    for (int j = 0; j < C::A_LD; ++j) dst[j] = *reinterpret_cast<const u32x2_t*>(base + a_off[j]);
+    for (int j = 0; j < C::A_LD; ++j)
+      dst[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(arc, a_off[j], ko, 0));
   };
   auto store_a = [&](int kt, const u32x2_t (&src)[C::A_LD]) {
     uint8_t* dst = lds + (kt & 1) * C::A_BYTES + a_dst;
