@@ -718,6 +718,17 @@ __device__ __forceinline__ void tile_mainloop_pf(const GemmArgs& a, const TileIt
 // copied into LDS once, before the loop.
 //   waves: 2 x 4 grid, wave (wm, wn) owns row blocks wm, wm + 2, ... (10) and
 //   row groups 4 wn .. 4 wn + 3 (gate / up pairs); 160 accumulator VGPRs.
+// Workgroup barrier for LDS hand-offs: LDS-only release / acquire fences
+// (they wait for this wave's LDS operations, lgkmcnt, not for its global
+// loads) keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 constexpr int kRsStride = 128;
 template <int AF>
 struct CfgDW {
@@ -804,10 +815,7 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
   load_b(1, B[1]);
   __builtin_amdgcn_sched_barrier(0);
   if (has_row) rowidx_w[threadIdx.x] = row_value(row_raw);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
+  lds_sync();
   // one-time copies.  Row scale bytes: row r at rs + r * kRsStride, its
   // 16-byte chunk c at c ^ ((r >> 1) & 7) (a copy covers 8 rows; lanes past
   // a row's K / 32 bytes copy its chunk 0 again into an unread chunk)
@@ -907,10 +915,7 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
   // The compiler's vmcnt waits (register loads only) order everything else.
   auto step = [&](int kt, auto Jc, u32x4_t (&bset)[WN], u32x2_t (&aload)[C::A_LD], u32x2_t (&astore)[C::A_LD]) {
     constexpr int J = decltype(Jc)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's stores and reads of the previous step are done
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    lds_sync();  // this wave's stores and reads of the previous step are done
     if constexpr (J == 0) {
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb)
