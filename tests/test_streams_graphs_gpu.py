@@ -26,8 +26,13 @@ def _forward(case, logits, out, ws):
                          workspace=ws)
 
 
+# MXFP4 activations on the direct-weight 320 x 256 tiles (x and SwiGLU-output
+# quantisation, chunked routing, both tile GEMMs and the ordered gather)
+EXTRA = {"a4_dw": W.WORKLOADS["a4"].replace(T=512, H=1024, I=512, E_global=16, E_local=16, top_k=4)}
+
+
 def _setup(name):
-    case = Case(W.WORKLOADS[name], deterministic=True)
+    case = Case(EXTRA[name] if name in EXTRA else W.WORKLOADS[name], deterministic=True)
     wl = case.wl
     ws = torch.empty(mx.mxfp4_moe_workspace_bytes(case.dims, wl.top_k), dtype=torch.uint8,
                      device="cuda")
@@ -64,7 +69,7 @@ def test_two_streams_run_concurrently():
             np.testing.assert_array_equal(bits_of(o), want)
 
 
-@pytest.mark.parametrize("name", ["decode", "ep_share", "verify_b32"])
+@pytest.mark.parametrize("name", ["decode", "ep_share", "verify_b32", "a4_dw"])
 def test_graph_replays_match_eager(name):
     """Three forwards recorded into one graph (each plan's kernels, no memset
     nodes: buffers are cleared by kernels), replayed three times with eager
