@@ -739,8 +739,10 @@ struct CfgDW {
   static constexpr int NT = 16 * NRG;       // 256 weight rows
   static constexpr int ARB = act_row_bytes(AF);
   static constexpr int A_BYTES = MT * ARB;
-  static constexpr int A_LD = A_BYTES / (kThreads * 8);  // 8-byte activation loads per lane and k-tile
-  static constexpr int ROWS_OFF = 2 * A_BYTES;
+  // activation rows of a k-tile pair: 16-byte loads per lane (128 bytes of
+  // each row), two LDS slots of two k-tiles each
+  static constexpr int A_LD = 2 * A_BYTES / (kThreads * 16);
+  static constexpr int ROWS_OFF = 4 * A_BYTES;
   static constexpr int RS_OFF = ROWS_OFF + MT * 4;
   static constexpr int WSC_OFF = RS_OFF + MT * kRsStride;
   static constexpr int STAGE_MAX = WSC_OFF;  // LDS free for the epilogue (slots, rows, row scales)
@@ -752,7 +754,7 @@ struct CfgDW {
   static constexpr bool fits(int64_t K) {
     return K > 0 && K % 512 == 0 && K / 32 <= kRsStride && lds_bytes(K) <= kTileLdsMax;
   }
-  static_assert(AF == kActFp4 && A_BYTES % (kThreads * 8) == 0 && (kThreads * 8) % 512 == 0, "direct-weight tile");
+  static_assert(AF == kActFp4 && (2 * A_BYTES) % (kThreads * 16) == 0, "direct-weight tile");
   __device__ static constexpr int rowblock(int wm, int rb) { return wm + WMW * rb; }
 };
 
@@ -826,39 +828,40 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
   int rs_row[RS_CP];
 #pragma unroll
   for (int ii = 0; ii < RS_CP; ++ii) rs_row[ii] = rowidx[8 * (wave + kWaves * ii) + (lane >> 3)];
-  // activation loads of one k-tile: 8-byte piece P = 320 w + 64 j + lane of
-  // the tile's 2560 (row P / 8, piece P % 8 of its 64 bytes), stored at its
-  // chunk's swizzled place: logical chunk c of row r at c ^ ((r >> 1) & 3);
-  // (r >> 1) & 3 does not depend on j, so piece j is an immediate 512 j away
+  // activation loads of a k-tile pair: load j of thread t takes 16-byte piece
+  // p = t % 8 of the pair's 128 bytes of tile row 64 j + t / 8 -- k-tile
+  // p / 4 of the pair, logical chunk p % 4 -- stored at that k-tile's half of
+  // the slot, chunk (p % 4) ^ ((row >> 1) & 3); that swizzle does not depend
+  // on j, so load j lands an immediate 64 rows further
   uint32_t a_off[C::A_LD];
   uint32_t a_dst;
   {
-    const int p8 = lane & 7;
+    const int t = (int)threadIdx.x;
+    const int p = t & 7;
 #pragma unroll
     for (int j = 0; j < C::A_LD; ++j) {
-      const int row = (C::MT / kWaves) * wave + 8 * j + (lane >> 3);
-      a_off[j] = (uint32_t)rowidx[row] * (uint32_t)(K / 2) + (uint32_t)p8 * 8u;
+      const int row = 64 * j + (t >> 3);
+      a_off[j] = (uint32_t)rowidx[row] * (uint32_t)(K / 2) + (uint32_t)p * 16u;
     }
-    const int row = (C::MT / kWaves) * wave + (lane >> 3);
-    a_dst = (uint32_t)(row * 64 + (((p8 >> 1) ^ ((row >> 1) & 3)) << 4) + (p8 & 1) * 8);
+    const int row = t >> 3;
+    a_dst = (uint32_t)((p >> 2) * C::A_BYTES + row * 64 + (((p & 3) ^ ((row >> 1) & 3)) << 4));
   }
-  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-  u32x2_t areg[2][C::A_LD];
-  // buffer loads: the k-tile as the scalar offset, the row piece as a 32-bit
-  // vector offset (no 64-bit address registers per load)
+  // buffer loads: the k-tile pair as the scalar offset, the row piece as a
+  // 32-bit vector offset (no 64-bit address registers per load)
   const int64_t a_bytes = a.a_rows * (K / 2);
   const __amdgpu_buffer_rsrc_t arc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.a_codes), (short)0, (int)(a_bytes < INT32_MAX ? a_bytes : INT32_MAX), 0x00020000);
-  auto load_a = [&](int kt, u32x2_t (&dst)[C::A_LD]) {
-    const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * 64u;
+  u32x4_t areg[C::A_LD];
+  auto load_a = [&](int kp) {  // k-tile pair kp (k-tiles 2 kp, 2 kp + 1)
+    const uint32_t ko = (uint32_t)(2 * kp < KT ? kp : KT / 2 - 1) * 128u;
 #pragma unroll
     for (int j = 0; j < C::A_LD; ++j)
-      dst[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(arc, a_off[j], ko, 0));
+      areg[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(arc, a_off[j], ko, 0));
   };
-  auto store_a = [&](int kt, const u32x2_t (&src)[C::A_LD]) {
-    uint8_t* dst = lds + (kt & 1) * C::A_BYTES + a_dst;
+  auto store_a = [&](int kp) {
+    uint8_t* dst = lds + (kp & 1) * 2 * C::A_BYTES + a_dst;
 #pragma unroll
-    for (int j = 0; j < C::A_LD; ++j) *reinterpret_cast<u32x2_t*>(dst + 512 * j) = src[j];
+    for (int j = 0; j < C::A_LD; ++j) *reinterpret_cast<u32x4_t*>(dst + 64 * 64 * j) = areg[j];
   };
   __builtin_amdgcn_sched_barrier(0);
   {
@@ -872,8 +875,7 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
       copy16(a.a_scales + (int64_t)rs_row[ii] * RSB + (cl < nch ? cl : 0) * 16, rs + i * 1024);
     }
   }
-  load_a(0, areg[0]);
-  load_a(1, areg[1]);
+  load_a(0);
   // weight scale dwords: the tile's row groups are contiguous; whole KiB by
   // every wave (NRG * K/512 / 4 <= 32 KiB: at most four each, a short share
   // repeating the last KiB), a last partial KiB (256-byte pieces) at the end
@@ -904,26 +906,17 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
 
   uint32_t scur[WN];
 
-  // step kt (J = kt % 4): a barrier publishes slot kt & 1 (k-tile kt's rows,
-  // stored in the middle of step kt - 1) and frees the registers that held
-  // them; k-tile kt + 2's rows are loaded into those registers; then the
-  // MFMAs of k-tile kt, with k-tile kt + 1's rows (loaded in step kt - 1)
-  // stored into slot (kt + 1) & 1 halfway through them -- that slot was last
-  // read in step kt - 1, before every wave's barrier of this step -- so the
-  // wait for those loads and the stores overlap the MFMAs already issued;
-  // last the weight loads of k-tile kt + 2 into the registers just consumed.
-  // The compiler's vmcnt waits (register loads only) order everything else.
-  auto step = [&](int kt, auto Jc, u32x4_t (&bset)[WN], u32x2_t (&aload)[C::A_LD], u32x2_t (&astore)[C::A_LD]) {
+  // Pair step kp (k-tiles kt = 2 kp and kt + 1; J0 = kt % 4): the pair's
+  // activation rows (loaded in the previous pair step) are stored into slot
+  // kp & 1 -- the compiler waits for those loads, and so for the earlier
+  // weight loads -- and a barrier publishes the slot (every wave's reads of
+  // that slot from pair kp - 2 ended before its barrier in pair kp - 1); the
+  // next pair's rows are loaded; then k-tile kt's MFMAs and the weight loads
+  // of k-tile kt + 2 into the registers they consumed, and the same for
+  // k-tile kt + 1.  One barrier per two k-tiles.
+  auto half = [&](int kt, auto Jc, u32x4_t (&bset)[WN], const uint8_t* slot) {
     constexpr int J = decltype(Jc)::value;
-    lds_sync();  // this wave's stores and reads of the previous step are done
-    if constexpr (J == 0) {
-#pragma unroll
-      for (int cb = 0; cb < WN; ++cb)
-        scur[cb] = *reinterpret_cast<const uint32_t*>(wsc + wsoff[cb] + (kt >> 2) * 256);
-    }
-    load_a(kt + 2, aload);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* ab = lds + (kt & 1) * C::A_BYTES + a_lane;
+    const uint8_t* ab = slot + (kt & 1) * C::A_BYTES + a_lane;
     const uint8_t* sbp = rs + s_lane + (((kt >> 2) ^ ssw) << 4) + 4 * J;
     u32x4_t av[RB];
     uint32_t as[RB];
@@ -931,7 +924,11 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
       av[rb] = *reinterpret_cast<const u32x4_t*>(ab + rb * 32 * 64);
       as[rb] = sbp[rb * 32 * kRsStride];
     };
-    auto mfma_rb = [&](int rb) {
+    read_a(0);
+    read_a(1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (rb + 2 < RB) read_a(rb + 2);
       const i32x8_t A = {(int)av[rb][0], (int)av[rb][1], (int)av[rb][2], (int)av[rb][3], 0, 0, 0, 0};
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) {
@@ -939,46 +936,37 @@ __device__ __forceinline__ void tile_mainloop_dw(const GemmArgs& a, const TileIt
         acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bv, acc[rb][cb], 4, 4, 0, (int)as[rb], J,
                                                                        (int)scur[cb]);
       }
-    };
-    constexpr int RH = RB / 2;
-    // first half: two operand reads, then four MFMAs, per row block (reads
-    // two blocks ahead)
-    read_a(0);
-    read_a(1);
-#pragma unroll
-    for (int rb = 0; rb < RH; ++rb) {
-      read_a(rb + 2);
-      mfma_rb(rb);
     }
+    // two operand reads, then four MFMAs, per row block (reads two blocks ahead)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int rb = 0; rb < RH; ++rb) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(kt + 1, astore);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rb = RH; rb < RB; ++rb) {
-      if (rb + 2 < RB) read_a(rb + 2);
-      mfma_rb(rb);
-    }
-#pragma unroll
-    for (int rb = RH; rb < RB; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       if (rb + 2 < RB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_b(kt + 2, bset);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // k-tile 0's rows into slot 0 before the first barrier
-  store_a(0, areg[0]);
-  for (int kt0 = 0; kt0 < KT; kt0 += 4) {
-    step(kt0, std::integral_constant<int, 0>{}, B[0], areg[0], areg[1]);
-    step(kt0 + 1, std::integral_constant<int, 1>{}, B[1], areg[1], areg[0]);
-    step(kt0 + 2, std::integral_constant<int, 2>{}, B[0], areg[0], areg[1]);
-    step(kt0 + 3, std::integral_constant<int, 3>{}, B[1], areg[1], areg[0]);
+  auto pair = [&](int kp, auto J0) {
+    constexpr int J = decltype(J0)::value;
+    const int kt = 2 * kp;
+    store_a(kp);
+    lds_sync();  // this wave's stores and reads of the previous pair are done
+    if constexpr (J == 0) {
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb)
+        scur[cb] = *reinterpret_cast<const uint32_t*>(wsc + wsoff[cb] + (kt >> 2) * 256);
+    }
+    load_a(kp + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* slot = lds + (kp & 1) * 2 * C::A_BYTES;
+    half(kt, std::integral_constant<int, J>{}, B[0], slot);
+    half(kt + 1, std::integral_constant<int, J + 1>{}, B[1], slot);
+  };
+  for (int kp0 = 0; kp0 < KT / 2; kp0 += 2) {
+    pair(kp0, std::integral_constant<int, 0>{});
+    pair(kp0 + 1, std::integral_constant<int, 2>{});
   }
 }
 
